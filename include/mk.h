@@ -1,0 +1,192 @@
+/*
+ * mk.h -- C ABI of the MI355X decode-step megakernel library (libmk.so).
+ *
+ * What it computes: one autoregressive decode step of a transformer LLM
+ * (embedding row -> per layer: RMSNorm, QKV projection, rotary embedding,
+ * attention over the paged KV cache, O projection + residual, RMSNorm,
+ * SwiGLU MLP or softmax top-k MoE + residual -> final RMSNorm, LM head,
+ * greedy argmax).  The Cohere megakernel article ("Egyetlen tartós kernelre
+ * épül a kiszolgálás") describes running that whole forward pass as one
+ * persistent kernel with one resident block per SM, working from a task list
+ * prepared on the host, with data dependencies signalled through counters in
+ * global memory; the Mirage MPK summary ("Part 1. Compiler", "Part 2.
+ * Runtime") describes the same split into a compiler that lowers the graph
+ * into fine-grained tasks and events, and a runtime whose workers run tasks
+ * and bump event counters.  This library is that design for one MI355X:
+ * mk_build_plan is the host-side lowering, mk_decode_step launches the
+ * persistent kernel (one workgroup per CU).
+ *
+ * Conventions
+ *  - Every pointer named *_dev or held in mk_weights / mk_kv is a device
+ *    pointer (HIP device memory of the plan's device).  The caller owns all of
+ *    them; the library never frees them and never writes weights.
+ *  - bf16 = IEEE bfloat16 bit patterns (uint16).  Matrices are row-major
+ *    [out_features][in_features]; a projection is y = W x.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls that take a stream are asynchronous and stream-ordered; they do
+ *    not synchronise the host (mk_plan_status excepted).
+ *  - Functions return MK_OK (0) or a negative MK_ERR_* code; the message of
+ *    the last failure on the calling thread is returned by mk_last_error().
+ *    No C++ exception crosses this boundary.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MK_OK = 0,
+  MK_ERR_INVALID_CONFIG = -1, /* model shape the library cannot plan        */
+  MK_ERR_INVALID_ARG = -2,    /* bad pointer / size / index argument          */
+  MK_ERR_HIP = -3,            /* a HIP runtime call failed                    */
+  MK_ERR_OOM = -4,            /* device allocation failed                     */
+  MK_ERR_PLAN = -5,           /* planner produced an invalid task graph       */
+  MK_ERR_TIMEOUT = -6,        /* a device-side dependency wait hit its budget */
+  MK_ERR_UNSUPPORTED = -7     /* valid request outside what is implemented    */
+};
+
+/* Executors.  PERSISTENT: one launch per step, grid = one workgroup per CU,
+ * tasks pulled from a ticket counter and ordered by HBM event counters.
+ * KERNEL_PER_OP: the same task code, one launch per operation of each layer,
+ * stream order standing in for the counters (the launch-overhead baseline). */
+enum { MK_EXEC_PERSISTENT = 0, MK_EXEC_KERNEL_PER_OP = 1 };
+
+/* Task operations (values of mk_task_info.op). */
+enum {
+  MK_OP_EMBED = 1, MK_OP_QKV = 2, MK_OP_ATTN = 3, MK_OP_MERGE = 4,
+  MK_OP_OPROJ = 5, MK_OP_GATEUP = 6, MK_OP_DOWN = 7, MK_OP_ROUTER = 8,
+  MK_OP_TOPK = 9, MK_OP_EGATEUP = 10, MK_OP_EDOWN = 11, MK_OP_COMBINE = 12,
+  MK_OP_LMHEAD = 13, MK_OP_ARGMAX = 14
+};
+
+/* Model shape and capacity.  n_experts == 0 selects the dense SwiGLU MLP
+ * (ffn_dim used); n_experts > 0 selects the MoE MLP (top_k, expert_ffn_dim).
+ * max_batch: decode slots per step.  page_size must be 16.
+ * max_pages_per_seq: columns of the page table.  n_pages: pages in each pool. */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  float rms_eps;
+  double rope_theta;
+  int32_t n_experts, top_k, expert_ffn_dim;
+  int32_t max_batch, page_size, max_pages_per_seq, n_pages;
+} mk_config;
+
+/* Device pointers to the weights (bf16).  Per-layer tensors are given by a
+ * host array of n_layers device pointers; expert tensors by a host array of
+ * n_layers*n_experts pointers indexed [layer*n_experts + expert].  Shapes:
+ *   embed, lm_head [vocab][hidden]; final_norm, attn_norm[l], ffn_norm[l]
+ *   [hidden]; wq[l] [n_q_heads*head_dim][hidden]; wk[l], wv[l]
+ *   [n_kv_heads*head_dim][hidden]; wo[l] [hidden][n_q_heads*head_dim];
+ *   dense: w_gate[l], w_up[l] [ffn_dim][hidden], w_down[l] [hidden][ffn_dim];
+ *   MoE: router[l] [n_experts][hidden]; e_gate, e_up [expert_ffn][hidden];
+ *   e_down [hidden][expert_ffn].  Unused members may be NULL.
+ * The host arrays are copied during mk_build_plan. */
+typedef struct {
+  const void *embed, *lm_head, *final_norm;
+  const void *const *attn_norm, *const *ffn_norm;
+  const void *const *wq, *const *wk, *const *wv, *const *wo;
+  const void *const *w_gate, *const *w_up, *const *w_down;
+  const void *const *router, *const *e_gate, *const *e_up, *const *e_down;
+} mk_weights;
+
+/* Paged KV cache (caller-owned).  k_pool, v_pool: bf16
+ * [n_layers][n_pages][n_kv_heads][page_size][head_dim].  page_table: device
+ * int32 [max_batch][max_pages_per_seq]; entry [b][j] is the pool page holding
+ * positions 16j..16j+15 of slot b.  The caller may edit page_table and the
+ * pools between steps (sequences joining / retiring). */
+typedef struct {
+  void *k_pool, *v_pool;
+  int32_t *page_table;
+} mk_kv;
+
+typedef struct {
+  int32_t executor;      /* MK_EXEC_*                                        */
+  int32_t n_workgroups;  /* persistent grid size; 0 = number of CUs           */
+  int32_t attn_splits;   /* KV splits per (sequence, KV head); 0 = auto       */
+  int32_t planned_ctx;   /* context the auto split is sized for; 0 = capacity */
+  int32_t debug_trace;   /* 1: record per-task start/finish tickets            */
+  int32_t device;        /* HIP device ordinal; -1 = current device            */
+  int64_t spin_budget;   /* dependency-wait budget in 100 MHz ticks; 0 = 1 s   */
+  int32_t n_cus;         /* override the CU count used for tile sizing; 0 = query */
+  int32_t reserved[7];
+} mk_plan_options;
+
+typedef struct mk_plan mk_plan;
+
+/* Fill *opts with defaults (persistent executor, auto sizes). */
+void mk_plan_options_default(mk_plan_options *opts);
+
+/* Lower the model into a task list, validate it, allocate the plan's device
+ * state (task table, event counters, activation scratch, RoPE table) on the
+ * device and upload it.  Synchronous.  *out receives the plan (free with
+ * mk_free).  opts may be NULL. */
+int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
+                  const mk_plan_options *opts, mk_plan **out);
+
+/* One decode step for all max_batch slots.
+ *  tokens_dev[b]     input token of slot b (int32, device)
+ *  positions_dev[b]  0-based position of that token (= number of tokens
+ *                    already cached for the slot); < 0 marks an empty slot
+ *  next_tokens_dev   out: greedy argmax per slot (-1 for empty slots)
+ *  logits_dev        out, optional (NULL): fp32 [max_batch][vocab]
+ * The step writes the slot's key/value at `position` into the page given by
+ * page_table[b][position/16].  tokens_dev may alias next_tokens_dev.  */
+int mk_decode_step(mk_plan *plan, const int32_t *tokens_dev,
+                   const int32_t *positions_dev, void *stream,
+                   int32_t *next_tokens_dev, float *logits_dev);
+
+/* Feed n prompt tokens tokens_dev[0..n) of one slot at positions
+ * start_pos..start_pos+n-1, filling its KV pages (other slots are left
+ * untouched).  next_token_dev (optional) receives the greedy token after the
+ * last prompt token, logits_dev (optional) its fp32 logits [vocab]. */
+int mk_prefill(mk_plan *plan, int32_t slot, const int32_t *tokens_dev,
+               int32_t n, int32_t start_pos, void *stream,
+               int32_t *next_token_dev, float *logits_dev);
+
+/* Synchronise `stream` and report a device-side error of this plan's last
+ * steps (MK_ERR_TIMEOUT when a dependency wait exceeded its budget).  The
+ * error is cleared and the plan's counters are reset. */
+int mk_plan_status(mk_plan *plan, void *stream);
+
+/* Release everything the plan allocated.  NULL is ignored. */
+void mk_free(mk_plan *plan);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *mk_last_error(void);
+
+/* ---- introspection (host only; no GPU needed) ----------------------------
+ * mk_inspect_plan runs the planner for `cfg` and `n_cus` CUs without touching
+ * a device and copies the task graph into caller arrays (cap = capacity in
+ * elements; *n_tasks / *n_events receive the true counts even when they
+ * exceed the capacity).  Event thresholds are per step. */
+typedef struct {
+  int32_t op, layer, a0, a1, a2, a3, a4, a5;
+  int32_t n_wait, wait_ev[3];
+  int32_t n_sig, sig_ev[2];
+  int32_t phase;             /* launch index under KERNEL_PER_OP            */
+  int64_t bytes;             /* algorithmic HBM bytes this task reads       */
+} mk_task_info;
+
+int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts,
+                    mk_task_info *tasks, int32_t task_cap, int32_t *n_tasks,
+                    int32_t *ev_thresholds, int32_t ev_cap, int32_t *n_events);
+
+/* Persistent-executor trace of the last step run with debug_trace = 1:
+ * per task {start ticket, finish ticket, run count, workgroup,
+ * deps-ready time, finish time (100 MHz ticks, low 32 bits)}, 6 x uint32
+ * each.  Synchronises `stream`.  cap in tasks. */
+int mk_read_trace(mk_plan *plan, void *stream, uint32_t *out, int32_t cap);
+
+/* Number of tasks and events of a built plan, and the number of CUs it was
+ * sized for. */
+int mk_plan_info(const mk_plan *plan, int32_t *n_tasks, int32_t *n_events,
+                 int32_t *n_cus, int32_t *n_phases);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

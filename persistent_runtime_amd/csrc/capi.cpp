@@ -1,0 +1,458 @@
+// capi.cpp -- the C ABI (include/mk.h): argument checks, plan lifetime,
+// device allocations, step launches and device-error read-back.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <memory>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "launch.h"
+#include "mk_task.h"
+#include "planner.h"
+
+using namespace mk;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &m) {
+  g_err = m;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  return fail(e == hipErrorOutOfMemory ? MK_ERR_OOM : MK_ERR_HIP, m);
+}
+
+#define HIP_TRY(call, what)                         \
+  do {                                              \
+    hipError_t e_ = (call);                         \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct mk_plan {
+  HostPlan hp;
+  int device = 0;
+  int grid = 0;
+  int executor = MK_EXEC_PERSISTENT;
+  bool trace = false;
+  DevPlan d{};
+  DevPlan *d_dev = nullptr;  // device copy of d
+  std::vector<void *> allocs;
+  uint32_t epoch = 0;
+  uint32_t epoch_limit = 1;
+  int32_t *stage_tok = nullptr, *stage_pos = nullptr, *stage_next = nullptr;
+  float *stage_logits = nullptr;
+  uint32_t *ctrl = nullptr;  // CTRL_WORDS control words then the event counters
+  int n_ctrl_words = 0;
+
+  ~mk_plan() {
+    for (void *p : allocs) hipFree(p);
+  }
+  template <class T>
+  int alloc(T **p, size_t count, const char *what) {
+    *p = nullptr;
+    if (count == 0) return MK_OK;
+    void *v = nullptr;
+    hipError_t e = hipMalloc(&v, count * sizeof(T));
+    if (e != hipSuccess) return hip_fail(e, what);
+    allocs.push_back(v);
+    *p = (T *)v;
+    return MK_OK;
+  }
+};
+
+extern "C" {
+
+const char *mk_last_error(void) { return g_err.c_str(); }
+
+void mk_plan_options_default(mk_plan_options *o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof(*o));
+  o->executor = MK_EXEC_PERSISTENT;
+  o->device = -1;
+}
+
+int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts, mk_task_info *tasks,
+                    int32_t task_cap, int32_t *n_tasks, int32_t *ev_thresholds,
+                    int32_t ev_cap, int32_t *n_events) {
+  try {
+    if (!cfg) return fail(MK_ERR_INVALID_ARG, "cfg is NULL");
+    mk_plan_options o;
+    mk_plan_options_default(&o);
+    if (opts) o = *opts;
+    int n_cus = o.n_cus > 0 ? o.n_cus : 256;
+    HostPlan hp;
+    std::string err;
+    int rc = build_host_plan(*cfg, o, n_cus, hp, err);
+    if (rc != MK_OK) return fail(rc, err);
+    const int T = (int)hp.tasks.size(), E = (int)hp.ev_thr.size();
+    if (n_tasks) *n_tasks = T;
+    if (n_events) *n_events = E;
+    for (int i = 0; tasks && i < T && i < task_cap; ++i) {
+      const Task &t = hp.tasks[i];
+      mk_task_info &q = tasks[i];
+      std::memset(&q, 0, sizeof q);
+      q.op = t.op; q.layer = t.layer;
+      q.a0 = t.a0; q.a1 = t.a1; q.a2 = t.a2; q.a3 = t.a3; q.a4 = t.a4; q.a5 = t.a5;
+      q.n_wait = t.n_wait;
+      for (int k = 0; k < 3; ++k) q.wait_ev[k] = k < t.n_wait ? t.wait_ev[k] : -1;
+      q.n_sig = t.n_sig;
+      for (int k = 0; k < 2; ++k) q.sig_ev[k] = k < t.n_sig ? t.sig_ev[k] : -1;
+      q.phase = hp.task_phase[i];
+      q.bytes = hp.task_bytes[i];
+    }
+    for (int e = 0; ev_thresholds && e < E && e < ev_cap; ++e) ev_thresholds[e] = hp.ev_thr[e];
+    return MK_OK;
+  } catch (const std::exception &ex) {
+    return fail(MK_ERR_PLAN, ex.what());
+  }
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int check_weights(const mk_config &c, const mk_weights &w, std::vector<const void *> &tab,
+                         std::string &err) {
+  const int L = c.n_layers, E = c.n_experts;
+  auto need = [&](const void *p, const char *name, int i) {
+    if (!p) {
+      err = std::string("weight pointer ") + name + "[" + std::to_string(i) + "] is NULL";
+      return false;
+    }
+    if (!aligned16(p)) {
+      err = std::string("weight pointer ") + name + "[" + std::to_string(i) +
+            "] is not 16-byte aligned";
+      return false;
+    }
+    return true;
+  };
+  if (!need(w.embed, "embed", 0) || !need(w.lm_head, "lm_head", 0) ||
+      !need(w.final_norm, "final_norm", 0))
+    return MK_ERR_INVALID_ARG;
+  // table order: attn_norm, ffn_norm, wq, wk, wv, wo, w_gate, w_up, w_down,
+  // router [L each], then e_gate, e_up, e_down [L*E each]
+  const void *const *per_layer[10] = {w.attn_norm, w.ffn_norm, w.wq, w.wk, w.wv,
+                                      w.wo, w.w_gate, w.w_up, w.w_down, w.router};
+  const char *names[10] = {"attn_norm", "ffn_norm", "wq", "wk", "wv",
+                           "wo", "w_gate", "w_up", "w_down", "router"};
+  tab.assign((size_t)10 * L + (size_t)3 * L * E, nullptr);
+  for (int k = 0; k < 10; ++k) {
+    const bool used = k < 6 || (E == 0 ? (k >= 6 && k <= 8) : k == 9);
+    if (!used) continue;
+    if (!per_layer[k]) {
+      err = std::string("weight table ") + names[k] + " is NULL";
+      return MK_ERR_INVALID_ARG;
+    }
+    for (int l = 0; l < L; ++l) {
+      if (!need(per_layer[k][l], names[k], l)) return MK_ERR_INVALID_ARG;
+      tab[(size_t)k * L + l] = per_layer[k][l];
+    }
+  }
+  if (E > 0) {
+    const void *const *ex[3] = {w.e_gate, w.e_up, w.e_down};
+    const char *en[3] = {"e_gate", "e_up", "e_down"};
+    for (int k = 0; k < 3; ++k) {
+      if (!ex[k]) {
+        err = std::string("weight table ") + en[k] + " is NULL";
+        return MK_ERR_INVALID_ARG;
+      }
+      for (int i = 0; i < L * E; ++i) {
+        if (!need(ex[k][i], en[k], i)) return MK_ERR_INVALID_ARG;
+        tab[(size_t)10 * L + (size_t)k * L * E + i] = ex[k][i];
+      }
+    }
+  }
+  return MK_OK;
+}
+
+int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
+                  const mk_plan_options *opts, mk_plan **out) {
+  try {
+    if (!out) return fail(MK_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!cfg || !w || !kv) return fail(MK_ERR_INVALID_ARG, "cfg, weights and kv are required");
+    mk_plan_options o;
+    mk_plan_options_default(&o);
+    if (opts) o = *opts;
+    if (o.executor != MK_EXEC_PERSISTENT && o.executor != MK_EXEC_KERNEL_PER_OP)
+      return fail(MK_ERR_INVALID_ARG, "unknown executor");
+    std::string err;
+    int rc = check_config(*cfg, err);
+    if (rc != MK_OK) return fail(rc, err);
+    std::vector<const void *> tab;
+    rc = check_weights(*cfg, *w, tab, err);
+    if (rc != MK_OK) return fail(rc, err);
+    if (!kv->k_pool || !kv->v_pool || !kv->page_table)
+      return fail(MK_ERR_INVALID_ARG, "kv pools and page table are required");
+    if (!aligned16(kv->k_pool) || !aligned16(kv->v_pool))
+      return fail(MK_ERR_INVALID_ARG, "kv pools must be 16-byte aligned");
+
+    int dev = o.device;
+    if (dev < 0) HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    DeviceGuard guard(dev);
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties");
+    if ((size_t)persistent_lds_bytes() > prop.sharedMemPerBlock)
+      return fail(MK_ERR_UNSUPPORTED, "device has less LDS per workgroup than the kernels need");
+
+    std::unique_ptr<mk_plan> p(new mk_plan());
+    p->device = dev;
+    p->executor = o.executor;
+    p->trace = o.debug_trace != 0;
+    const int hw_cus = prop.multiProcessorCount;
+    const int n_cus = o.n_cus > 0 ? o.n_cus : hw_cus;
+    p->grid = o.n_workgroups > 0 ? o.n_workgroups : hw_cus;
+    rc = build_host_plan(*cfg, o, n_cus, p->hp, err);
+    if (rc != MK_OK) return fail(rc, err);
+    HostPlan &hp = p->hp;
+    const mk_config &c = hp.cfg;
+    const int T = (int)hp.tasks.size(), E = (int)hp.ev_thr.size();
+    const int L = c.n_layers, B = c.max_batch;
+
+    // epoch limit: (epoch + 1) * max threshold must stay below 2^31
+    int32_t max_thr = 1;
+    for (int32_t v : hp.ev_thr) max_thr = std::max(max_thr, v);
+    p->epoch_limit = (uint32_t)(((1u << 31) - 1u) / (uint32_t)max_thr) - 2u;
+
+    // device allocations
+    Task *d_tasks;
+    if ((rc = p->alloc(&d_tasks, T, "task table"))) return rc;
+    p->n_ctrl_words = CTRL_WORDS + E;
+    if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
+    const int64_t nf = hp.n_x + hp.n_xmid + hp.n_q + 2 * hp.n_k + hp.n_part + hp.n_attn + hp.n_h +
+                       hp.n_rl + hp.n_tk + hp.n_he + hp.n_ye + hp.n_amax;
+    float *fs;
+    if ((rc = p->alloc(&fs, (size_t)nf, "activation scratch"))) return rc;
+    int32_t *is;
+    if ((rc = p->alloc(&is, (size_t)(hp.n_tk + hp.n_amax + 3 * B), "index scratch"))) return rc;
+    const void **d_tab;
+    if ((rc = p->alloc(&d_tab, tab.size(), "weight tables"))) return rc;
+    const int half = c.head_dim / 2;
+    float *rope;
+    if ((rc = p->alloc(&rope, (size_t)2 * hp.max_pos * half, "rope tables"))) return rc;
+    uint32_t *trace = nullptr;
+    if (p->trace && (rc = p->alloc(&trace, (size_t)T * 6, "trace"))) return rc;
+    if ((rc = p->alloc(&p->stage_logits, (size_t)B * c.vocab, "prefill logits"))) return rc;
+
+    // uploads
+    HIP_TRY(hipMemcpy(d_tasks, hp.tasks.data(), (size_t)T * sizeof(Task), hipMemcpyHostToDevice),
+            "upload tasks");
+    HIP_TRY(hipMemcpy(d_tab, tab.data(), tab.size() * sizeof(void *), hipMemcpyHostToDevice),
+            "upload weight tables");
+    {
+      // rotary tables: angle p * theta^(-2i/hd) and its cos/sin in double,
+      // rounded once to float
+      std::vector<float> cs((size_t)hp.max_pos * half), sn((size_t)hp.max_pos * half);
+      for (int i = 0; i < half; ++i) {
+        const double f = std::pow(c.rope_theta, -2.0 * i / c.head_dim);
+        for (int ps = 0; ps < hp.max_pos; ++ps) {
+          const double a = (double)ps * f;
+          cs[(size_t)ps * half + i] = (float)std::cos(a);
+          sn[(size_t)ps * half + i] = (float)std::sin(a);
+        }
+      }
+      HIP_TRY(hipMemcpy(rope, cs.data(), cs.size() * 4, hipMemcpyHostToDevice), "upload rope");
+      HIP_TRY(hipMemcpy(rope + cs.size(), sn.data(), sn.size() * 4, hipMemcpyHostToDevice),
+              "upload rope");
+    }
+    HIP_TRY(hipMemset(p->ctrl, 0, (size_t)p->n_ctrl_words * 4), "zero counters");
+    HIP_TRY(hipMemset(fs, 0, (size_t)nf * 4), "zero scratch");
+    HIP_TRY(hipMemset(is, 0, (size_t)(hp.n_tk + hp.n_amax + 3 * B) * 4), "zero scratch");
+    if (trace) HIP_TRY(hipMemset(trace, 0, (size_t)T * 24), "zero trace");
+
+    DevPlan &d = p->d;
+    d.L = L; d.H = c.hidden; d.nq = c.n_q_heads; d.nkv = c.n_kv_heads; d.hd = c.head_dim;
+    d.F = c.ffn_dim; d.V = c.vocab; d.E = c.n_experts; d.topk = c.top_k;
+    d.Fe = c.expert_ffn_dim; d.B = B; d.maxp = c.max_pages_per_seq; d.npages = c.n_pages;
+    d.S = hp.S; d.G = hp.G; d.max_pos = hp.max_pos; d.n_lm_tiles = hp.n_lm_tiles;
+    d.eps = c.rms_eps;
+    d.embed = (const uint16_t *)w->embed;
+    d.lm_head = (const uint16_t *)w->lm_head;
+    d.final_norm = (const uint16_t *)w->final_norm;
+    const uint16_t *const *T16 = (const uint16_t *const *)d_tab;
+    d.attn_norm = T16 + 0 * L; d.ffn_norm = T16 + 1 * L;
+    d.wq = T16 + 2 * L; d.wk = T16 + 3 * L; d.wv = T16 + 4 * L; d.wo = T16 + 5 * L;
+    d.w_gate = T16 + 6 * L; d.w_up = T16 + 7 * L; d.w_down = T16 + 8 * L;
+    d.router = T16 + 9 * L;
+    const size_t LE = (size_t)L * c.n_experts;
+    d.e_gate = T16 + 10 * L; d.e_up = T16 + 10 * L + LE; d.e_down = T16 + 10 * L + 2 * LE;
+    d.k_pool = (uint16_t *)kv->k_pool;
+    d.v_pool = (uint16_t *)kv->v_pool;
+    d.page_table = kv->page_table;
+    float *f = fs;
+    auto take = [&](int64_t n) { float *r = n ? f : nullptr; f += n; return r; };
+    d.x = take(hp.n_x); d.xmid = take(hp.n_xmid); d.q = take(hp.n_q); d.k = take(hp.n_k);
+    d.v = take(hp.n_k); d.part = take(hp.n_part); d.attn = take(hp.n_attn); d.h = take(hp.n_h);
+    d.rl = take(hp.n_rl); d.tk_w = take(hp.n_tk); d.he = take(hp.n_he); d.ye = take(hp.n_ye);
+    d.amax_v = take(hp.n_amax);
+    d.tk_ids = hp.n_tk ? is : nullptr;
+    d.amax_i = is + hp.n_tk;
+    p->stage_tok = is + hp.n_tk + hp.n_amax;
+    p->stage_pos = p->stage_tok + B;
+    p->stage_next = p->stage_pos + B;
+    d.rope_cos = rope;
+    d.rope_sin = rope + (size_t)hp.max_pos * half;
+    d.ctrl = p->ctrl;
+    d.ev = p->ctrl + CTRL_WORDS;
+    d.tasks = d_tasks;
+    d.n_tasks = T;
+    d.spin_budget = o.spin_budget > 0 ? o.spin_budget : 100000000LL;  // 1 s at 100 MHz
+    d.trace = trace;
+    if ((rc = p->alloc(&p->d_dev, 1, "plan copy"))) return rc;
+    HIP_TRY(hipMemcpy(p->d_dev, &d, sizeof d, hipMemcpyHostToDevice), "upload plan");
+    *out = p.release();
+    return MK_OK;
+  } catch (const std::exception &ex) {
+    return fail(MK_ERR_PLAN, ex.what());
+  }
+}
+
+static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positions,
+                     hipStream_t s, int32_t *next, float *logits) {
+  const DevPlan &d = plan->d;
+  CallArgs ca;
+  ca.tokens = tokens;
+  ca.positions = positions;
+  ca.next_tokens = next;
+  ca.logits = logits;
+  ca.epoch = plan->epoch;
+  if (plan->executor == MK_EXEC_PERSISTENT) {
+    if (plan->trace) {
+      HIP_TRY(launch_zero_u32(d.trace, (int)plan->hp.tasks.size() * 6, s), "trace reset");
+      HIP_TRY(launch_zero_u32(plan->ctrl + CTRL_CLOCK, 1, s), "trace reset");
+    }
+    HIP_TRY(launch_persistent(plan->d_dev, ca, plan->grid, s), "persistent launch");
+    if (++plan->epoch >= plan->epoch_limit) {
+      HIP_TRY(launch_zero_u32(d.ev, (int)plan->hp.ev_thr.size(), s), "counter reset");
+      plan->epoch = 0;
+    }
+  } else {
+    for (auto &ph : plan->hp.phases)
+      HIP_TRY(launch_phase(plan->d_dev, ca, ph.first, ph.second - ph.first, s), "phase launch");
+  }
+  return MK_OK;
+}
+
+int mk_decode_step(mk_plan *plan, const int32_t *tokens_dev, const int32_t *positions_dev,
+                   void *stream, int32_t *next_tokens_dev, float *logits_dev) {
+  try {
+    if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
+    if (!tokens_dev || !positions_dev || !next_tokens_dev)
+      return fail(MK_ERR_INVALID_ARG, "tokens, positions and next_tokens are required");
+    DeviceGuard guard(plan->device);
+    return step_impl(plan, tokens_dev, positions_dev, (hipStream_t)stream, next_tokens_dev,
+                     logits_dev);
+  } catch (const std::exception &ex) {
+    return fail(MK_ERR_PLAN, ex.what());
+  }
+}
+
+int mk_prefill(mk_plan *plan, int32_t slot, const int32_t *tokens_dev, int32_t n,
+               int32_t start_pos, void *stream, int32_t *next_token_dev, float *logits_dev) {
+  try {
+    if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
+    const mk_config &c = plan->hp.cfg;
+    if (slot < 0 || slot >= c.max_batch) return fail(MK_ERR_INVALID_ARG, "slot out of range");
+    if (!tokens_dev || n < 1) return fail(MK_ERR_INVALID_ARG, "need n >= 1 prompt tokens");
+    if (start_pos < 0 || (int64_t)start_pos + n > plan->hp.max_pos)
+      return fail(MK_ERR_INVALID_ARG, "prompt positions exceed the page-table capacity");
+    DeviceGuard guard(plan->device);
+    hipStream_t s = (hipStream_t)stream;
+    for (int i = 0; i < n; ++i) {
+      HIP_TRY(launch_stage(plan->stage_tok, plan->stage_pos, c.max_batch, slot, tokens_dev, i,
+                           start_pos, s),
+              "prefill staging");
+      int rc = step_impl(plan, plan->stage_tok, plan->stage_pos, s, plan->stage_next,
+                         (i == n - 1 && logits_dev) ? plan->stage_logits : nullptr);
+      if (rc != MK_OK) return rc;
+    }
+    if (next_token_dev)
+      HIP_TRY(hipMemcpyAsync(next_token_dev, plan->stage_next + slot, 4, hipMemcpyDeviceToDevice, s),
+              "prefill token copy");
+    if (logits_dev)
+      HIP_TRY(hipMemcpyAsync(logits_dev, plan->stage_logits + (size_t)slot * c.vocab,
+                             (size_t)c.vocab * 4, hipMemcpyDeviceToDevice, s),
+              "prefill logits copy");
+    return MK_OK;
+  } catch (const std::exception &ex) {
+    return fail(MK_ERR_PLAN, ex.what());
+  }
+}
+
+int mk_plan_status(mk_plan *plan, void *stream) {
+  if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
+  DeviceGuard guard(plan->device);
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  uint32_t w[CTRL_WORDS];
+  HIP_TRY(hipMemcpy(w, plan->ctrl, sizeof w, hipMemcpyDeviceToHost), "read error word");
+  if (w[CTRL_ERR] == DEVERR_NONE) return MK_OK;
+  char buf[256];
+  int code;
+  if (w[CTRL_ERR] == DEVERR_TIMEOUT) {
+    snprintf(buf, sizeof buf,
+             "dependency wait timed out: task %u waited on event %u (counter %u, needed %u)",
+             w[CTRL_ERR_TASK], w[CTRL_ERR_EV], w[CTRL_ERR_SEEN], w[CTRL_ERR_WANT]);
+    code = MK_ERR_TIMEOUT;
+  } else {
+    snprintf(buf, sizeof buf,
+             "invalid device-side input in task %u (kind %d): value %d, limit %u",
+             w[CTRL_ERR_TASK], (int)w[CTRL_ERR_EV], (int)w[CTRL_ERR_SEEN], w[CTRL_ERR_WANT]);
+    code = MK_ERR_INVALID_ARG;
+  }
+  HIP_TRY(hipMemset(plan->ctrl, 0, (size_t)plan->n_ctrl_words * 4), "reset counters");
+  plan->epoch = 0;
+  return fail(code, buf);
+}
+
+int mk_read_trace(mk_plan *plan, void *stream, uint32_t *out, int32_t cap) {
+  if (!plan || !out) return fail(MK_ERR_INVALID_ARG, "plan and out are required");
+  if (!plan->d.trace) return fail(MK_ERR_INVALID_ARG, "plan was built without debug_trace");
+  DeviceGuard guard(plan->device);
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  const int T = (int)plan->hp.tasks.size();
+  const int n = std::min(T, (int)cap);
+  HIP_TRY(hipMemcpy(out, plan->d.trace, (size_t)n * 24, hipMemcpyDeviceToHost), "read trace");
+  return MK_OK;
+}
+
+int mk_plan_info(const mk_plan *plan, int32_t *n_tasks, int32_t *n_events, int32_t *n_cus,
+                 int32_t *n_phases) {
+  if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
+  if (n_tasks) *n_tasks = (int32_t)plan->hp.tasks.size();
+  if (n_events) *n_events = (int32_t)plan->hp.ev_thr.size();
+  if (n_cus) *n_cus = plan->hp.n_cus;
+  if (n_phases) *n_phases = (int32_t)plan->hp.phases.size();
+  return MK_OK;
+}
+
+void mk_free(mk_plan *plan) {
+  if (!plan) return;
+  DeviceGuard guard(plan->device);
+  hipDeviceSynchronize();
+  delete plan;
+}
+
+}  // extern "C"

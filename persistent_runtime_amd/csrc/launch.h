@@ -1,0 +1,29 @@
+// launch.h -- host-side launchers of the device code in kernels.hip.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "mk_task.h"
+
+namespace mk {
+
+// One decode step as a single persistent launch: `grid` workgroups (one per
+// CU) pull tickets until the task list is exhausted.  `d` is a device copy.
+hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, hipStream_t s);
+
+// Kernel-per-op: tasks [first, first+count) of one launch phase, one
+// workgroup per task, no counters (stream order orders the phases).
+hipError_t launch_phase(const DevPlan *d, const CallArgs &ca, int first, int count,
+                        hipStream_t s);
+
+// Prefill staging: slot `slot` gets tokens[i] at position start+i, every
+// other slot is marked empty.
+hipError_t launch_stage(int32_t *stage_tok, int32_t *stage_pos, int B, int slot,
+                        const int32_t *tokens, int i, int start, hipStream_t s);
+
+// Zero n words (counter reset between epochs).
+hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t s);
+
+// Resource use of the persistent kernel (for reports).
+int persistent_lds_bytes();
+
+}  // namespace mk

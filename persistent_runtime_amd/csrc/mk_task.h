@@ -1,0 +1,108 @@
+// mk_task.h -- task table, device-side plan state and sizing constants shared
+// by the host planner (planner.cpp), the C ABI (capi.cpp) and the device code
+// (kernels.hip).  Plain C++: no HIP types, so the planner builds without HIP.
+//
+// Design (Mirage MPK summary, "Part 1. Compiler" / "Part 2. Runtime"; Cohere
+// megakernel article, "Egyetlen tartós kernelre épül a kiszolgálás"): the
+// host lowers a decode step into tasks, each one tile of one operation; every
+// task waits on up to three event counters and bumps up to two.  An event
+// fires once its counter reaches its threshold (the number of producer tasks
+// per step).  Counters are monotonic across steps: a waiter of step `epoch`
+// needs counter >= (epoch + 1) * threshold, so no reset launch is needed.
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+// ---- workgroup geometry ---------------------------------------------------
+constexpr int kThreads = 512;          // one workgroup per CU, 8 wave64s
+constexpr int kWaves = kThreads / 64;
+// A GEMV tile is streamed as "wave-chunks": 64 lanes x one vector load each.
+// kChunkBytes16: 64 lanes x 16 B; the 8-B variant is used when a row is not
+// a multiple of 1 KiB.  Each wave holds up to kMaxChunks 16-B loads per lane.
+constexpr int kMaxChunks = 16;
+constexpr int kMaxTileUnits16 = kWaves * kMaxChunks;        // 1 KiB units/tile
+constexpr int kPageSize = 16;
+constexpr int kMaxGroup = 8;           // query heads per KV head
+constexpr int kMaxBatchGemv = 4;       // slots a GEMV tile handles at once
+constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
+constexpr int kLdsXBytes = 128 * 1024; // budget for staged activations
+
+enum Op : int16_t {
+  OP_EMBED = 1, OP_QKV = 2, OP_ATTN = 3, OP_MERGE = 4, OP_OPROJ = 5,
+  OP_GATEUP = 6, OP_DOWN = 7, OP_ROUTER = 8, OP_TOPK = 9, OP_EGATEUP = 10,
+  OP_EDOWN = 11, OP_COMBINE = 12, OP_LMHEAD = 13, OP_ARGMAX = 14
+};
+
+// 64-byte task descriptor.  Field use per op:
+//   EMBED   a0=slot
+//   QKV     a0=matrix (0 q, 1 k, 2 v) a1=row0 a2=rows
+//   ATTN    a0=slot a1=kv head a2=split
+//   MERGE   a0=slot a1=kv head
+//   OPROJ/DOWN/ROUTER  a1=row0 a2=rows
+//   GATEUP  a1=row0 a2=rows per matrix (gate rows then the same up rows)
+//   TOPK    a0=slot
+//   EGATEUP a0=slot a1=row0 a2=rows per matrix a3=expert slot
+//   EDOWN   a0=slot a1=row0 a2=rows a3=expert slot
+//   COMBINE a0=slot a1=row0 a2=rows
+//   LMHEAD  a1=row0 a2=rows a4=tile index
+//   ARGMAX  a0=slot
+struct alignas(16) Task {
+  int16_t op, layer, n_wait, n_sig;
+  int32_t a0, a1, a2, a3, a4, a5;
+  int32_t wait_ev[3];
+  int32_t wait_thr[3];
+  int32_t sig_ev[2];
+};
+static_assert(sizeof(Task) == 64, "task descriptor is 64 bytes");
+
+// control words (u32) at the head of the counter buffer
+enum Ctrl {
+  CTRL_TICKET = 0, CTRL_DONE = 1, CTRL_ERR = 2, CTRL_ERR_TASK = 3,
+  CTRL_ERR_EV = 4, CTRL_ERR_SEEN = 5, CTRL_ERR_WANT = 6, CTRL_CLOCK = 7,
+  CTRL_WORDS = 16
+};
+enum DevErr { DEVERR_NONE = 0, DEVERR_TIMEOUT = 1, DEVERR_BAD_INPUT = 2 };
+
+// Static plan state; the plan keeps a copy in device memory.
+struct DevPlan {
+  // shape
+  int32_t L, H, nq, nkv, hd, F, V, E, topk, Fe, B, maxp, npages, S, G;
+  int32_t max_pos, n_lm_tiles;
+  float eps;
+  // weights (bf16 as uint16)
+  const uint16_t *embed, *lm_head, *final_norm;
+  const uint16_t *const *attn_norm, *const *ffn_norm;   // device tables [L]
+  const uint16_t *const *wq, *const *wk, *const *wv, *const *wo;
+  const uint16_t *const *w_gate, *const *w_up, *const *w_down;
+  const uint16_t *const *router;                        // [L]
+  const uint16_t *const *e_gate, *const *e_up, *const *e_down;  // [L*E]
+  // KV cache
+  uint16_t *k_pool, *v_pool;
+  const int32_t *page_table;
+  // scratch (fp32 unless noted); layouts in planner.cpp
+  float *x, *xmid, *q, *k, *v, *part, *attn, *h;
+  float *rl, *tk_w, *he, *ye, *amax_v;
+  int32_t *tk_ids, *amax_i;
+  const float *rope_cos, *rope_sin;                     // [max_pos][hd/2]
+  // control
+  uint32_t *ev;            // event counters, after CTRL_WORDS control words
+  uint32_t *ctrl;
+  const Task *tasks;
+  int32_t n_tasks;
+  int64_t spin_budget;     // in s_memrealtime ticks (100 MHz)
+  uint32_t *trace;         // 6 u32 per task, or null
+};
+
+// Per-step arguments, passed by value next to a device copy of DevPlan.
+struct CallArgs {
+  const int32_t *tokens, *positions;
+  int32_t *next_tokens;
+  float *logits;
+  uint32_t epoch;
+};
+
+// scratch sizes (elements), shared by planner and device code
+inline int64_t part_stride(int hd) { return hd + 4; }  // o[hd], m, l, pad
+
+}  // namespace mk

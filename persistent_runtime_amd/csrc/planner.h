@@ -1,0 +1,55 @@
+// planner.h -- host-side lowering of a decode step into the task graph.
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_task.h"
+
+namespace mk {
+
+struct GemvShape {       // how one operation's rows are cut into tiles
+  int rows_per_tile;     // rows per matrix segment
+  int vec_bytes;         // 16 or 8: per-lane load width
+  int tiles;
+};
+
+struct HostPlan {
+  mk_config cfg{};
+  int n_cus = 0;
+  int S = 1;                        // attention splits per (slot, KV head)
+  int G = 1;                        // query heads per KV head
+  int n_lm_tiles = 0;
+  int max_pos = 0;
+  std::vector<Task> tasks;
+  std::vector<int32_t> ev_thr;      // per-step threshold of each event
+  std::vector<int32_t> task_phase;  // launch index under kernel-per-op
+  std::vector<std::pair<int32_t, int32_t>> phases;  // [begin, end) per launch
+  std::vector<int64_t> task_bytes;  // algorithmic bytes read per task
+  // scratch sizes in elements
+  int64_t n_x = 0, n_xmid = 0, n_q = 0, n_k = 0, n_part = 0, n_attn = 0,
+          n_h = 0, n_rl = 0, n_tk = 0, n_he = 0, n_ye = 0, n_amax = 0;
+  GemvShape qkv{}, oproj{}, gateup{}, down{}, lmhead{}, router{}, egateup{},
+      edown{};
+};
+
+// Vector width (bytes per lane load) for rows of K bf16 elements, or 0 when
+// a row is not a multiple of 512 bytes.
+int vec_bytes_for(int K);
+
+// Check a configuration; returns MK_OK or MK_ERR_INVALID_CONFIG /
+// MK_ERR_UNSUPPORTED with a message.
+int check_config(const mk_config &c, std::string &err);
+
+// Lower cfg into a task graph sized for n_cus CUs.
+int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
+                    HostPlan &p, std::string &err);
+
+// Structural checks: every waited event is signalled only by earlier tasks
+// (ticket order is a topological order), thresholds equal the number of
+// signalling tasks, no event is left without a waiter except the last.
+int validate_plan(const HostPlan &p, std::string &err);
+
+}  // namespace mk

