@@ -51,17 +51,31 @@ def test_tiny_teacher_forced(tiny, executor, splits):
     worst, ids, cache = teacher_forced_run(r, Wt, _prompt(), 16)
     assert worst <= LOGIT_TOL, worst
     assert_ids(ids)
-    # KV pages hold the rotated keys / values of every position, in bf16
+    check_kv_pages(r, cache, TINY)
+    r.plan.free()
+
+
+def check_kv_pages(r, cache, cfg, slot=0):
+    """KV pages hold the rotated keys / values of every position, in bf16.
+
+    Layer 0's keys and values depend only on the token embedding, identical on
+    both sides, so they must equal the oracle's fp32 values rounded to bf16
+    (within 1 bf16 ulp): this pins the page / slot placement exactly.  Deeper
+    layers see inputs perturbed by the device's bf16 KV cache, so they are
+    held to a relative bound instead."""
     n = cache.length()
-    k, v = r.kv.read_tokens(0, n)
+    k, v = r.kv.read_tokens(slot, n)
     k = k.float().cpu().numpy()
     v = v.float().cpu().numpy()
-    for l in range(TINY["n_layers"]):
+    for l in range(cfg["n_layers"]):
         dk = np.abs(k[l] - cache.K[l])
         dv = np.abs(v[l] - cache.V[l])
-        assert np.all(dk <= bf16_ulp(cache.K[l]) + 1e-6), float(dk.max())
-        assert np.all(dv <= bf16_ulp(cache.V[l]) + 1e-6), float(dv.max())
-    r.plan.free()
+        if l == 0:
+            assert np.all(dk <= bf16_ulp(cache.K[l]) + 1e-6), float(dk.max())
+            assert np.all(dv <= bf16_ulp(cache.V[l]) + 1e-6), float(dv.max())
+        else:
+            assert dk.max() <= 0.02 * np.abs(cache.K[l]).max(), float(dk.max())
+            assert dv.max() <= 0.02 * np.abs(cache.V[l]).max(), float(dv.max())
 
 
 def test_tiny_free_running_greedy_matches(tiny):
