@@ -50,7 +50,8 @@ enum {
 };
 
 /* Executors.  PERSISTENT: one launch per step, grid = one workgroup per CU,
- * tasks pulled from a ticket counter and ordered by HBM event counters.
+ * each workgroup running its own planner-assigned queue of tasks in list
+ * order, ordered across workgroups by HBM event counters.
  * KERNEL_PER_OP: the same task code, one launch per operation of each layer,
  * stream order standing in for the counters (the launch-overhead baseline). */
 enum { MK_EXEC_PERSISTENT = 0, MK_EXEC_KERNEL_PER_OP = 1 };
@@ -105,10 +106,12 @@ typedef struct {
 
 typedef struct {
   int32_t executor;      /* MK_EXEC_*                                        */
-  int32_t n_workgroups;  /* persistent grid size; 0 = number of CUs           */
+  int32_t n_workgroups;  /* persistent workers (grid size); 0 = number of CUs.
+                            All must be resident at once (cooperative launch) */
   int32_t attn_splits;   /* KV splits per (sequence, KV head); 0 = auto       */
   int32_t planned_ctx;   /* context the auto split is sized for; 0 = capacity */
-  int32_t debug_trace;   /* 1: record per-task start/finish tickets            */
+  int32_t debug_trace;   /* 1: per-task start/finish tickets (serialising) and
+                            times; 2: per-task times only                    */
   int32_t device;        /* HIP device ordinal; -1 = current device            */
   int64_t spin_budget;   /* dependency-wait budget in 100 MHz ticks; 0 = 1 s   */
   int32_t n_cus;         /* override the CU count used for tile sizing; 0 = query */
@@ -159,15 +162,19 @@ void mk_free(mk_plan *plan);
 const char *mk_last_error(void);
 
 /* ---- introspection (host only; no GPU needed) ----------------------------
- * mk_inspect_plan runs the planner for `cfg` and `n_cus` CUs without touching
- * a device and copies the task graph into caller arrays (cap = capacity in
- * elements; *n_tasks / *n_events receive the true counts even when they
- * exceed the capacity).  Event thresholds are per step. */
+ * mk_inspect_plan runs the planner for `cfg` with opts->n_cus CUs and
+ * opts->n_workgroups workers (0: 256 each) without touching a device and
+ * copies the task graph into caller arrays (cap = capacity in elements;
+ * *n_tasks / *n_events receive the true counts even when they exceed the
+ * capacity).  Event thresholds are per step. */
 typedef struct {
-  int32_t op, layer, a0, a1, a2, a3, a4, a5;
+  int32_t op, layer, a0, a1, a2, a3, a4;
+  int32_t sig_count;         /* completions reported (0: reported by a later
+                                task of the same worker's run)               */
   int32_t n_wait, wait_ev[3];
   int32_t n_sig, sig_ev[2];
   int32_t phase;             /* launch index under KERNEL_PER_OP            */
+  int32_t worker;            /* persistent workgroup whose queue holds it   */
   int64_t bytes;             /* algorithmic HBM bytes this task reads       */
 } mk_task_info;
 

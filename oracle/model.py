@@ -249,12 +249,15 @@ def decode_step(Wt: OracleWeights, cfg: dict, cache: KVCache, token: int,
     return (logits, x) if return_hidden else logits
 
 
-def forward_full(Wt: OracleWeights, cfg: dict, tokens):
+def forward_full(Wt: OracleWeights, cfg: dict, tokens, return_cache=False):
     """Full causal forward over a whole token sequence (no cache reuse).
 
     Position t attends to positions 0..t.  Returns logits [T, vocab].  This is
-    the recompute that incremental decoding must reproduce.
+    the recompute that incremental decoding must reproduce.  With
+    return_cache=True it also returns the rotated keys and values it computed,
+    as a KVCache ready for incremental decoding from position T.
     """
+    cache = KVCache(cfg, Wt.dtype) if return_cache else None
     dtype = Wt.dtype
     tokens = [int(t) for t in tokens]
     T = len(tokens)
@@ -269,6 +272,8 @@ def forward_full(Wt: OracleWeights, cfg: dict, tokens):
         Vx = (A @ Wt.get("wv", l).T).reshape(T, nkv, hd)
         Q = rope(Q, cos[:, None, :], sin[:, None, :])
         Kx = rope(Kx, cos[:, None, :], sin[:, None, :])
+        if cache is not None:
+            cache.K[l], cache.V[l] = Kx.copy(), Vx.copy()
         O = np.empty_like(Q)
         for t in range(T):
             O[t] = attention(Q[t], Kx[: t + 1], Vx[: t + 1], nkv)
@@ -281,4 +286,5 @@ def forward_full(Wt: OracleWeights, cfg: dict, tokens):
         else:
             X = X + np.stack([_ffn(Wt, cfg, l, B[t], dtype) for t in range(T)])
     Hn = rmsnorm(X, Wt.get("final_norm"), eps, dtype)
-    return Hn @ Wt.get("lm_head").T
+    logits = Hn @ Wt.get("lm_head").T
+    return (logits, cache) if return_cache else logits

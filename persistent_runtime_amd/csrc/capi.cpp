@@ -105,9 +105,10 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts, mk_task_i
     mk_plan_options_default(&o);
     if (opts) o = *opts;
     int n_cus = o.n_cus > 0 ? o.n_cus : 256;
+    int n_workers = o.n_workgroups > 0 ? o.n_workgroups : n_cus;
     HostPlan hp;
     std::string err;
-    int rc = build_host_plan(*cfg, o, n_cus, hp, err);
+    int rc = build_host_plan(*cfg, o, n_cus, n_workers, hp, err);
     if (rc != MK_OK) return fail(rc, err);
     const int T = (int)hp.tasks.size(), E = (int)hp.ev_thr.size();
     if (n_tasks) *n_tasks = T;
@@ -117,12 +118,13 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts, mk_task_i
       mk_task_info &q = tasks[i];
       std::memset(&q, 0, sizeof q);
       q.op = t.op; q.layer = t.layer;
-      q.a0 = t.a0; q.a1 = t.a1; q.a2 = t.a2; q.a3 = t.a3; q.a4 = t.a4; q.a5 = t.a5;
+      q.a0 = t.a0; q.a1 = t.a1; q.a2 = t.a2; q.a3 = t.a3; q.a4 = t.a4; q.sig_count = t.a5;
       q.n_wait = t.n_wait;
       for (int k = 0; k < 3; ++k) q.wait_ev[k] = k < t.n_wait ? t.wait_ev[k] : -1;
       q.n_sig = t.n_sig;
       for (int k = 0; k < 2; ++k) q.sig_ev[k] = k < t.n_sig ? t.sig_ev[k] : -1;
       q.phase = hp.task_phase[i];
+      q.worker = hp.task_worker[i];
       q.bytes = hp.task_bytes[i];
     }
     for (int e = 0; ev_thresholds && e < E && e < ev_cap; ++e) ev_thresholds[e] = hp.ev_thr[e];
@@ -133,6 +135,96 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts, mk_task_i
 }
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Fill the device addresses of every GEMV task (weights of its tile, input
+// activations, output and residual) once the plan's buffers exist.  `tab`
+// holds the per-layer weight pointers in check_weights' order.
+static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, const mk_weights &w,
+                          const DevPlan &d) {
+  const mk_config &c = hp.cfg;
+  const int L = c.n_layers, B = c.max_batch, H = c.hidden;
+  const int QD = c.n_q_heads * c.head_dim, KVD = c.n_kv_heads * c.head_dim;
+  const int F = c.ffn_dim, E = c.n_experts, TK = c.top_k, Fe = c.expert_ffn_dim;
+  auto W = [&](int kind, int l) { return (const uint16_t *)tab[(size_t)kind * L + l]; };
+  for (Task &t : hp.tasks) {
+    const int l = t.layer;
+    t.w0 = t.w1 = nullptr;
+    t.src = t.aux = nullptr;
+    t.dst = nullptr;
+    t.gain = nullptr;
+    t.K = 0;
+    t.ostride = 0;
+    switch (t.op) {
+      case OP_QKV: {
+        const int Nm = t.a0 == 0 ? QD : KVD;
+        float *base = t.a0 == 0 ? d.q : (t.a0 == 1 ? d.k : d.v);
+        t.w0 = W(2 + t.a0, l) + (size_t)t.a1 * H;
+        t.src = d.x + (size_t)l * B * H;
+        t.gain = W(0, l);
+        t.K = H;
+        t.dst = base + (size_t)l * B * Nm + t.a1;
+        t.ostride = Nm;
+        break;
+      }
+      case OP_OPROJ:
+        t.w0 = W(5, l) + (size_t)t.a1 * QD;
+        t.src = d.attn + (size_t)l * B * QD;
+        t.K = QD;
+        t.dst = d.xmid + (size_t)l * B * H + t.a1;
+        t.aux = d.x + (size_t)l * B * H + t.a1;
+        t.ostride = H;
+        break;
+      case OP_GATEUP:
+        t.w0 = W(6, l) + (size_t)t.a1 * H;
+        t.w1 = W(7, l) + (size_t)t.a1 * H;
+        t.src = d.xmid + (size_t)l * B * H;
+        t.gain = W(1, l);
+        t.K = H;
+        t.dst = d.h + (size_t)l * B * F + t.a1;
+        t.ostride = F;
+        break;
+      case OP_DOWN:
+        t.w0 = W(8, l) + (size_t)t.a1 * F;
+        t.src = d.h + (size_t)l * B * F;
+        t.K = F;
+        t.dst = d.x + (size_t)(l + 1) * B * H + t.a1;
+        t.aux = d.xmid + (size_t)l * B * H + t.a1;
+        t.ostride = H;
+        break;
+      case OP_ROUTER:
+        t.w0 = W(9, l) + (size_t)t.a1 * H;
+        t.src = d.xmid + (size_t)l * B * H;
+        t.gain = W(1, l);
+        t.K = H;
+        t.dst = d.rl + (size_t)l * B * E + t.a1;
+        t.ostride = E;
+        break;
+      case OP_LMHEAD:
+        t.w0 = (const uint16_t *)w.lm_head + (size_t)t.a1 * H;
+        t.src = d.x + (size_t)L * B * H;
+        t.gain = (const uint16_t *)w.final_norm;
+        t.K = H;
+        break;
+      case OP_EGATEUP: {
+        const size_t bj = ((size_t)l * B + t.a0) * TK + t.a3;
+        t.src = d.xmid + ((size_t)l * B + t.a0) * H;
+        t.gain = W(1, l);
+        t.K = H;
+        t.dst = d.he + bj * Fe + t.a1;
+        break;
+      }
+      case OP_EDOWN: {
+        const size_t bj = ((size_t)l * B + t.a0) * TK + t.a3;
+        t.src = d.he + bj * Fe;
+        t.K = Fe;
+        t.dst = d.ye + bj * H + t.a1;
+        break;
+      }
+      default:
+        break;
+    }
+  }
+}
 
 static int check_weights(const mk_config &c, const mk_weights &w, std::vector<const void *> &tab,
                          std::string &err) {
@@ -225,7 +317,9 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     const int hw_cus = prop.multiProcessorCount;
     const int n_cus = o.n_cus > 0 ? o.n_cus : hw_cus;
     p->grid = o.n_workgroups > 0 ? o.n_workgroups : hw_cus;
-    rc = build_host_plan(*cfg, o, n_cus, p->hp, err);
+    if (p->grid > hw_cus)
+      return fail(MK_ERR_INVALID_ARG, "more persistent workers than CUs (one resident workgroup per CU)");
+    rc = build_host_plan(*cfg, o, n_cus, p->grid, p->hp, err);
     if (rc != MK_OK) return fail(rc, err);
     HostPlan &hp = p->hp;
     const mk_config &c = hp.cfg;
@@ -240,6 +334,9 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     // device allocations
     Task *d_tasks;
     if ((rc = p->alloc(&d_tasks, T, "task table"))) return rc;
+    int32_t *d_wq;
+    if ((rc = p->alloc(&d_wq, hp.worker_off.size() + hp.worker_list.size(), "worker queues")))
+      return rc;
     p->n_ctrl_words = CTRL_WORDS + E;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
     const int64_t nf = hp.n_x + hp.n_xmid + hp.n_q + 2 * hp.n_k + hp.n_part + hp.n_attn + hp.n_h +
@@ -258,10 +355,10 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     if ((rc = p->alloc(&p->stage_logits, (size_t)B * c.vocab, "prefill logits"))) return rc;
 
     // uploads
-    HIP_TRY(hipMemcpy(d_tasks, hp.tasks.data(), (size_t)T * sizeof(Task), hipMemcpyHostToDevice),
-            "upload tasks");
     HIP_TRY(hipMemcpy(d_tab, tab.data(), tab.size() * sizeof(void *), hipMemcpyHostToDevice),
             "upload weight tables");
+    HIP_TRY(hipMemcpy(d_wq, hp.worker_off.data(), hp.worker_off.size() * 4, hipMemcpyHostToDevice),
+            "upload worker queues");
     {
       // rotary tables: angle p * theta^(-2i/hd) and its cos/sin in double,
       // rounded once to float
@@ -319,8 +416,29 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.ev = p->ctrl + CTRL_WORDS;
     d.tasks = d_tasks;
     d.n_tasks = T;
+    d.worker_off = d_wq;
+    d.task_pos = d_wq + hp.worker_off.size();
+    d.n_workers = hp.n_workers;
     d.spin_budget = o.spin_budget > 0 ? o.spin_budget : 100000000LL;  // 1 s at 100 MHz
     d.trace = trace;
+    d.trace_mode = o.debug_trace;
+    resolve_tasks(hp, tab, *w, d);
+    {
+      // device table in worker-major order, plus list index -> position
+      std::vector<Task> stream((size_t)T);
+      std::vector<int32_t> pos((size_t)T);
+      for (int k = 0; k < T; ++k) {
+        const int g = hp.worker_list[k];
+        stream[k] = hp.tasks[g];
+        stream[k].gidx = g;
+        pos[g] = k;
+      }
+      HIP_TRY(hipMemcpy(d_tasks, stream.data(), (size_t)T * sizeof(Task), hipMemcpyHostToDevice),
+              "upload tasks");
+      HIP_TRY(hipMemcpy(d_wq + hp.worker_off.size(), pos.data(), (size_t)T * 4,
+                        hipMemcpyHostToDevice),
+              "upload task positions");
+    }
     if ((rc = p->alloc(&p->d_dev, 1, "plan copy"))) return rc;
     HIP_TRY(hipMemcpy(p->d_dev, &d, sizeof d, hipMemcpyHostToDevice), "upload plan");
     *out = p.release();

@@ -2,22 +2,27 @@
 //
 // The persistent kernel follows the Cohere megakernel article ("Egyetlen
 // tartós kernelre épül a kiszolgálás"): exactly one workgroup per CU stays
-// resident for the whole step and works from the host-prepared task list;
-// dependencies are counters in global memory.  The worker loop is the one the
-// Mirage MPK summary describes ("Part 2. Runtime", Worker): take the next
-// task, run it, notify its event, repeat.  Tasks are taken from one atomic
-// ticket counter in list order, which the planner makes a topological order,
-// so the lowest unfinished ticket always has its inputs ready and the loop is
-// deadlock-free even without co-residency guarantees.
+// resident for the whole step and works from a task list the host prepared;
+// dependencies are counters in global memory.  Each workgroup is one worker of
+// the Mirage MPK runtime ("Part 2. Runtime", Worker): it runs its own queue of
+// tasks in order and bumps event counters as tasks finish.  Inside the
+// workgroup the roles MPK gives to separate SMs are split between waves: wave
+// 0 is the control wave (it polls dependency counters, keeps the next task
+// descriptors in an LDS ring, writes a tile's outputs and signals), waves 1..7
+// only stream weights and compute.  Keeping control traffic out of the
+// compute waves matters on gfx950, where one counter (vmcnt) tracks all of a
+// wave's outstanding loads and stores: a wave that polls or drains its stores
+// would also wait for its weight prefetches.
 //
-// Before a task waits for its producers it already issues the loads of its
-// own weight tile (weights never change, so they may be read early): the
-// Cohere article's weight prefetch ("Honnan jön a gyorsulás?").
+// Weights never change, so the compute waves load the next tile's weights
+// while the current tile is still being reduced and published, and before the
+// next tile's inputs are ready: the Cohere article's weight prefetch ("Honnan
+// jön a gyorsulás?").
 //
-// Memory ordering: a producer's outputs are made visible with an agent-scope
-// release fence before its counter increment; a consumer polls the counter
-// with relaxed loads and then issues an agent-scope acquire fence (on the
-// multi-XCD MI355X this writes back / invalidates the per-XCD L2 as needed).
+// Activations a task writes and another reads go through HBM with
+// agent-coherent (sc1) stores and loads; a producer's wave waits for its
+// stores to complete and then bumps the counter with a relaxed atomic, so no
+// L2 write-back or invalidate fence is needed on the multi-XCD MI355X.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -59,6 +64,14 @@ DEV uint16_t f2bf(float f) {  // round to nearest even
   return (uint16_t)(u >> 16);
 }
 DEV int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// The work-item id, re-materialised at each use: the opaque copy keeps the
+// compiler from hoisting lane-dependent offsets out of the worker loop and
+// holding them in registers for the whole kernel.
+DEV int tidx() {
+  int v = (int)threadIdx.x;
+  asm volatile("" : "+v"(v));
+  return v;
+}
 DEV float unif(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
 DEV float lanef(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
@@ -128,15 +141,124 @@ DEV void wave_argmax(float &v, int &i) {
   v = bv;
   i = bi;
 }
-DEV int vec_bytes(int K) { return ((K * 2) % 1024 == 0) ? 16 : 8; }
+
+// Activations that one task writes and another reads: agent-coherent
+// accesses (sc1: written through to memory, read past the per-XCD L2).
+DEV float lda(const float *p) {
+  return __hip_atomic_load((const AS1 float *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV void sta(float *p, float v) {
+  __hip_atomic_store((AS1 float *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV int ldai(const int32_t *p) {
+  return __hip_atomic_load((const AS1 int32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV void stai(int32_t *p, int32_t v) {
+  __hip_atomic_store((AS1 int32_t *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr int kCpolSc1 = 16;  // cache-policy bit: device-scope coherent
+DEV __amdgpu_buffer_rsrc_t rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+}
+// 16-byte coherent load at byte offset `off` from a uniform base
+DEV f32x4 lda4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1);
+}
+// wait until this wave's vector memory operations (its stores) completed
+DEV void vm_drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+constexpr int kPartSlot = kMaxTileUnits16 * 4;   // GEMV partials per slot of a tile
+constexpr int kRing = 4;                          // task descriptors kept ahead
 
 struct Smem {
-  float xs[kLdsXBytes / 4];                                // staged activations
-  float red[kMaxBatchGemv][kWaves][2 * kMaxChunks + 1];    // GEMV partial sums
-  float ybuf[kMaxBatchGemv][256];                          // LM-head tile rows
+  float xs[kLdsXBytes / 4];                                 // staged activations
+  float red[2][kMaxBatchGemv][kPartSlot];                   // GEMV partial sums
+  uint32_t ring[kRing][32];                                 // task descriptors
   float misc[64];
   int imisc[64];
 };
+
+// A task descriptor held in scalar registers.
+struct TD {
+  int op, layer, n_wait, n_sig, a0, a1, a2, a3, a4, a5;
+  int wait_ev[3], wait_thr[3], sig_ev[2];
+  const uint16_t *w0, *w1;
+  const float *src;
+  float *dst;
+  const float *aux;
+  const uint16_t *gain;
+  int K, ostride, gidx;
+};
+
+DEV const void *ptr_of(uint32_t lo, uint32_t hi) {
+  return (const void *)(((uint64_t)hi << 32) | lo);
+}
+// Decode the 32 words of a Task (layout in mk_task.h); `w` must be uniform.
+DEV TD decode_td(const uint32_t *w) {
+  TD t;
+  t.op = (int)(int16_t)(w[0] & 0xffffu);
+  t.layer = (int)(int16_t)(w[0] >> 16);
+  t.n_wait = (int)(int16_t)(w[1] & 0xffffu);
+  t.n_sig = (int)(int16_t)(w[1] >> 16);
+  t.a0 = (int)w[2]; t.a1 = (int)w[3]; t.a2 = (int)w[4]; t.a3 = (int)w[5];
+  t.a4 = (int)w[6]; t.a5 = (int)w[7];
+  for (int i = 0; i < 3; ++i) { t.wait_ev[i] = (int)w[8 + i]; t.wait_thr[i] = (int)w[11 + i]; }
+  t.sig_ev[0] = (int)w[14]; t.sig_ev[1] = (int)w[15];
+  t.w0 = (const uint16_t *)ptr_of(w[16], w[17]);
+  t.w1 = (const uint16_t *)ptr_of(w[18], w[19]);
+  t.src = (const float *)ptr_of(w[20], w[21]);
+  t.dst = (float *)ptr_of(w[22], w[23]);
+  t.aux = (const float *)ptr_of(w[24], w[25]);
+  t.gain = (const uint16_t *)ptr_of(w[26], w[27]);
+  t.K = (int)w[28]; t.ostride = (int)w[29]; t.gidx = (int)w[30];
+  return t;
+}
+// From the LDS ring (every lane reads the same words; made uniform).
+DEV TD td_from_ring(const uint32_t *slot) {
+  uint32_t w[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 v = ((const u32x4 *)slot)[i];
+    w[4 * i + 0] = (uint32_t)uni((int)v.x);
+    w[4 * i + 1] = (uint32_t)uni((int)v.y);
+    w[4 * i + 2] = (uint32_t)uni((int)v.z);
+    w[4 * i + 3] = (uint32_t)uni((int)v.w);
+  }
+  return decode_td(w);
+}
+// From global memory through the scalar cache (kernel-per-op launches).
+DEV TD td_from_table(const Task *tab, int pos) {
+  const AS4 uint32_t *p = (const AS4 uint32_t *)(tab + pos);
+  uint32_t w[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i] = p[i];
+  return decode_td(w);
+}
+
+// Per-worker uniform state carried from task to task (identical in every
+// wave, so uniform decisions need no communication).
+struct WState {
+  const float *x_src;      // LDS activation cache key: source, gain, row length
+  const uint16_t *x_gain;
+  int x_K, x_nb;
+  int sat_ev[2];           // recently satisfied waits (event, wanted count)
+  uint32_t sat_want[2];
+  int par;                 // partial-sum buffer parity
+};
+
+DEV void init_ws(WState &ws) {
+  ws.x_src = nullptr;
+  ws.x_gain = nullptr;
+  ws.x_K = 0;
+  ws.x_nb = 0;
+  ws.sat_ev[0] = ws.sat_ev[1] = -1;
+  ws.sat_want[0] = ws.sat_want[1] = 0;
+  ws.par = 0;
+}
 
 DEV void set_error(CP &d, uint32_t code, int task, int ev, uint32_t seen, uint32_t want) {
   if (atomicCAS(&d.ctrl[CTRL_ERR], 0u, code) == 0u) {
@@ -151,13 +273,28 @@ DEV bool error_set(CP &d) {
 }
 
 // ------------------------------------------------------- dependency waits --
-// Thread 0 polls each counter until it reaches (epoch+1)*threshold, then
-// issues one acquire fence; the barrier hands the result to the workgroup.
+// A task needs each of its events' counters to reach (epoch+1)*threshold.
+// Waits this worker already saw satisfied in this step are skipped without a
+// poll (tiles of one operation share their input event).  Otherwise thread 0
+// (control wave) polls; a barrier hands the outcome to the workgroup.
 // Returns false when the step is being drained after an error.
-DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, CT &t, int tix) {
-  if (threadIdx.x == 0) {
+DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws) {
+  bool need = false;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (i >= t.n_wait) break;
+    const int e = t.wait_ev[i];
+    const uint32_t want = (ca.epoch + 1u) * (uint32_t)t.wait_thr[i];
+    const bool seen = (ws.sat_ev[0] == e && ws.sat_want[0] == want) ||
+                      (ws.sat_ev[1] == e && ws.sat_want[1] == want);
+    need = need || !seen;
+  }
+  if (!need) return true;
+  if (tidx() == 0) {
     int ok = 1;
-    for (int i = 0; i < t.n_wait && ok; ++i) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (i >= t.n_wait || !ok) break;
       uint32_t *c = d.ev + t.wait_ev[i];
       const uint32_t want = (ca.epoch + 1u) * (uint32_t)t.wait_thr[i];
       uint32_t seen = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -169,94 +306,116 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, CT &t, int tix) {
           if ((int32_t)(seen - want) >= 0) break;
           if (error_set(d)) { ok = 0; break; }
           if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
-            set_error(d, DEVERR_TIMEOUT, tix, t.wait_ev[i], seen, want);
+            set_error(d, DEVERR_TIMEOUT, t.gidx, t.wait_ev[i], seen, want);
             ok = 0;
             break;
           }
         }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (ok && d.trace) {
-      uint32_t *tr = d.trace + (size_t)tix * 6;
-      stg(tr + 0, atomicAdd(&d.ctrl[CTRL_CLOCK], 1u));
-      atomicAdd(&tr[2], 1u);
-      stg(tr + 3, (uint32_t)blockIdx.x);
-      stg(tr + 4, (uint32_t)wall_clock64());
-    }
     sm.imisc[0] = ok;
   }
   __syncthreads();
-  return sm.imisc[0] != 0;
+  const bool ok = sm.imisc[0] != 0;
+  if (ok) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (i >= t.n_wait) break;
+      ws.sat_ev[1] = ws.sat_ev[0];
+      ws.sat_want[1] = ws.sat_want[0];
+      ws.sat_ev[0] = t.wait_ev[i];
+      ws.sat_want[0] = (ca.epoch + 1u) * (uint32_t)t.wait_thr[i];
+    }
+  }
+  return ok;
 }
 
-// All threads' outputs are complete after the barrier; thread 0 releases
-// them at agent scope and bumps the task's counters.
-DEV void signal_done(CP &d, CT &t, int tix) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (d.trace) {
-      uint32_t *tr = d.trace + (size_t)tix * 6;
-      stg(tr + 1, atomicAdd(&d.ctrl[CTRL_CLOCK], 1u));
-      stg(tr + 5, (uint32_t)wall_clock64());
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    for (int i = 0; i < t.n_sig; ++i)
-      __hip_atomic_fetch_add(d.ev + t.sig_ev[i], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Debug trace, 6 words per task: start / finish tickets from one shared
+// clock counter (trace mode 1 only: it serialises), run count, workgroup,
+// start / finish time (100 MHz).  Trace mode 2 keeps times only and uses
+// words 0 and 1 for intermediate time stamps.
+DEV void trace_start(CP &d, const TD &t) {
+  if (d.trace && tidx() == 0) {
+    uint32_t *tr = d.trace + (size_t)t.gidx * 6;
+    if (d.trace_mode == 1) stg(tr + 0, atomicAdd(&d.ctrl[CTRL_CLOCK], 1u));
+    atomicAdd(&tr[2], 1u);
+    stg(tr + 3, (uint32_t)blockIdx.x);
+    stg(tr + 4, (uint32_t)wall_clock64());
+  }
+}
+DEV void trace_finish(CP &d, const TD &t) {
+  if (d.trace && tidx() == 0) {
+    uint32_t *tr = d.trace + (size_t)t.gidx * 6;
+    if (d.trace_mode == 1) stg(tr + 1, atomicAdd(&d.ctrl[CTRL_CLOCK], 1u));
+    stg(tr + 5, (uint32_t)wall_clock64());
+  }
+}
+DEV void trace_mark(CP &d, const TD &t, int word) {
+  if (d.trace && d.trace_mode == 2 && tidx() == 0)
+    stg(d.trace + (size_t)t.gidx * 6 + word, (uint32_t)wall_clock64());
+}
+// Report the task's completions (a5 of them; 0 when a later task of the same
+// run reports them).  The caller (thread 0) has drained its wave's stores.
+DEV void signal_done(CP &d, const TD &t) {
+  if (tidx() == 0 && t.a5 > 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (i < t.n_sig)
+        __hip_atomic_fetch_add(d.ev + t.sig_ev[i], (uint32_t)t.a5, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ------------------------------------------------------------ GEMV tiles --
 // A tile is `nseg` blocks of `seg_rows` consecutive rows (row length K bf16)
-// cut at the same row offset (gate and up share a tile).  Its bytes are
-// streamed as wave-chunks: 64 lanes x one VW-byte load, contiguous in memory
-// (rows are a whole number of wave-chunks).  Wave w owns chunks
-// [w*cpw, (w+1)*cpw); every lane keeps its loads in registers (the prefetch),
-// multiplies them with the activations staged in LDS, and each wave reduces
-// the partial dot product of each row it touched; rows are then summed over
-// the waves that share them in fixed wave order (deterministic).
-template <int VW> struct VT;
-template <> struct VT<16> { typedef u32x4 T; static constexpr int N = kMaxChunks; };
-template <> struct VT<8> { typedef u32x2 T; static constexpr int N = 2 * kMaxChunks; };
+// cut at the same row offset (gate and up share a tile), read as one
+// flattened sequence of elements.  It is streamed as 1 KiB chunks (64 lanes x
+// 16 bytes); compute wave c owns chunks [c*cpw, (c+1)*cpw).  Every lane keeps
+// its loads in registers and multiplies them with the activations staged in
+// LDS; each 16-lane DPP row of a chunk (128 elements) is summed and stored as
+// one partial, so the partials of the tile are in element order.  Rows are
+// multiples of 256 elements, hence a row owns the contiguous partials
+// [r*K/128, (r+1)*K/128), which the epilogue adds up in a fixed order
+// (deterministic).  No lane-dependent branch is needed anywhere: a chunk's
+// address is a select between the two segment bases, the lane's column
+// advances by 512 mod K per chunk.
+typedef u32x4 Buf[kMaxChunks];  // one tile's weights, per lane (16-byte slots)
 
 struct Geo {
   const uint16_t *seg0, *seg1;
-  int seg_rows, K, wc, units, cpw;
+  uint32_t seg_bytes;  // bytes of the first segment
+  int K, units, cpw, step;
 };
 
-DEV Geo make_geo(const uint16_t *s0, const uint16_t *s1, int seg_rows, int nseg, int K, int vw) {
+DEV Geo make_geo(const uint16_t *s0, const uint16_t *s1, int seg_rows, int nseg, int K) {
   Geo g;
   g.seg0 = s0;
   g.seg1 = s1;
-  g.seg_rows = seg_rows;
+  g.seg_bytes = (uint32_t)seg_rows * (uint32_t)K * 2u;
   g.K = K;
-  g.wc = (K * 2) / (64 * vw);
-  g.units = nseg * seg_rows * g.wc;
-  g.cpw = (g.units + kWaves - 1) / kWaves;
+  g.units = (nseg * seg_rows * K) >> 9;
+  g.cpw = (g.units + kCW - 1) / kCW;
+  g.step = 512 % K;
   return g;
 }
+DEV int cw_chunks(const Geo &g, int cw) { return min(g.cpw, g.units - cw * g.cpw); }
 
-template <int VW>
-DEV void gemv_load(const Geo &g, typename VT<VW>::T *w) {
-  constexpr int N = VT<VW>::N;
-  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int u0 = wave * g.cpw;
-  const int cnt = min(g.cpw, g.units - u0);
-  int r = u0 / g.wc, c = u0 - r * g.wc;
+// Issue the loads of compute wave cw's chunks of a tile into w.
+DEV void load_slots(const Geo &g, Buf &w, int cw) {
+  const int cnt = cw_chunks(g, cw);
+  const uint32_t o0 = (uint32_t)(cw * g.cpw) * 1024u + (uint32_t)(tidx() & 63) * 16u;
+  const uint64_t b0 = (uint64_t)g.seg0, b1 = (uint64_t)g.seg1 - g.seg_bytes;
 #pragma unroll
-  for (int j = 0; j < N; ++j) {
+  for (int j = 0; j < kMaxChunks; ++j) {
     if (j < cnt) {
-      const bool s1 = r >= g.seg_rows;
-      const uint16_t *base = s1 ? g.seg1 : g.seg0;
-      const int rr = s1 ? r - g.seg_rows : r;
-      const uint16_t *p = base + (size_t)rr * g.K + c * (32 * VW) + lane * (VW / 2);
-      w[j] = ldnt((const typename VT<VW>::T *)p);
+      const uint32_t o = o0 + (uint32_t)j * 1024u;
+      const uint64_t a = (o < g.seg_bytes ? b0 : b1) + o;
+      w[j] = ldnt((const u32x4 *)a);
     }
-    if (++c == g.wc) { c = 0; ++r; }
   }
 }
 
-DEV float chunk_dot(const u32x4 &w, const float *x) {
+DEV float dot8(u32x4 w, const float *x) {
   const f32x4 a = *(const f32x4 *)x, b = *(const f32x4 *)(x + 4);
   float s = bf_lo(w.x) * a.x;
   s = fmaf(bf_hi(w.x), a.y, s);
@@ -268,65 +427,115 @@ DEV float chunk_dot(const u32x4 &w, const float *x) {
   s = fmaf(bf_hi(w.w), b.w, s);
   return s;
 }
-DEV float chunk_dot(const u32x2 &w, const float *x) {
-  const f32x4 a = *(const f32x4 *)x;
-  float s = bf_lo(w.x) * a.x;
-  s = fmaf(bf_hi(w.x), a.y, s);
-  s = fmaf(bf_lo(w.y), a.z, s);
-  s = fmaf(bf_hi(w.y), a.w, s);
-  return s;
+
+// Sum over the 16 lanes of each DPP row; every lane of the row gets it.
+DEV float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
 }
 
-template <int VW>
-DEV void gemv_dot(const Geo &g, const typename VT<VW>::T *w, const float *xs, float *red) {
-  constexpr int N = VT<VW>::N;
-  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int u0 = wave * g.cpw;
-  const int cnt = min(g.cpw, g.units - u0);
-  int c = u0 % g.wc;
-  float carry = 0.f;
-  int slot = 0;
+// Compute wave cw: the partials of its chunks with the staged activations xs
+// of one slot into part[4*chunk + DPP row].  When `pre`, each slot is
+// refilled with the next tile `gn` as soon as it has been used, so the next
+// tile streams in while this one is consumed.  The body is straight-line
+// code (uniform branches only), which lets the compiler wait for each slot
+// with "all but the newest loads done" instead of draining the queue.
+DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, bool pre,
+                   const Geo &gn) {
+  const int lane = tidx() & 63;
+  const int cnt = cw_chunks(g, cw);
+  const int ncnt = pre ? cw_chunks(gn, cw) : 0;
+  const int q0 = cw * g.cpw;
+  int col = (int)(((uint32_t)q0 * 512u + (uint32_t)lane * 8u) % (uint32_t)g.K);
+  float *pp = part + q0 * 4 + (lane >> 4);
+  const bool writer = (lane & 15) == 0;
+  const uint32_t no0 = (uint32_t)(cw * gn.cpw) * 1024u + (uint32_t)lane * 16u;
+  const uint64_t nb0 = (uint64_t)gn.seg0, nb1 = (uint64_t)gn.seg1 - gn.seg_bytes;
 #pragma unroll
-  for (int j = 0; j < N; ++j) {
+  for (int j = 0; j < kMaxChunks; ++j) {
     if (j < cnt) {
-      carry += chunk_dot(w[j], xs + c * (32 * VW) + lane * (VW / 2));
-      if (c == g.wc - 1 || j == cnt - 1) {
-        const float s = wave_sum(carry);
-        if (lane == 0) red[wave * (N + 1) + slot] = s;
-        ++slot;
-        carry = 0.f;
-      }
+      const float v = row16_sum(dot8(w[j], xs + col));
+      if (writer) pp[j * 4] = v;
+      col += g.step;
+      col = col >= g.K ? col - g.K : col;
     }
-    if (++c == g.wc) c = 0;
+    if (j < ncnt) {
+      const uint32_t o = no0 + (uint32_t)j * 1024u;
+      w[j] = ldnt((const u32x4 *)((o < gn.seg_bytes ? nb0 : nb1) + o));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep each refill right after its use
   }
 }
 
-template <int VW>
-DEV float gemv_row(const Geo &g, const float *red, int row) {
-  constexpr int N = VT<VW>::N;
-  const int uf = row * g.wc, ul = uf + g.wc - 1;
-  const int w0 = uf / g.cpw, w1 = ul / g.cpw;
+// The same for n > 1 staged slots (rows xs[b*K ..), partials at
+// part[b*kPartSlot ..)); the next tile is loaded after the last slot.
+DEV void gemv_dotn(const Geo &g, Buf &w, const float *xs, int n, float *part, int cw) {
+  const int lane = tidx() & 63;
+  const int cnt = cw_chunks(g, cw);
+  const int q0 = cw * g.cpw;
+  const bool writer = (lane & 15) == 0;
+  for (int b = 0; b < n; ++b) {
+    int col = (int)(((uint32_t)q0 * 512u + (uint32_t)lane * 8u) % (uint32_t)g.K);
+    float *pp = part + b * kPartSlot + q0 * 4 + (lane >> 4);
+    const float *xb = xs + b * g.K;
+#pragma unroll
+    for (int j = 0; j < kMaxChunks; ++j) {
+      if (j < cnt) {
+        const float v = row16_sum(dot8(w[j], xb + col));
+        if (writer) pp[j * 4] = v;
+        col += g.step;
+        col = col >= g.K ? col - g.K : col;
+      }
+    }
+  }
+}
+
+// Row `row` of the tile: the sum of its K/128 partials, in order.
+DEV float gemv_row(const Geo &g, const float *part, int row) {
+  const int ne = g.K >> 7;
+  const float2 *p = (const float2 *)(part + row * ne);
   float s = 0.f;
-  for (int w = w0; w <= w1; ++w) s += red[w * (N + 1) + (row - (w * g.cpw) / g.wc)];
+  for (int i = 0; i < (ne >> 1); ++i) {
+    const float2 v = p[i];
+    s += v.x;
+    s += v.y;
+  }
   return s;
 }
 
-// Copy nb activation rows src[b*stride + 0..K) into LDS; with a gain vector,
-// RMS-normalise each row: x / sqrt(mean(x^2) + eps) * gain.
-DEV void stage_x(Smem &sm, const float *src, size_t stride, int K, int nb, const uint16_t *gain,
+// Stage nb activation rows src[b*K .. +K) (written by other tasks) into LDS;
+// with a gain vector, RMS-normalise each row: x / sqrt(mean(x^2) + eps) * g.
+// All waves take part.  Skipped when the same rows are already staged (the
+// worker's previous tile of the same operation).  Ends with a barrier.
+DEV void stage_x(Smem &sm, WState &ws, const float *src, int K, int nb, const uint16_t *gain,
                  float eps) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (ws.x_src == src && ws.x_gain == gain && ws.x_K == K && ws.x_nb == nb) return;
+  const int tid = tidx(), lane = tid & 63, wave = tid >> 6;
+  const __amdgpu_buffer_rsrc_t r = rsrc(src);
   for (int b = 0; b < nb; ++b) {
-    const f32x4 *s4 = (const f32x4 *)(src + (size_t)b * stride);
     f32x4 *d4 = (f32x4 *)(sm.xs + (size_t)b * K);
     float ss = 0.f;
-    for (int i = tid; i < K / 4; i += kThreads) {
-      const f32x4 v = ldg(s4 + i);
-      d4[i] = v;
-      ss = fmaf(v.x, v.x, ss);
-      ss = fmaf(v.y, v.y, ss);
-      ss = fmaf(v.z, v.z, ss);
-      ss = fmaf(v.w, v.w, ss);
+    // Up to four 16-byte loads in flight per lane before any is consumed.
+    // K is a multiple of 256, so every range test below is wave-uniform.
+    for (int i0 = uni(wave) * 64; i0 < K / 4; i0 += 4 * kThreads) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (i0 + u * kThreads < K / 4)
+          v[u] = lda4(r, (uint32_t)((size_t)b * K * 4 + (size_t)(i0 + u * kThreads + lane) * 16));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (i0 + u * kThreads < K / 4) d4[i0 + u * kThreads + lane] = v[u];
+        ss = fmaf(v[u].x, v[u].x, ss);
+        ss = fmaf(v[u].y, v[u].y, ss);
+        ss = fmaf(v[u].z, v[u].z, ss);
+        ss = fmaf(v[u].w, v[u].w, ss);
+      }
     }
     if (gain) {
       ss = wave_sum(ss);
@@ -344,169 +553,146 @@ DEV void stage_x(Smem &sm, const float *src, size_t stride, int K, int nb, const
     }
     __syncthreads();
   }
+  ws.x_src = src;
+  ws.x_gain = gain;
+  ws.x_K = K;
+  ws.x_nb = nb;
 }
 
-// One GEMV task: resolve the tile, prefetch its weights, wait, stage the
-// input, multiply, reduce, run the operation's epilogue, signal.
-template <int VW>
-DEV void run_gemv(Smem &sm, CP &d, const CallArgs &ca, CT &t, int tix, bool persistent) {
-  constexpr int N = VT<VW>::N;
-  typename VT<VW>::T w[N];
-  const int op = t.op, l = t.layer, B = d.B, H = d.H;
-  const int a0 = t.a0, a1 = t.a1, seg_rows = t.a2, a3 = t.a3, a4 = t.a4;
-  const int QD = d.nq * d.hd;
-  const uint16_t *s0 = nullptr, *s1 = nullptr;
-  int nseg = 1, K = H, nb = B, bfirst = 0;
-  const float *src = nullptr;
-  const uint16_t *gain = nullptr;
-  const bool expert = (op == OP_EGATEUP || op == OP_EDOWN);
+DEV bool is_gemv(int op) {
+  return op == OP_QKV || op == OP_OPROJ || op == OP_GATEUP || op == OP_DOWN ||
+         op == OP_ROUTER || op == OP_LMHEAD || op == OP_EGATEUP || op == OP_EDOWN;
+}
+// weights known before the task's inputs are (prefetchable)
+DEV bool static_weights(int op) { return is_gemv(op) && op != OP_EGATEUP && op != OP_EDOWN; }
+DEV Geo static_geo(const TD &t) { return make_geo(t.w0, t.w1, t.a2, t.w1 ? 2 : 1, t.K); }
 
-  if (!expert) {
-    switch (op) {
-      case OP_QKV: {
-        const uint16_t *W = a0 == 0 ? tab(d.wq, l) : (a0 == 1 ? tab(d.wk, l) : tab(d.wv, l));
-        s0 = W + (size_t)a1 * H;
-        src = d.x + (size_t)l * B * H;
-        gain = tab(d.attn_norm, l);
-        break;
-      }
-      case OP_OPROJ:
-        K = QD;
-        s0 = tab(d.wo, l) + (size_t)a1 * K;
-        src = d.attn + (size_t)l * B * K;
-        break;
-      case OP_GATEUP:
-        s0 = tab(d.w_gate, l) + (size_t)a1 * H;
-        s1 = tab(d.w_up, l) + (size_t)a1 * H;
-        nseg = 2;
-        src = d.xmid + (size_t)l * B * H;
-        gain = tab(d.ffn_norm, l);
-        break;
-      case OP_DOWN:
-        K = d.F;
-        s0 = tab(d.w_down, l) + (size_t)a1 * K;
-        src = d.h + (size_t)l * B * K;
-        break;
-      case OP_ROUTER:
-        s0 = tab(d.router, l) + (size_t)a1 * H;
-        src = d.xmid + (size_t)l * B * H;
-        gain = tab(d.ffn_norm, l);
-        break;
-      default:  // OP_LMHEAD
-        s0 = d.lm_head + (size_t)a1 * H;
-        src = d.x + (size_t)d.L * B * H;
-        gain = d.final_norm;
-        break;
-    }
-    const Geo g0 = make_geo(s0, s1, seg_rows, nseg, K, VW);
-    gemv_load<VW>(g0, w);  // weight prefetch: before the dependency wait
-    if (persistent && !wait_deps(sm, d, ca, t, tix)) return;
-  } else {
-    if (persistent && !wait_deps(sm, d, ca, t, tix)) return;
-    bfirst = a0;
-    nb = 1;
-    const int pos = ldg(ca.positions + bfirst);
-    if (pos < 0) {  // empty slot: nothing to compute
-      if (persistent) signal_done(d, t, tix);
-      return;
-    }
-    const int e = uni(ldg(d.tk_ids + ((size_t)l * B + bfirst) * d.topk + a3));
-    if (e < 0 || e >= d.E) {
-      if (threadIdx.x == 0) set_error(d, DEVERR_BAD_INPUT, tix, -1, (uint32_t)e, (uint32_t)d.E);
-      if (persistent) signal_done(d, t, tix);
-      return;
-    }
-    const size_t le = (size_t)l * d.E + e;
-    if (op == OP_EGATEUP) {
-      s0 = tab(d.e_gate, le) + (size_t)a1 * H;
-      s1 = tab(d.e_up, le) + (size_t)a1 * H;
-      nseg = 2;
-      src = d.xmid + ((size_t)l * B + bfirst) * H;
-      gain = tab(d.ffn_norm, l);
-    } else {
-      K = d.Fe;
-      s0 = tab(d.e_down, le) + (size_t)a1 * K;
-      src = d.he + (((size_t)l * B + bfirst) * d.topk + a3) * K;
-    }
-    const Geo g0 = make_geo(s0, s1, seg_rows, nseg, K, VW);
-    gemv_load<VW>(g0, w);
+// Expert tiles: the expert the router chose for (slot, expert slot).
+// Returns false (and flags an error) for an out-of-range id.
+DEV bool expert_geo(CP &d, const TD &t, Geo &g) {
+  const int e = uni(ldai(d.tk_ids + ((size_t)t.layer * d.B + t.a0) * d.topk + t.a3));
+  if (e < 0 || e >= d.E) {
+    if (tidx() == 0) set_error(d, DEVERR_BAD_INPUT, t.gidx, -1, (uint32_t)e, (uint32_t)d.E);
+    return false;
   }
+  const size_t le = (size_t)t.layer * d.E + e;
+  if (t.op == OP_EGATEUP)
+    g = make_geo(tab(d.e_gate, le) + (size_t)t.a1 * d.H, tab(d.e_up, le) + (size_t)t.a1 * d.H,
+                 t.a2, 2, d.H);
+  else
+    g = make_geo(tab(d.e_down, le) + (size_t)t.a1 * d.Fe, nullptr, t.a2, 1, d.Fe);
+  return true;
+}
 
-  const Geo g = make_geo(s0, s1, seg_rows, nseg, K, VW);
+// Control wave: write the outputs of rows [0, rows) for slots b0..b0+n-1.
+DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const Geo &g, const float *red_base,
+                       int bfirst, int b0, int n) {
+  const int lane = tidx() & 63;
+  const int op = t.op, rows = t.a2;
+  const int bstride = kPartSlot;
+  if (op == OP_LMHEAD) {
+    for (int bi = 0; bi < n; ++bi) {
+      const int b = bfirst + b0 + bi;
+      const float *red = red_base + bi * bstride;
+      float bv = -INFINITY;
+      int bix = 0x7fffffff;
+      for (int i = lane; i < rows; i += 64) {
+        const float y = gemv_row(g, red, i);
+        if (ca.logits) stg(ca.logits + (size_t)b * d.V + t.a1 + i, y);
+        if (better(y, t.a1 + i, bv, bix)) { bv = y; bix = t.a1 + i; }
+      }
+      wave_argmax(bv, bix);
+      if (lane == 0) {
+        const size_t o = (size_t)b * d.n_lm_tiles + t.a4;
+        sta(d.amax_v + o, bv);
+        stai(d.amax_i + o, bix);
+      }
+    }
+    return;
+  }
+  const size_t os = (size_t)t.ostride;
+  for (int idx = lane; idx < n * rows; idx += 64) {
+    const int bi = idx / rows, i = idx - bi * rows;
+    const float *red = red_base + bi * bstride;
+    const float y = gemv_row(g, red, i);
+    float *dst = t.dst + (size_t)(b0 + bi) * os + i;
+    switch (op) {
+      case OP_OPROJ: case OP_DOWN:  // residual add
+        sta(dst, lda(t.aux + (size_t)(b0 + bi) * os + i) + y);
+        break;
+      case OP_GATEUP: case OP_EGATEUP:  // SwiGLU of the gate and up rows
+        sta(dst, silu(y) * gemv_row(g, red, rows + i));
+        break;
+      default:  // QKV, ROUTER, EDOWN
+        sta(dst, y);
+        break;
+    }
+  }
+}
+
+// One GEMV task.  `w` holds the compute waves' weights of this tile when
+// w_loaded (prefetched during the previous task).  When the next task `tn`
+// has static weights, the compute waves refill `w` with them right after
+// their dot products.  Returns false when the step is drained after an error.
+DEV bool run_gemv(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent, WState &ws,
+                  Buf &w, bool w_loaded, bool pre, const Geo &gn) {
+  const int wave = uni(tidx() >> 6), cw = wave - 1;
+  Geo g;
+  int nb = d.B, bfirst = 0;
+  if (!static_weights(t.op)) {
+    if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+    trace_start(d, t);
+    nb = 1;
+    bfirst = t.a0;
+    if (ldg(ca.positions + t.a0) < 0 || !expert_geo(d, t, g)) {
+      // empty slot (or a rejected expert id): nothing to compute
+      if (persistent && wave == 0) {
+        trace_finish(d, t);
+        signal_done(d, t);
+      }
+      return true;
+    }
+    if (cw >= 0) load_slots(g, w, cw);
+  } else {
+    g = static_geo(t);
+    if (!w_loaded && cw >= 0) load_slots(g, w, cw);
+    if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+    trace_start(d, t);
+  }
+  const int K = g.K;
   const int bb_max = min(kMaxBatchGemv, kLdsXBytes / (K * 4));
-  const int tid = threadIdx.x;
   for (int b0 = 0; b0 < nb; b0 += bb_max) {
     const int n = min(bb_max, nb - b0);
-    stage_x(sm, src + (size_t)b0 * K, K, K, n, gain, d.eps);
-    for (int bi = 0; bi < n; ++bi) gemv_dot<VW>(g, w, sm.xs + (size_t)bi * K, &sm.red[bi][0][0]);
-    __syncthreads();
-    for (int idx = tid; idx < n * seg_rows; idx += kThreads) {
-      const int bi = idx / seg_rows, i = idx - bi * seg_rows;
-      const int b = bfirst + b0 + bi;
-      const float *red = &sm.red[bi][0][0];
-      const float y = gemv_row<VW>(g, red, i);
-      const int r = a1 + i;
-      switch (op) {
-        case OP_QKV: {
-          const int Nm = a0 == 0 ? QD : d.nkv * d.hd;
-          float *dst = a0 == 0 ? d.q : (a0 == 1 ? d.k : d.v);
-          stg(dst + ((size_t)l * B + b) * Nm + r, y);
-          break;
-        }
-        case OP_OPROJ: {
-          const size_t o = ((size_t)l * B + b) * H + r;
-          stg(d.xmid + o, ldg(d.x + o) + y);
-          break;
-        }
-        case OP_GATEUP: {
-          const float u = gemv_row<VW>(g, red, seg_rows + i);
-          stg(d.h + ((size_t)l * B + b) * d.F + r, silu(y) * u);
-          break;
-        }
-        case OP_DOWN: {
-          const size_t o = ((size_t)l * B + b) * H + r;
-          stg(d.x + o + (size_t)B * H, ldg(d.xmid + o) + y);
-          break;
-        }
-        case OP_ROUTER:
-          stg(d.rl + ((size_t)l * B + b) * d.E + r, y);
-          break;
-        case OP_EGATEUP: {
-          const float u = gemv_row<VW>(g, red, seg_rows + i);
-          stg(d.he + (((size_t)l * B + b) * d.topk + a3) * d.Fe + r, silu(y) * u);
-          break;
-        }
-        case OP_EDOWN:
-          stg(d.ye + (((size_t)l * B + b) * d.topk + a3) * H + r, y);
-          break;
-        default:  // OP_LMHEAD
-          if (ca.logits) stg(ca.logits + (size_t)b * d.V + r, y);
-          sm.ybuf[bi][i] = y;
-          break;
-      }
-    }
-    if (op == OP_LMHEAD) {
-      __syncthreads();
-      // per-slot (max, lowest index) over this tile's rows, one wave per slot
-      const int wave = uni(tid >> 6), lane = tid & 63;
-      if (wave < n) {
-        float bv = -INFINITY;
-        int bix = 0x7fffffff;
-        for (int i = lane; i < seg_rows; i += 64) {
-          const float v = sm.ybuf[wave][i];
-          if (better(v, a1 + i, bv, bix)) { bv = v; bix = a1 + i; }
-        }
-        wave_argmax(bv, bix);
-        if (lane == 0) {
-          const size_t o = (size_t)(bfirst + b0 + wave) * d.n_lm_tiles + a4;
-          stg(d.amax_v + o, bv);
-          stg(d.amax_i + o, bix);
-        }
+    const bool last = b0 + n >= nb;
+    if (n < nb) ws.x_src = nullptr;  // chunked batch: no reuse
+    stage_x(sm, ws, t.src + (size_t)b0 * K, K, n, t.gain, d.eps);
+    trace_mark(d, t, 0);
+    float *red = &sm.red[ws.par][0][0];
+    if (cw >= 0) {
+      if (n == 1) {
+        gemv_dot1(g, w, sm.xs, red, cw, pre && last, gn);
+      } else {
+        gemv_dotn(g, w, sm.xs, n, red, cw);
+        if (pre && last) load_slots(gn, w, cw);
       }
     }
     __syncthreads();
+    trace_mark(d, t, 1);
+    if (wave == 0) gemv_epilogue(d, ca, t, g, red, bfirst, b0, n);
+    ws.par ^= 1;
+    if (n < nb) {
+      ws.x_src = nullptr;
+      __syncthreads();  // the next batch chunk restages xs and reuses red
+    }
   }
-  if (persistent) signal_done(d, t, tix);
+  if (persistent && wave == 0) {
+    // The epilogue's stores are all this wave's: drain them only where the
+    // run's completions are reported (the wait covers the earlier tasks too).
+    if (t.a5 > 0) vm_drain();
+    trace_finish(d, t);  // before the signal: consumers start after it
+    signal_done(d, t);
+  }
+  return true;
 }
 
 // -------------------------------------------------------------- attention --
@@ -518,10 +704,11 @@ DEV void run_gemv(Smem &sm, CP &d, const CallArgs &ca, CT &t, int tix, bool pers
 // scores; the task leaves (max, sum, weighted values) for the merge, or the
 // normalised output when there is a single split.
 template <int HD>
-DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, CT &t, int tix) {
+DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
+  const int tix = t.gidx;
   const int l = t.layer, b = t.a0, g = t.a1, sp = t.a2;
   const int G = d.G, S = d.S, B = d.B, nkv = d.nkv, nq = d.nq;
-  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  const int tid = tidx(), lane = tid & 63, wave = uni(tid >> 6);
   constexpr int PS = HD + 4;
   float *qs = sm.xs;                         // [G][HD]
   float *kc = qs + kMaxGroup * HD;           // [HD]
@@ -539,11 +726,11 @@ DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, CT &t, int tix) {
     for (int idx = tid; idx < G * HD; idx += kThreads) {
       const int h = idx / HD, dd = idx - h * HD;
       if (S == 1) {
-        stg(d.attn + (head0 + h) * HD + dd, 0.f);
+        sta(d.attn + (head0 + h) * HD + dd, 0.f);
       } else {
         float *pp = d.part + ((head0 + h) * S + sp) * PS;
-        stg(pp + dd, 0.f);
-        if (dd == 0) { stg(pp + HD, -INFINITY); stg(pp + HD + 1, 0.f); }
+        sta(pp + dd, 0.f);
+        if (dd == 0) { sta(pp + HD, -INFINITY); sta(pp + HD + 1, 0.f); }
       }
     }
     return;
@@ -558,7 +745,7 @@ DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, CT &t, int tix) {
   const float *qg = d.q + head0 * HD;
   for (int idx = tid; idx < G * HD; idx += kThreads) {
     const int h = idx / HD, i = idx - h * HD, i0 = i & (HD / 2 - 1);
-    const float a = ldg(qg + h * HD + i0), c2 = ldg(qg + h * HD + i0 + HD / 2);
+    const float a = lda(qg + h * HD + i0), c2 = lda(qg + h * HD + i0 + HD / 2);
     const float cv = ldg(cs + i0), sv = ldg(sn + i0);
     const float r = (i < HD / 2) ? a * cv - c2 * sv : a * sv + c2 * cv;
     qs[h * HD + i] = r * scale;
@@ -570,10 +757,10 @@ DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, CT &t, int tix) {
     if (!pg_ok && tid == 0) set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pg, (uint32_t)d.npages);
     for (int i = tid; i < HD; i += kThreads) {
       const int i0 = i & (HD / 2 - 1);
-      const float a = ldg(d.k + kvo + i0), c2 = ldg(d.k + kvo + i0 + HD / 2);
+      const float a = lda(d.k + kvo + i0), c2 = lda(d.k + kvo + i0 + HD / 2);
       const float cv = ldg(cs + i0), sv = ldg(sn + i0);
       const float kr = (i < HD / 2) ? a * cv - c2 * sv : a * sv + c2 * cv;
-      const uint16_t kb = f2bf(kr), vb = f2bf(ldg(d.v + kvo + i));
+      const uint16_t kb = f2bf(kr), vb = f2bf(lda(d.v + kvo + i));
       kc[i] = bf1(kb);
       vc[i] = bf1(vb);
       if (pg_ok) {
@@ -703,62 +890,63 @@ DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, CT &t, int tix) {
       }
     }
     if (S == 1) {
-      stg(d.attn + (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f);
+      sta(d.attn + (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f);
     } else {
       float *pp = d.part + ((head0 + h) * S + sp) * PS;
-      stg(pp + dd, Os);
-      if (dd == 0) { stg(pp + HD, M); stg(pp + HD + 1, Ls); }
+      sta(pp + dd, Os);
+      if (dd == 0) { sta(pp + HD, M); sta(pp + HD + 1, Ls); }
     }
   }
 }
 
 // Log-sum-exp merge of the S split partials of one (slot, KV head).
-DEV void run_merge(CP &d, CT &t) {
+DEV void run_merge(CP &d, const TD &t) {
   const int l = t.layer, b = t.a0, g = t.a1, G = d.G, S = d.S, HD = d.hd;
   const int PS = HD + 4;
   const size_t head0 = ((size_t)l * d.B + b) * d.nq + (size_t)g * G;
-  for (int idx = threadIdx.x; idx < G * HD; idx += kThreads) {
+  for (int idx = tidx(); idx < G * HD; idx += kThreads) {
     const int h = idx / HD, dd = idx - h * HD;
     const float *pp = d.part + (head0 + h) * S * PS;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ldg(pp + s * PS + HD));
+    for (int s = 0; s < S; ++s) M = fmaxf(M, lda(pp + s * PS + HD));
     float Ls = 0.f, Os = 0.f;
     if (M != -INFINITY)
       for (int s = 0; s < S; ++s) {
-        const float ms = ldg(pp + s * PS + HD);
+        const float ms = lda(pp + s * PS + HD);
         if (ms == -INFINITY) continue;
         const float f = exp2f(ms - M);
-        Ls = fmaf(f, ldg(pp + s * PS + HD + 1), Ls);
-        Os = fmaf(f, ldg(pp + s * PS + dd), Os);
+        Ls = fmaf(f, lda(pp + s * PS + HD + 1), Ls);
+        Os = fmaf(f, lda(pp + s * PS + dd), Os);
       }
-    stg(d.attn + (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f);
+    sta(d.attn + (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f);
   }
 }
 
 // ------------------------------------------------------------- small ops --
-DEV void run_embed(CP &d, const CallArgs &ca, CT &t, int tix) {
+DEV void run_embed(CP &d, const CallArgs &ca, const TD &t) {
+  const int tix = t.gidx;
   const int b = t.a0, H = d.H;
   const int pos = uni(ldg(ca.positions + b));
   const int tok = uni(ldg(ca.tokens + b));
   const bool ok = pos >= 0 && tok >= 0 && tok < d.V;
-  if (pos >= 0 && !ok && threadIdx.x == 0)
+  if (pos >= 0 && !ok && tidx() == 0)
     set_error(d, DEVERR_BAD_INPUT, tix, -3, (uint32_t)tok, (uint32_t)d.V);
   float *x = d.x + (size_t)b * H;
   const uint16_t *e = d.embed + (size_t)(ok ? tok : 0) * H;
-  for (int i = threadIdx.x; i < H; i += kThreads) stg(x + i, ok ? bf1(ldg(e + i)) : 0.f);
+  for (int i = tidx(); i < H; i += kThreads) sta(x + i, ok ? bf1(ldg(e + i)) : 0.f);
 }
 
 // Softmax router top-k: k rounds of (max, lowest index) over the logits not
 // yet taken; weights = softmax over the chosen logits; ids ascending.
-DEV void run_topk(Smem &sm, CP &d, CT &t) {
+DEV void run_topk(Smem &sm, CP &d, const TD &t) {
   const int l = t.layer, b = t.a0, E = d.E, K = d.topk;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tidx(), lane = tid & 63, wave = tid >> 6;
   const float *r = d.rl + ((size_t)l * d.B + b) * E;
   float *vals = sm.xs;
   int *taken = (int *)(sm.xs + kThreads);
   int *ids = sm.imisc + 8;            // [16]
   float *lg = sm.misc + 32;           // [16]
-  for (int i = tid; i < E; i += kThreads) { vals[i] = ldg(r + i); taken[i] = 0; }
+  for (int i = tid; i < E; i += kThreads) { vals[i] = lda(r + i); taken[i] = 0; }
   __syncthreads();
   for (int j = 0; j < K; ++j) {
     float bv = -INFINITY;
@@ -792,34 +980,34 @@ DEV void run_topk(Smem &sm, CP &d, CT &t) {
     for (int j = 0; j < K; ++j) { sm.misc[48 + j] = expf(lg[j] - mx); wsum += sm.misc[48 + j]; }
     const size_t o = ((size_t)l * d.B + b) * K;
     for (int j = 0; j < K; ++j) {
-      stg(d.tk_ids + o + j, ids[j]);
-      stg(d.tk_w + o + j, sm.misc[48 + j] / wsum);
+      stai(d.tk_ids + o + j, ids[j]);
+      sta(d.tk_w + o + j, sm.misc[48 + j] / wsum);
     }
   }
 }
 
-DEV void run_combine(CP &d, const CallArgs &ca, CT &t) {
+DEV void run_combine(CP &d, const CallArgs &ca, const TD &t) {
   const int l = t.layer, b = t.a0, H = d.H, K = d.topk, B = d.B;
   const bool active = ldg(ca.positions + b) >= 0;
   const size_t xo = ((size_t)l * B + b) * H;
   const float *w = d.tk_w + ((size_t)l * B + b) * K;
   const float *y = d.ye + ((size_t)l * B + b) * K * H;
   const int r0 = t.a1, r1 = t.a1 + t.a2;
-  for (int i = r0 + threadIdx.x; i < r1; i += kThreads) {
+  for (int i = r0 + tidx(); i < r1; i += kThreads) {
     float acc = 0.f;
-    for (int j = 0; j < K; ++j) acc = fmaf(ldg(w + j), ldg(y + (size_t)j * H + i), acc);
-    stg(d.x + xo + (size_t)B * H + i, active ? ldg(d.xmid + xo + i) + acc : 0.f);
+    for (int j = 0; j < K; ++j) acc = fmaf(lda(w + j), lda(y + (size_t)j * H + i), acc);
+    sta(d.x + xo + (size_t)B * H + i, active ? lda(d.xmid + xo + i) + acc : 0.f);
   }
 }
 
-DEV void run_argmax(Smem &sm, CP &d, const CallArgs &ca, CT &t) {
+DEV void run_argmax(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
   const int b = t.a0, nt = d.n_lm_tiles;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tidx(), lane = tid & 63, wave = tid >> 6;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   for (int i = tid; i < nt; i += kThreads) {
-    const float v = ldg(d.amax_v + (size_t)b * nt + i);
-    const int ix = ldg(d.amax_i + (size_t)b * nt + i);
+    const float v = lda(d.amax_v + (size_t)b * nt + i);
+    const int ix = ldai(d.amax_i + (size_t)b * nt + i);
     if (better(v, ix, bv, bi)) { bv = v; bi = ix; }
   }
   wave_argmax(bv, bi);
@@ -835,29 +1023,16 @@ DEV void run_argmax(Smem &sm, CP &d, const CallArgs &ca, CT &t) {
   }
 }
 
-// ------------------------------------------------------------- dispatcher --
-DEV void run_task(Smem &sm, CP &d, const CallArgs &ca, int tix, bool persistent) {
-  CT &t = ((CT *)d.tasks)[tix];
-  const int op = t.op;
-  switch (op) {
-    case OP_QKV: case OP_OPROJ: case OP_GATEUP: case OP_DOWN: case OP_ROUTER:
-    case OP_LMHEAD: case OP_EGATEUP: case OP_EDOWN: {
-      int K = d.H;
-      if (op == OP_OPROJ) K = d.nq * d.hd;
-      else if (op == OP_DOWN) K = d.F;
-      else if (op == OP_EDOWN) K = d.Fe;
-      if (vec_bytes(K) == 16) run_gemv<16>(sm, d, ca, t, tix, persistent);
-      else run_gemv<8>(sm, d, ca, t, tix, persistent);
-      return;
-    }
-    default: break;
-  }
-  if (persistent && !wait_deps(sm, d, ca, t, tix)) return;
-  switch (op) {
-    case OP_EMBED: run_embed(d, ca, t, tix); break;
+// Non-GEMV task (all waves): wait, run, publish (every wave drains its
+// stores, then thread 0 reports).
+DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent, WState &ws) {
+  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  trace_start(d, t);
+  switch (t.op) {
+    case OP_EMBED: run_embed(d, ca, t); break;
     case OP_ATTN:
-      if (d.hd == 128) run_attn<128>(sm, d, ca, t, tix);
-      else run_attn<64>(sm, d, ca, t, tix);
+      if (d.hd == 128) run_attn<128>(sm, d, ca, t);
+      else run_attn<64>(sm, d, ca, t);
       break;
     case OP_MERGE: run_merge(d, t); break;
     case OP_TOPK: run_topk(sm, d, t); break;
@@ -865,45 +1040,103 @@ DEV void run_task(Smem &sm, CP &d, const CallArgs &ca, int tix, bool persistent)
     case OP_ARGMAX: run_argmax(sm, d, ca, t); break;
     default: break;
   }
-  if (persistent) signal_done(d, t, tix);
+  ws.x_src = nullptr;  // LDS reused: the activation cache is gone
+  if (persistent) vm_drain();
+  __syncthreads();
+  if (persistent) {
+    trace_finish(d, t);
+    signal_done(d, t);
+  }
+  return true;
 }
 
+// Run task t; `w` holds its weights when w_loaded.  When the worker's next
+// task has static weights (pre), their tile geometry is gn and this task
+// leaves them loading into `w`.  Returns whether it did; `alive` turns false
+// when the step is drained after an error.  Uniform across waves.
+DEV bool run_task(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent, WState &ws,
+                  Buf &w, bool w_loaded, bool pre, const Geo &gn, bool &alive) {
+  if (is_gemv(t.op)) {
+    alive = run_gemv(sm, d, ca, t, persistent, ws, w, w_loaded, pre, gn);
+    return alive && pre;
+  }
+  // The buffer holds nothing a later task reads (no task before this one
+  // prefetched for it): overwrite it so its registers are free during the
+  // small task.
+#pragma unroll
+  for (int j = 0; j < kMaxChunks; ++j) w[j] = (u32x4){0u, 0u, 0u, 0u};
+  alive = run_small(sm, d, ca, t, persistent, ws);
+  if (alive && pre) {
+    const int cw = uni(tidx() >> 6) - 1;
+    if (cw >= 0) load_slots(gn, w, cw);
+    return true;
+  }
+  return false;
+}
+
+// Geometry of the next task's tile from its descriptor words in the ring:
+// op (word 0), rows (a2, word 4), w0 / w1 (words 16-19), K (word 28).
+DEV bool next_geo(const uint32_t *slot, Geo &g) {
+  const int op = (int)(int16_t)(uni((int)slot[0]) & 0xffff);
+  if (!static_weights(op)) return false;
+  const int rows = uni((int)slot[4]);
+  const uint16_t *w0 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[16]), (uint32_t)uni((int)slot[17]));
+  const uint16_t *w1 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[18]), (uint32_t)uni((int)slot[19]));
+  const int K = uni((int)slot[28]);
+  g = make_geo(w0, w1, rows, w1 ? 2 : 1, K);
+  return true;
+}
+
+// The persistent worker runs its queue in order.  The control wave keeps the
+// descriptors of the current and the next task in an LDS ring (loaded two
+// tasks ahead); one register tile buffer carries each task's prefetched
+// weights into the next.
 __global__ void __launch_bounds__(kThreads)
     mk_persistent_kernel(const DevPlan *__restrict__ dplan, CallArgs ca) {
   __shared__ Smem sm;
-  __shared__ uint32_t s_ticket;
-  for (;;) {
-    // Re-read the plan through an opaque pointer every task so the compiler
-    // does not keep it live in registers across the loop.
-    CP *dp = (CP *)dplan;
-    asm volatile("" : "+s"(dp));
-    CP &d = *dp;
-    if (threadIdx.x == 0) {
-      uint32_t tk = atomicAdd(&d.ctrl[CTRL_TICKET], 1u);
-      if (error_set(d)) tk = 0xffffffffu;
-      s_ticket = tk;
-    }
-    __syncthreads();
-    const uint32_t t = (uint32_t)uni((int)s_ticket);
-    __syncthreads();
-    if (t >= (uint32_t)d.n_tasks) break;
-    run_task(sm, d, ca, (int)t, true);
+  CP &d = *(CP *)dplan;
+  const int wid = blockIdx.x;
+  const int beg = ((const AS4 int *)d.worker_off)[wid];
+  const int end = ((const AS4 int *)d.worker_off)[wid + 1];
+  const int wave = uni(tidx() >> 6), lane = tidx() & 63;
+  const u32x4 *tabv = (const u32x4 *)d.tasks;  // 8 x 16 bytes per descriptor
+  u32x4 pend = {0u, 0u, 0u, 0u};
+  if (wave == 0 && lane < 8) {
+    for (int i = 0; i < 2 && beg + i < end; ++i)
+      ((u32x4 *)sm.ring[i])[lane] = ldg(tabv + (size_t)(beg + i) * 8 + lane);
+    if (beg + 2 < end) pend = ldg(tabv + (size_t)(beg + 2) * 8 + lane);
   }
-  // the last workgroup out re-arms the ticket counter for the next step
-  if (threadIdx.x == 0) {
-    uint32_t *ctrl = ((CP *)dplan)->ctrl;
-    const uint32_t prev = atomicAdd(&ctrl[CTRL_DONE], 1u);
-    if (prev == gridDim.x - 1) {
-      atomicExch(&ctrl[CTRL_TICKET], 0u);
-      atomicExch(&ctrl[CTRL_DONE], 0u);
+  __syncthreads();
+  WState ws;
+  init_ws(ws);
+  Buf buf;
+  bool alive = true, loaded = false;
+  for (int k = beg; k < end; ++k) {
+    const int i = k - beg;
+    const TD t = td_from_ring(sm.ring[i % kRing]);
+    Geo gn;
+    const bool pre = k + 1 < end && next_geo(sm.ring[(i + 1) % kRing], gn);
+    if (wave == 0 && lane < 8) {  // ring refill, published by the task's barriers
+      if (k + 2 < end) ((u32x4 *)sm.ring[(i + 2) % kRing])[lane] = pend;
+      if (k + 3 < end) pend = ldg(tabv + (size_t)(k + 3) * 8 + lane);
     }
+    loaded = run_task(sm, d, ca, t, true, ws, buf, loaded, pre, gn, alive);
+    if (!alive) break;
   }
 }
 
 __global__ void __launch_bounds__(kThreads)
     mk_phase_kernel(const DevPlan *__restrict__ dplan, CallArgs ca, int first) {
   __shared__ Smem sm;
-  run_task(sm, *(CP *)dplan, ca, first + (int)blockIdx.x, false);
+  CP &d = *(CP *)dplan;
+  const int pos = ((const AS4 int *)d.task_pos)[first + (int)blockIdx.x];
+  const TD t = td_from_table(d.tasks, pos);
+  WState ws;
+  init_ws(ws);
+  Buf buf;
+  bool alive = true;
+  Geo gn;
+  run_task(sm, d, ca, t, false, ws, buf, false, false, gn, alive);
 }
 
 __global__ void mk_stage_kernel(int32_t *tok, int32_t *pos, int B, int slot,
@@ -920,9 +1153,12 @@ __global__ void mk_zero_kernel(uint32_t *p, int n) {
 }
 
 // ---------------------------------------------------------------- launch --
+// All workers must be resident at once (each may wait on any other), which a
+// cooperative launch guarantees or refuses.
 hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(mk_persistent_kernel, dim3(grid), dim3(kThreads), 0, s, d, ca);
-  return hipGetLastError();
+  void *args[] = {(void *)&d, (void *)&ca};
+  return hipLaunchCooperativeKernel((const void *)mk_persistent_kernel, dim3(grid), dim3(kThreads),
+                                    args, 0, s);
 }
 
 hipError_t launch_phase(const DevPlan *d, const CallArgs &ca, int first, int count,
@@ -944,6 +1180,6 @@ hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
-int persistent_lds_bytes() { return (int)sizeof(Smem) + 4; }
+int persistent_lds_bytes() { return (int)sizeof(Smem); }
 
 }  // namespace mk

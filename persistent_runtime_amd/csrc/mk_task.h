@@ -15,13 +15,17 @@
 namespace mk {
 
 // ---- workgroup geometry ---------------------------------------------------
-constexpr int kThreads = 512;          // one workgroup per CU, 8 wave64s
+// One workgroup per CU: wave 0 is the control wave (dependency polls, task
+// descriptors, output stores, signals); waves 1..7 stream weights and
+// compute.  Small tasks (attention, merges, routing, argmax) use all eight.
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-// A GEMV tile is streamed as "wave-chunks": 64 lanes x one vector load each.
-// kChunkBytes16: 64 lanes x 16 B; the 8-B variant is used when a row is not
-// a multiple of 1 KiB.  Each wave holds up to kMaxChunks 16-B loads per lane.
+constexpr int kCW = kWaves - 1;        // compute waves
+// A GEMV tile is streamed as "wave-chunks": 64 lanes x one vector load each
+// (16 B per lane; 8 B when a row is not a multiple of 1 KiB).  Each compute
+// wave holds up to kMaxChunks 16-byte loads per lane.
 constexpr int kMaxChunks = 16;
-constexpr int kMaxTileUnits16 = kWaves * kMaxChunks;        // 1 KiB units/tile
+constexpr int kMaxTileUnits16 = kCW * kMaxChunks;           // 1 KiB units/tile
 constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 8;           // query heads per KV head
 constexpr int kMaxBatchGemv = 4;       // slots a GEMV tile handles at once
@@ -47,14 +51,34 @@ enum Op : int16_t {
 //   COMBINE a0=slot a1=row0 a2=rows
 //   LMHEAD  a1=row0 a2=rows a4=tile index
 //   ARGMAX  a0=slot
+// a5 (every op): how many completions this task reports to its events.  A
+// worker that runs several consecutive tasks signalling the same events
+// reports them once, from the last task of the run (a5 = run length); the
+// others carry a5 = 0.
+// The second half is resolved by the C ABI once the plan's buffers exist, so
+// a task needs one scalar load and no chain of dependent table lookups:
+//   w0, w1  first weight row of the tile in segment 0 / 1 (experts: null,
+//           the expert is chosen at run time)
+//   src     activation input of slot 0 (slots are K apart)
+//   dst     output of slot 0 at the tile's first row (slots `ostride` apart)
+//   aux     residual input, indexed like dst (null when unused)
+//   gain    RMSNorm gain applied to src, or null
 struct alignas(16) Task {
   int16_t op, layer, n_wait, n_sig;
   int32_t a0, a1, a2, a3, a4, a5;
   int32_t wait_ev[3];
   int32_t wait_thr[3];
   int32_t sig_ev[2];
+  const uint16_t *w0, *w1;
+  const float *src;
+  float *dst;
+  const float *aux;
+  const uint16_t *gain;
+  int32_t K, ostride;
+  int32_t gidx;             // the task's index in list order
+  int32_t pad;
 };
-static_assert(sizeof(Task) == 64, "task descriptor is 64 bytes");
+static_assert(sizeof(Task) == 128, "task descriptor is 128 bytes");
 
 // control words (u32) at the head of the counter buffer
 enum Ctrl {
@@ -88,10 +112,14 @@ struct DevPlan {
   // control
   uint32_t *ev;            // event counters, after CTRL_WORDS control words
   uint32_t *ctrl;
-  const Task *tasks;
+  const Task *tasks;           // worker-major: each worker's queue is contiguous
   int32_t n_tasks;
+  const int32_t *worker_off;   // [n_workers + 1]: worker w runs tasks[off[w], off[w+1])
+  const int32_t *task_pos;     // list index -> position in `tasks`
+  int32_t n_workers;
   int64_t spin_budget;     // in s_memrealtime ticks (100 MHz)
   uint32_t *trace;         // 6 u32 per task, or null
+  int32_t trace_mode;      // 1: dependency tickets + times, 2: times only
 };
 
 // Per-step arguments, passed by value next to a device copy of DevPlan.

@@ -24,29 +24,24 @@
 namespace mk {
 
 int vec_bytes_for(int K) {
-  long rb = (long)K * 2;
-  if (K <= 0) return 0;
-  if (rb % 1024 == 0) return 16;
-  if (rb % 512 == 0) return 8;
-  return 0;
+  // rows are streamed in 16-byte lanes; 1 KiB chunks may straddle one row
+  // boundary at lane 32, which needs rows of a multiple of 512 bytes
+  if (K <= 0 || (K % 256) != 0) return 0;
+  return 16;
 }
 
-static int units_per_row(int K, int vw) { return (int)((long)K * 2 / (64L * vw)); }
-static int max_units(int vw) { return kMaxTileUnits16 * 16 / vw; }
-
 // Rows per tile for an operation over `total_rows` rows of K elements, with
-// `nseg` matrices cut at the same rows (gate and up).  If align > 0 the row
-// count must divide it (tiles never straddle a head boundary).
+// `nseg` matrices cut at the same rows (gate and up).  A tile holds at most
+// kMaxTileUnits16 chunks of 1 KiB and a whole number of them.  If align > 0
+// the row count must divide it (tiles never straddle a head boundary).
 static bool choose_tile(long total_rows, int K, int nseg, int n_cus, int align,
                         GemvShape &s) {
   s.vec_bytes = vec_bytes_for(K);
   if (!s.vec_bytes) return false;
-  int wc = units_per_row(K, s.vec_bytes);
-  int rmax = max_units(s.vec_bytes) / (wc * nseg);
-  if (rmax < 1) return false;
   double best = 0;
   int best_r = 0;
-  for (int r = 1; r <= rmax; ++r) {
+  for (int r = 1; (long)nseg * r * K <= (long)kMaxTileUnits16 * 512; ++r) {
+    if (((long)nseg * r * K) % 512) continue;
     if (align > 0 && align % r) continue;
     long tiles = (total_rows + r - 1) / r;
     long waves = (tiles + n_cus - 1) / n_cus;
@@ -81,7 +76,7 @@ int check_config(const mk_config &c, std::string &err) {
   } else {
     if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > 16)
       return bad("top_k must be in [1, min(n_experts, 16)]");
-    if (c.n_experts > kThreads) return bad("at most 512 experts");
+    if (c.n_experts > 512) return bad("at most 512 experts");
     if (c.expert_ffn_dim < 1) return bad("MoE model needs expert_ffn_dim > 0");
   }
   const int Ks[4] = {c.hidden, c.n_q_heads * c.head_dim,
@@ -146,10 +141,10 @@ struct Builder {
 }  // namespace
 
 int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
-                    HostPlan &p, std::string &err) {
+                    int n_workers, HostPlan &p, std::string &err) {
   int rc = check_config(c, err);
   if (rc != MK_OK) return rc;
-  if (n_cus < 1) { err = "n_cus < 1"; return MK_ERR_INVALID_ARG; }
+  if (n_cus < 1 || n_workers < 1) { err = "n_cus and n_workers must be >= 1"; return MK_ERR_INVALID_ARG; }
   p = HostPlan{};
   p.cfg = c;
   p.n_cus = n_cus;
@@ -179,17 +174,16 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     ok = ok && choose_tile(c.n_experts, H, 1, n_cus, 0, p.router) &&
          choose_tile((long)Fe * c.top_k * B, H, 2, n_cus, 0, p.egateup) &&
          choose_tile((long)H * c.top_k * B, Fe, 1, n_cus, 0, p.edown);
-    // expert tiles must not straddle experts: round rows to divisors
-    auto fit = [&](GemvShape &s, int rows) {
+    // expert tiles must not straddle experts: round rows to divisors that
+    // keep whole 1 KiB chunks
+    auto fit = [&](GemvShape &s, int rows, int K, int nseg) {
       int r = std::min(s.rows_per_tile, rows);
-      while (rows % r) --r;
+      while (r > 1 && (rows % r || ((long)nseg * r * K) % 512)) --r;
       s.rows_per_tile = r;
       s.tiles = rows / r;
+      return rows % r == 0 && ((long)nseg * r * K) % 512 == 0;
     };
-    if (ok) {
-      fit(p.egateup, Fe);
-      fit(p.edown, H);
-    }
+    if (ok) ok = fit(p.egateup, Fe, H, 2) && fit(p.edown, H, Fe, 1);
   }
   if (!ok) { err = "no tile shape fits the row lengths"; return MK_ERR_UNSUPPORTED; }
   p.n_lm_tiles = p.lmhead.tiles;
@@ -330,6 +324,62 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   // per-task thresholds
   for (auto &t : p.tasks)
     for (int i = 0; i < t.n_wait; ++i) t.wait_thr[i] = p.ev_thr[t.wait_ev[i]];
+
+  // Worker queues (the MPK runtime's per-worker task queues).  Each launch
+  // phase's tasks are dealt in contiguous blocks, so a worker's consecutive
+  // tiles are neighbours in memory (weight streams stay within DRAM and
+  // translation pages); when a phase does not divide evenly, the extra tasks
+  // go to the workers with the least bytes so far.  Every queue is a
+  // subsequence of the list order, which is topological, so with all workers
+  // resident the lowest unfinished task always has its inputs ready.
+  const int T = (int)p.tasks.size();
+  p.n_workers = n_workers;
+  p.task_worker.assign(T, 0);
+  std::vector<std::vector<int32_t>> q(n_workers);
+  std::vector<int64_t> load(n_workers, 0);
+  std::vector<int> order(n_workers);
+  for (auto &ph : p.phases) {
+    const int n = ph.second - ph.first;
+    const int base = n / n_workers, extra = n % n_workers;
+    // least-loaded workers take the extra tasks (ties: lower index)
+    for (int w = 0; w < n_workers; ++w) order[w] = w;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return load[a] < load[b]; });
+    std::vector<int> cnt(n_workers, base);
+    for (int k = 0; k < extra; ++k) cnt[order[k]]++;
+    int i = ph.first;
+    for (int w = 0; w < n_workers; ++w)
+      for (int k = 0; k < cnt[w]; ++k, ++i) {
+        q[w].push_back(i);
+        p.task_worker[i] = w;
+        load[w] += std::max<int64_t>(p.task_bytes[i], 16384);
+      }
+  }
+  // A run of consecutive tasks in one queue that signal the same events
+  // reports all its completions once, from its last task.
+  auto same_sig = [](const Task &a, const Task &b) {
+    if (a.n_sig != b.n_sig || a.n_sig == 0) return false;
+    for (int k = 0; k < a.n_sig; ++k)
+      if (a.sig_ev[k] != b.sig_ev[k]) return false;
+    return true;
+  };
+  p.worker_off.assign(n_workers + 1, 0);
+  p.worker_list.clear();
+  p.worker_list.reserve(T);
+  for (int w = 0; w < n_workers; ++w) {
+    const auto &lst = q[w];
+    size_t k = 0;
+    while (k < lst.size()) {
+      size_t j = k;
+      while (j + 1 < lst.size() && same_sig(p.tasks[lst[j]], p.tasks[lst[j + 1]])) ++j;
+      for (size_t m = k; m < j; ++m) p.tasks[lst[m]].a5 = 0;
+      p.tasks[lst[j]].a5 = (int)(j - k + 1);
+      k = j + 1;
+    }
+    p.worker_off[w] = (int32_t)p.worker_list.size();
+    p.worker_list.insert(p.worker_list.end(), lst.begin(), lst.end());
+  }
+  p.worker_off[n_workers] = (int32_t)p.worker_list.size();
   return validate_plan(p, err);
 }
 
@@ -383,6 +433,39 @@ int validate_plan(const HostPlan &p, std::string &err) {
       snprintf(buf, sizeof buf, "event %d is signalled but never waited on", e);
       err = buf;
       return MK_ERR_PLAN;
+    }
+  // completions reported per event equal its threshold; no self-waits
+  std::vector<int64_t> reported(E, 0);
+  for (int i = 0; i < T; ++i) {
+    const Task &t = p.tasks[i];
+    for (int k = 0; k < t.n_sig; ++k) {
+      reported[t.sig_ev[k]] += t.a5;
+      for (int m = 0; m < t.n_wait; ++m)
+        if (t.wait_ev[m] == t.sig_ev[k]) { err = "a task waits on an event it signals"; return MK_ERR_PLAN; }
+    }
+  }
+  for (int e = 0; e < E; ++e)
+    if (reported[e] != p.ev_thr[e]) {
+      snprintf(buf, sizeof buf, "event %d: %lld completions reported, threshold %d", e,
+               (long long)reported[e], p.ev_thr[e]);
+      err = buf;
+      return MK_ERR_PLAN;
+    }
+  // worker queues: a partition of the tasks, each queue increasing
+  if ((int)p.worker_off.size() != p.n_workers + 1 || (int)p.worker_list.size() != T) {
+    err = "worker queues do not partition the tasks";
+    return MK_ERR_PLAN;
+  }
+  std::vector<char> seen(T, 0);
+  for (int w = 0; w < p.n_workers; ++w)
+    for (int k = p.worker_off[w]; k < p.worker_off[w + 1]; ++k) {
+      const int ti = p.worker_list[k];
+      if (ti < 0 || ti >= T || seen[ti]) { err = "worker queues do not partition the tasks"; return MK_ERR_PLAN; }
+      seen[ti] = 1;
+      if (k > p.worker_off[w] && p.worker_list[k - 1] >= ti) {
+        err = "a worker queue is not in list order";
+        return MK_ERR_PLAN;
+      }
     }
   // phases tile the task list
   int pos = 0;

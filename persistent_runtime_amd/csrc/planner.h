@@ -28,6 +28,10 @@ struct HostPlan {
   std::vector<int32_t> task_phase;  // launch index under kernel-per-op
   std::vector<std::pair<int32_t, int32_t>> phases;  // [begin, end) per launch
   std::vector<int64_t> task_bytes;  // algorithmic bytes read per task
+  int n_workers = 0;                // persistent workgroups (one per CU)
+  std::vector<int32_t> task_worker; // worker that runs each task
+  std::vector<int32_t> worker_off;  // [n_workers + 1]
+  std::vector<int32_t> worker_list; // task indices per worker, in list order
   // scratch sizes in elements
   int64_t n_x = 0, n_xmid = 0, n_q = 0, n_k = 0, n_part = 0, n_attn = 0,
           n_h = 0, n_rl = 0, n_tk = 0, n_he = 0, n_ye = 0, n_amax = 0;
@@ -43,13 +47,15 @@ int vec_bytes_for(int K);
 // MK_ERR_UNSUPPORTED with a message.
 int check_config(const mk_config &c, std::string &err);
 
-// Lower cfg into a task graph sized for n_cus CUs.
+// Lower cfg into a task graph sized for n_cus CUs and give every one of
+// n_workers persistent workgroups its task queue.
 int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
-                    HostPlan &p, std::string &err);
+                    int n_workers, HostPlan &p, std::string &err);
 
 // Structural checks: every waited event is signalled only by earlier tasks
-// (ticket order is a topological order), thresholds equal the number of
-// signalling tasks, no event is left without a waiter except the last.
+// (list order is a topological order), thresholds equal the number of
+// completions reported, no task waits on an event it signals, every worker
+// queue is increasing in list order and reports each of its runs once.
 int validate_plan(const HostPlan &p, std::string &err);
 
 }  // namespace mk

@@ -75,10 +75,10 @@ class mk_plan_options(C.Structure):
 class mk_task_info(C.Structure):
     _fields_ = [("op", C.c_int32), ("layer", C.c_int32), ("a0", C.c_int32),
                 ("a1", C.c_int32), ("a2", C.c_int32), ("a3", C.c_int32),
-                ("a4", C.c_int32), ("a5", C.c_int32), ("n_wait", C.c_int32),
+                ("a4", C.c_int32), ("sig_count", C.c_int32), ("n_wait", C.c_int32),
                 ("wait_ev", C.c_int32 * 3), ("n_sig", C.c_int32),
                 ("sig_ev", C.c_int32 * 2), ("phase", C.c_int32),
-                ("bytes", C.c_int64)]
+                ("worker", C.c_int32), ("bytes", C.c_int64)]
 
 
 def _load():

@@ -285,6 +285,23 @@ def test_incremental_decode_equals_full_recompute_tiny():
         assert np.max(np.abs(lg - full[p])) < 1e-10, p
 
 
+def test_full_forward_cache_equals_incremental_cache():
+    cfg = TINY
+    W, Wt = _tiny_weights(cfg, np.float64)
+    toks = synth.make_prompt(17, cfg["vocab"]).tolist()
+    _, fc = O.forward_full(Wt, cfg, toks, return_cache=True)
+    ic = O.KVCache(cfg, np.float64)
+    for p, t in enumerate(toks):
+        O.decode_step(Wt, cfg, ic, t, p)
+    for l in range(cfg["n_layers"]):
+        assert np.allclose(fc.K[l], ic.K[l], atol=1e-12)
+        assert np.allclose(fc.V[l], ic.V[l], atol=1e-12)
+    # continuing from the full-forward cache gives the same next logits
+    a = O.decode_step(Wt, cfg, fc, 5, 17)
+    b = O.decode_step(Wt, cfg, ic, 5, 17)
+    assert np.max(np.abs(a - b)) < 1e-10
+
+
 def test_incremental_decode_equals_full_recompute_moe():
     cfg = dict(_tiny_moe_cfg(E=8, k=2), n_layers=2)
     W, Wt = _tiny_weights(cfg, np.float64)
