@@ -26,8 +26,8 @@ decode with a KV cache equals full causal recompute".
 """
 from .model import (rmsnorm, rope_cos_sin, rope, softmax, attention, silu,
                     swiglu, route_topk, KVCache, OracleWeights, decode_step,
-                    forward_full, greedy_argmax, top2_margin)
+                    forward_full, greedy_argmax, top2_margin, round_bf16)
 
 __all__ = ["rmsnorm", "rope_cos_sin", "rope", "softmax", "attention", "silu",
            "swiglu", "route_topk", "KVCache", "OracleWeights", "decode_step",
-           "forward_full", "greedy_argmax", "top2_margin"]
+           "forward_full", "greedy_argmax", "top2_margin", "round_bf16"]

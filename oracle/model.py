@@ -57,6 +57,19 @@ class OracleWeights:
 # ----------------------------------------------------------------------------
 # primitives
 # ----------------------------------------------------------------------------
+def round_bf16(x):
+    """Round to the nearest bfloat16 value (ties to even), kept in x's dtype.
+
+    bfloat16 keeps 8 significant bits and fp32's exponent range.  With
+    x = m * 2^e and 0.5 <= |m| < 1, the result is rint(m * 2^8) * 2^(e-8),
+    where rint rounds half to even.  Values are assumed inside the normal
+    range (|x| >= 2^-126), which holds for every cached key and value here.
+    """
+    x = np.asarray(x)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8).astype(x.dtype, copy=False)
+
+
 def rmsnorm(x, g, eps, dtype=np.float32):
     """RMSNorm: x / sqrt(mean(x^2) + eps) * g, over the last axis.
 
@@ -168,25 +181,34 @@ def top2_margin(logits):
 class KVCache:
     """Per-layer cached keys/values of one sequence, [T, nkv, hd] each.
 
-    The oracle keeps them in its working dtype (fp32), not bf16.
+    Reading: the cache stores keys (after the rotary embedding) and values in
+    bfloat16, the model's storage type (the pages keep the KV cache in paged
+    HBM blocks and name no other format); attention reads the stored values,
+    the current token's included.  With kv_bf16=True entries are rounded to
+    bfloat16 when stored (held in the working dtype); kv_bf16=False keeps
+    them unrounded.
     """
 
-    def __init__(self, cfg, dtype=np.float32, K=None, V=None):
+    def __init__(self, cfg, dtype=np.float32, K=None, V=None, kv_bf16=True):
         L = cfg["n_layers"]
         nkv, hd = cfg["n_kv_heads"], cfg["head_dim"]
+        self.kv_bf16 = kv_bf16
         if K is None:
             self.K = [np.zeros((0, nkv, hd), dtype) for _ in range(L)]
             self.V = [np.zeros((0, nkv, hd), dtype) for _ in range(L)]
         else:
-            self.K = [np.asarray(K[l], dtype=dtype) for l in range(L)]
-            self.V = [np.asarray(V[l], dtype=dtype) for l in range(L)]
+            self.K = [self._store(np.asarray(K[l], dtype=dtype)) for l in range(L)]
+            self.V = [self._store(np.asarray(V[l], dtype=dtype)) for l in range(L)]
+
+    def _store(self, a):
+        return round_bf16(a) if self.kv_bf16 else a
 
     def length(self):
         return self.K[0].shape[0]
 
     def append(self, layer, k, v):
-        self.K[layer] = np.concatenate([self.K[layer], k[None]], axis=0)
-        self.V[layer] = np.concatenate([self.V[layer], v[None]], axis=0)
+        self.K[layer] = np.concatenate([self.K[layer], self._store(k)[None]], axis=0)
+        self.V[layer] = np.concatenate([self.V[layer], self._store(v)[None]], axis=0)
 
 
 def _ffn(Wt, cfg, layer, b, dtype, forced=None, info=None):
@@ -249,15 +271,17 @@ def decode_step(Wt: OracleWeights, cfg: dict, cache: KVCache, token: int,
     return (logits, x) if return_hidden else logits
 
 
-def forward_full(Wt: OracleWeights, cfg: dict, tokens, return_cache=False):
+def forward_full(Wt: OracleWeights, cfg: dict, tokens, return_cache=False, kv_bf16=True):
     """Full causal forward over a whole token sequence (no cache reuse).
 
-    Position t attends to positions 0..t.  Returns logits [T, vocab].  This is
-    the recompute that incremental decoding must reproduce.  With
-    return_cache=True it also returns the rotated keys and values it computed,
-    as a KVCache ready for incremental decoding from position T.
+    Position t attends to positions 0..t, reading keys and values in the
+    cache's storage format (kv_bf16 as in KVCache).  Returns logits
+    [T, vocab].  This is the recompute that incremental decoding must
+    reproduce.  With return_cache=True it also returns the rotated keys and
+    values it computed, as a KVCache ready for incremental decoding from
+    position T.
     """
-    cache = KVCache(cfg, Wt.dtype) if return_cache else None
+    cache = KVCache(cfg, Wt.dtype, kv_bf16=kv_bf16) if return_cache else None
     dtype = Wt.dtype
     tokens = [int(t) for t in tokens]
     T = len(tokens)
@@ -272,6 +296,8 @@ def forward_full(Wt: OracleWeights, cfg: dict, tokens, return_cache=False):
         Vx = (A @ Wt.get("wv", l).T).reshape(T, nkv, hd)
         Q = rope(Q, cos[:, None, :], sin[:, None, :])
         Kx = rope(Kx, cos[:, None, :], sin[:, None, :])
+        if kv_bf16:
+            Kx, Vx = round_bf16(Kx), round_bf16(Vx)
         if cache is not None:
             cache.K[l], cache.V[l] = Kx.copy(), Vx.copy()
         O = np.empty_like(Q)

@@ -313,9 +313,11 @@ def test_incremental_decode_equals_full_recompute_moe():
         assert np.max(np.abs(lg - full[p])) < 1e-10, p
 
 
-def _torch_forward(W, cfg, toks):
+def _torch_forward(W, cfg, toks, kv_bf16=False):
     """An independent composition of torch library primitives (rms_norm,
-    complex-number rotation, causal SDPA with GQA, silu), float64."""
+    complex-number rotation, causal SDPA with GQA, silu), float64; with
+    kv_bf16 the rotated keys and the values pass through torch's bfloat16
+    conversion (from float32) before attention."""
     t = lambda a: torch.from_numpy(synth.bf16_to_f32_np(a).astype(np.float64))
     T = len(toks)
     H, nq, nkv, hd = cfg["hidden"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
@@ -334,6 +336,9 @@ def _torch_forward(W, cfg, toks):
         Q = rr((A @ t(W["wq"][l]).T).view(T, nq, hd))
         K = rr((A @ t(W["wk"][l]).T).view(T, nkv, hd))
         V = (A @ t(W["wv"][l]).T).view(T, nkv, hd)
+        if kv_bf16:
+            K = K.float().to(torch.bfloat16).double()
+            V = V.float().to(torch.bfloat16).double()
         o = F.scaled_dot_product_attention(Q.transpose(0, 1), K.transpose(0, 1),
                                            V.transpose(0, 1), is_causal=True,
                                            enable_gqa=True)
@@ -348,9 +353,46 @@ def test_full_forward_matches_independent_torch_composition():
     cfg = TINY
     W, Wt = _tiny_weights(cfg, np.float64)
     toks = synth.make_prompt(12, cfg["vocab"]).tolist()
-    ours = O.forward_full(Wt, cfg, toks)
+    ours = O.forward_full(Wt, cfg, toks, kv_bf16=False)
     ref = _torch_forward(W, cfg, toks)
     assert np.max(np.abs(ours - ref)) < 1e-9
+
+
+def test_full_forward_bf16_kv_matches_torch_composition():
+    """With the cache in bfloat16 the oracle rounds K and V from its float32
+    working values; torch rounds its own float32 values with its own
+    conversion.  A rounding decision could differ only where the two float32
+    values differ across a rounding boundary; on this seed none does, so the
+    logits agree to float32 accuracy, while skipping the rounding moves them
+    by about 2e-3."""
+    cfg = TINY
+    W, Wt = _tiny_weights(cfg, np.float32)
+    toks = synth.make_prompt(12, cfg["vocab"]).tolist()
+    ours = O.forward_full(Wt, cfg, toks)
+    ref = _torch_forward(W, cfg, toks, kv_bf16=True)
+    assert np.max(np.abs(ours.astype(np.float64) - ref)) < 1e-5
+    plain = O.forward_full(Wt, cfg, toks, kv_bf16=False).astype(np.float64)
+    assert np.max(np.abs(plain - ref)) > 5e-4
+
+
+def test_round_bf16_against_torch_and_ties():
+    g = np.random.default_rng(7)
+    x = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-30, 30, 20000),
+                        -g.standard_normal(1000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(O.round_bf16(x), ref)
+    # ties go to the even neighbour: 1 + 2^-8 lies halfway between 1 and
+    # 1 + 2^-7 (even: 1); 1 + 3*2^-8 halfway between 1 + 2^-7 (odd) and
+    # 1 + 2^-6 (even)
+    t = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3.0, 0.5 + 2.0 ** -10])
+    want = np.array([1.0, 1 + 2.0 ** -6, -1.0, 3.0, 0.5])
+    assert np.array_equal(O.round_bf16(t), want)
+    assert np.array_equal(O.round_bf16(t.astype(np.float32)), want.astype(np.float32))
+    # idempotent, and at most half a bf16 ulp away
+    r = O.round_bf16(x)
+    assert np.array_equal(O.round_bf16(r), r)
+    m, e = np.frexp(x.astype(np.float64))
+    assert np.all(np.abs(r.astype(np.float64) - x) <= np.ldexp(1.0, e - 9))
 
 
 def test_fp32_oracle_error_bound_vs_fp64_shadow():
@@ -358,7 +400,10 @@ def test_fp32_oracle_error_bound_vs_fp64_shadow():
     W, Wt32 = _tiny_weights(cfg, np.float32)
     Wt64 = O.OracleWeights(W, cfg, np.float64)
     toks = synth.make_prompt(39, cfg["vocab"]).tolist()
-    c32, c64 = O.KVCache(cfg, np.float32), O.KVCache(cfg, np.float64)
+    # the arithmetic error of the fp32 working type alone (no KV rounding,
+    # whose decisions could flip between the two precisions)
+    c32 = O.KVCache(cfg, np.float32, kv_bf16=False)
+    c64 = O.KVCache(cfg, np.float64, kv_bf16=False)
     worst = 0.0
     for p, t in enumerate(toks):
         a = O.decode_step(Wt32, cfg, c32, t, p)
