@@ -175,6 +175,8 @@ typedef struct {
   int32_t n_sig, sig_ev[2];
   int32_t phase;             /* launch index under KERNEL_PER_OP            */
   int32_t worker;            /* persistent workgroup whose queue holds it   */
+  int32_t rows_per_pass;     /* static-weight GEMVs: rows streamed per pass
+                                (one register tile); 0 for other tasks       */
   int64_t bytes;             /* algorithmic HBM bytes this task reads       */
 } mk_task_info;
 

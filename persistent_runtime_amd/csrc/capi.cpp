@@ -125,6 +125,7 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts, mk_task_i
       for (int k = 0; k < 2; ++k) q.sig_ev[k] = k < t.n_sig ? t.sig_ev[k] : -1;
       q.phase = hp.task_phase[i];
       q.worker = hp.task_worker[i];
+      q.rows_per_pass = t.rpp;
       q.bytes = hp.task_bytes[i];
     }
     for (int e = 0; ev_thresholds && e < E && e < ev_cap; ++e) ev_thresholds[e] = hp.ev_thr[e];
@@ -462,7 +463,8 @@ static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positi
       HIP_TRY(launch_zero_u32(d.trace, (int)plan->hp.tasks.size() * 6, s), "trace reset");
       HIP_TRY(launch_zero_u32(plan->ctrl + CTRL_CLOCK, 1, s), "trace reset");
     }
-    HIP_TRY(launch_persistent(plan->d_dev, ca, plan->grid, s), "persistent launch");
+    HIP_TRY(launch_persistent(plan->d_dev, ca, plan->grid, plan->hp.cfg.max_batch, s),
+            "persistent launch");
     if (++plan->epoch >= plan->epoch_limit) {
       HIP_TRY(launch_zero_u32(d.ev, (int)plan->hp.ev_thr.size(), s), "counter reset");
       plan->epoch = 0;

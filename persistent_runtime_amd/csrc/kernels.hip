@@ -172,11 +172,17 @@ DEV void vm_drain() {
 }
 
 constexpr int kPartSlot = kMaxTileUnits16 * 4;   // GEMV partials per slot of a tile
+constexpr int kRowSlot = kMaxTileUnits16 * 2;    // rows per tile (rows hold >= 256 elements)
+#ifndef MK_REFILL_PER_SLOT
+#define MK_REFILL_PER_SLOT 0
+#endif
+constexpr bool kRefillPerSlot = MK_REFILL_PER_SLOT;
 constexpr int kRing = 4;                          // task descriptors kept ahead
 
 struct Smem {
   float xs[kLdsXBytes / 4];                                 // staged activations
-  float red[2][kMaxBatchGemv][kPartSlot];                   // GEMV partial sums
+  float red[kMaxPass][kPartSlot];                           // GEMV partials [pass*n + slot]
+  float rows[kMaxPass][kRowSlot];                           // GEMV row sums, same order
   uint32_t ring[kRing][32];                                 // task descriptors
   float misc[64];
   int imisc[64];
@@ -191,7 +197,7 @@ struct TD {
   float *dst;
   const float *aux;
   const uint16_t *gain;
-  int K, ostride, gidx;
+  int K, ostride, gidx, rpp;
 };
 
 DEV const void *ptr_of(uint32_t lo, uint32_t hi) {
@@ -214,7 +220,7 @@ DEV TD decode_td(const uint32_t *w) {
   t.dst = (float *)ptr_of(w[22], w[23]);
   t.aux = (const float *)ptr_of(w[24], w[25]);
   t.gain = (const uint16_t *)ptr_of(w[26], w[27]);
-  t.K = (int)w[28]; t.ostride = (int)w[29]; t.gidx = (int)w[30];
+  t.K = (int)w[28]; t.ostride = (int)w[29]; t.gidx = (int)w[30]; t.rpp = (int)w[31];
   return t;
 }
 // From the LDS ring (every lane reads the same words; made uniform).
@@ -247,7 +253,6 @@ struct WState {
   int x_K, x_nb;
   int sat_ev[2];           // recently satisfied waits (event, wanted count)
   uint32_t sat_want[2];
-  int par;                 // partial-sum buffer parity
 };
 
 DEV void init_ws(WState &ws) {
@@ -257,7 +262,6 @@ DEV void init_ws(WState &ws) {
   ws.x_nb = 0;
   ws.sat_ev[0] = ws.sat_ev[1] = -1;
   ws.sat_want[0] = ws.sat_want[1] = 0;
-  ws.par = 0;
 }
 
 DEV void set_error(CP &d, uint32_t code, int task, int ev, uint32_t seen, uint32_t want) {
@@ -400,19 +404,24 @@ DEV Geo make_geo(const uint16_t *s0, const uint16_t *s1, int seg_rows, int nseg,
 }
 DEV int cw_chunks(const Geo &g, int cw) { return min(g.cpw, g.units - cw * g.cpw); }
 
+// Address of lane's 16 bytes of chunk j of compute wave cw in tile g; slots
+// beyond the wave's chunks read the tile's first chunk instead (always
+// inside the tile), so every slot is written by a load.  Unconditional loads
+// keep each slot in one register across tiles: a slot that a branch might
+// leave unchanged would be copied between registers, which forces a wait for
+// every load in flight.
+DEV uint64_t slot_addr(const Geo &g, int cw, int j) {
+  const uint32_t lane16 = (uint32_t)(tidx() & 63) * 16u;
+  const uint32_t o = (uint32_t)(cw * g.cpw + j) * 1024u + lane16;
+  const uint64_t b0 = (uint64_t)g.seg0, b1 = (uint64_t)g.seg1 - g.seg_bytes;
+  const uint64_t a = (o < g.seg_bytes ? b0 : b1) + o;
+  return j < cw_chunks(g, cw) ? a : b0 + lane16;
+}
+
 // Issue the loads of compute wave cw's chunks of a tile into w.
 DEV void load_slots(const Geo &g, Buf &w, int cw) {
-  const int cnt = cw_chunks(g, cw);
-  const uint32_t o0 = (uint32_t)(cw * g.cpw) * 1024u + (uint32_t)(tidx() & 63) * 16u;
-  const uint64_t b0 = (uint64_t)g.seg0, b1 = (uint64_t)g.seg1 - g.seg_bytes;
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
-    if (j < cnt) {
-      const uint32_t o = o0 + (uint32_t)j * 1024u;
-      const uint64_t a = (o < g.seg_bytes ? b0 : b1) + o;
-      w[j] = ldnt((const u32x4 *)a);
-    }
-  }
+  for (int j = 0; j < kMaxChunks; ++j) w[j] = ldnt((const u32x4 *)slot_addr(g, cw, j));
 }
 
 DEV float dot8(u32x4 w, const float *x) {
@@ -447,13 +456,13 @@ DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, b
                    const Geo &gn) {
   const int lane = tidx() & 63;
   const int cnt = cw_chunks(g, cw);
-  const int ncnt = pre ? cw_chunks(gn, cw) : 0;
   const int q0 = cw * g.cpw;
   int col = (int)(((uint32_t)q0 * 512u + (uint32_t)lane * 8u) % (uint32_t)g.K);
   float *pp = part + q0 * 4 + (lane >> 4);
   const bool writer = (lane & 15) == 0;
-  const uint32_t no0 = (uint32_t)(cw * gn.cpw) * 1024u + (uint32_t)lane * 16u;
-  const uint64_t nb0 = (uint64_t)gn.seg0, nb1 = (uint64_t)gn.seg1 - gn.seg_bytes;
+  // without a next tile the slots re-read this tile's first chunk
+  const Geo &gr = pre ? gn : g;
+  const int crw = pre ? cw : 0;
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
     if (j < cnt) {
@@ -462,10 +471,7 @@ DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, b
       col += g.step;
       col = col >= g.K ? col - g.K : col;
     }
-    if (j < ncnt) {
-      const uint32_t o = no0 + (uint32_t)j * 1024u;
-      w[j] = ldnt((const u32x4 *)((o < gn.seg_bytes ? nb0 : nb1) + o));
-    }
+    w[j] = ldnt((const u32x4 *)(pre ? slot_addr(gr, crw, j) : slot_addr(g, 0, kMaxChunks)));
     __builtin_amdgcn_sched_barrier(0);  // keep each refill right after its use
   }
 }
@@ -493,17 +499,27 @@ DEV void gemv_dotn(const Geo &g, Buf &w, const float *xs, int n, float *part, in
   }
 }
 
-// Row `row` of the tile: the sum of its K/128 partials, in order.
-DEV float gemv_row(const Geo &g, const float *part, int row) {
+// Row sums of a tile's R rows for n slots, over the compute waves: row r is
+// the sum of its K/128 partials part[r*K/128 ..).  A group of G lanes (the
+// power of two >= K/128, at most 64) takes one row, each lane a strided share
+// of the partials, then the group adds up by butterfly exchange (fixed order:
+// deterministic).
+DEV void gemv_rows(const Geo &g, int R, const float *part, float *rows, int n, int cw) {
+  const int lane = tidx() & 63;
   const int ne = g.K >> 7;
-  const float2 *p = (const float2 *)(part + row * ne);
-  float s = 0.f;
-  for (int i = 0; i < (ne >> 1); ++i) {
-    const float2 v = p[i];
-    s += v.x;
-    s += v.y;
+  const int G = ne >= 64 ? 64 : (1 << (32 - __builtin_clz((unsigned)ne - 1u)));
+  const int per = 64 / G;
+  const int sub = lane / G, j = lane - sub * G;
+  for (int b = 0; b < n; ++b) {
+    for (int r0 = cw * per; r0 < R; r0 += kCW * per) {
+      const int r = r0 + sub;
+      float v = 0.f;
+      if (r < R)
+        for (int e = j; e < ne; e += G) v += part[b * kPartSlot + r * ne + e];
+      for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o, 64);
+      if (j == 0 && r < R) rows[b * kRowSlot + r] = v;
+    }
   }
-  return s;
 }
 
 // Stage nb activation rows src[b*K .. +K) (written by other tasks) into LDS;
@@ -515,26 +531,36 @@ DEV void stage_x(Smem &sm, WState &ws, const float *src, int K, int nb, const ui
   if (ws.x_src == src && ws.x_gain == gain && ws.x_K == K && ws.x_nb == nb) return;
   const int tid = tidx(), lane = tid & 63, wave = tid >> 6;
   const __amdgpu_buffer_rsrc_t r = rsrc(src);
+  const u32x2 *g2 = (const u32x2 *)gain;  // four bf16 gains per 16-byte vector
   for (int b = 0; b < nb; ++b) {
     f32x4 *d4 = (f32x4 *)(sm.xs + (size_t)b * K);
     float ss = 0.f;
-    // Up to four 16-byte loads in flight per lane before any is consumed.
-    // K is a multiple of 256, so every range test below is wave-uniform.
+    // Up to four 16-byte loads (and their gains) in flight per lane before
+    // any is consumed.  K is a multiple of 256, so every range test below is
+    // wave-uniform.  LDS receives x * gain; the row's 1/rms follows below.
     for (int i0 = uni(wave) * 64; i0 < K / 4; i0 += 4 * kThreads) {
       f32x4 v[4];
+      u32x2 gv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         v[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        if (i0 + u * kThreads < K / 4)
-          v[u] = lda4(r, (uint32_t)((size_t)b * K * 4 + (size_t)(i0 + u * kThreads + lane) * 16));
+        gv[u] = (u32x2){0x3f803f80u, 0x3f803f80u};  // bf16 ones
+        if (i0 + u * kThreads < K / 4) {
+          const int i = i0 + u * kThreads + lane;
+          v[u] = lda4(r, (uint32_t)((size_t)b * K * 4 + (size_t)i * 16));
+          if (gain) gv[u] = ldg(g2 + i);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (i0 + u * kThreads < K / 4) d4[i0 + u * kThreads + lane] = v[u];
         ss = fmaf(v[u].x, v[u].x, ss);
         ss = fmaf(v[u].y, v[u].y, ss);
         ss = fmaf(v[u].z, v[u].z, ss);
         ss = fmaf(v[u].w, v[u].w, ss);
+        if (i0 + u * kThreads < K / 4)
+          d4[i0 + u * kThreads + lane] =
+              (f32x4){v[u].x * bf_lo(gv[u].x), v[u].y * bf_hi(gv[u].x), v[u].z * bf_lo(gv[u].y),
+                      v[u].w * bf_hi(gv[u].y)};
       }
     }
     if (gain) {
@@ -548,8 +574,8 @@ DEV void stage_x(Smem &sm, WState &ws, const float *src, int K, int nb, const ui
       float tot = 0.f;
       for (int w = 0; w < kWaves; ++w) tot += sm.misc[b * kWaves + w];
       const float rs = 1.0f / sqrtf(tot / (float)K + eps);
-      float *xb = sm.xs + (size_t)b * K;
-      for (int i = tid; i < K; i += kThreads) xb[i] = xb[i] * rs * bf1(ldg(gain + i));
+      f32x4 *xb = (f32x4 *)(sm.xs + (size_t)b * K);
+      for (int i = tid; i < K / 4; i += kThreads) xb[i] = xb[i] * rs;
     }
     __syncthreads();
   }
@@ -565,7 +591,19 @@ DEV bool is_gemv(int op) {
 }
 // weights known before the task's inputs are (prefetchable)
 DEV bool static_weights(int op) { return is_gemv(op) && op != OP_EGATEUP && op != OP_EDOWN; }
-DEV Geo static_geo(const TD &t) { return make_geo(t.w0, t.w1, t.a2, t.w1 ? 2 : 1, t.K); }
+// Passes of a static-weight task: rows [p*rpp, min((p+1)*rpp, a2)) of each
+// segment.
+DEV int task_rpp(int rpp, int rows) { return rpp > 0 && rpp < rows ? rpp : rows; }
+DEV int n_passes(const TD &t) {
+  const int r = task_rpp(t.rpp, t.a2);
+  return (t.a2 + r - 1) / r;
+}
+DEV Geo pass_geo(const uint16_t *w0, const uint16_t *w1, int rows, int rpp, int K, int p) {
+  const int r = task_rpp(rpp, rows);
+  const size_t off = (size_t)p * r * K;
+  return make_geo(w0 + off, w1 ? w1 + off : nullptr, min(r, rows - p * r), w1 ? 2 : 1, K);
+}
+DEV Geo static_geo(const TD &t) { return pass_geo(t.w0, t.w1, t.a2, t.rpp, t.K, 0); }
 
 // Expert tiles: the expert the router chose for (slot, expert slot).
 // Returns false (and flags an error) for an out-of-range id.
@@ -585,19 +623,24 @@ DEV bool expert_geo(CP &d, const TD &t, Geo &g) {
 }
 
 // Control wave: write the outputs of rows [0, rows) for slots b0..b0+n-1.
-DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const Geo &g, const float *red_base,
-                       int bfirst, int b0, int n) {
+DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const float *rsum, int bfirst,
+                       int b0, int n, float aux0, int rpp) {
   const int lane = tidx() & 63;
   const int op = t.op, rows = t.a2;
-  const int bstride = kPartSlot;
+  // output row i of slot bi: pass p = i / rpp, row r of the pass; the pass's
+  // row sums (segment 0 rows, then segment 1) are at rsum[(p*n + bi)*kRowSlot]
+  auto at = [&](int bi, int i, int seg) {
+    const int p = i / rpp, r = i - p * rpp;
+    const int rp = min(rpp, rows - p * rpp);
+    return rsum[(p * n + bi) * kRowSlot + seg * rp + r];
+  };
   if (op == OP_LMHEAD) {
     for (int bi = 0; bi < n; ++bi) {
       const int b = bfirst + b0 + bi;
-      const float *red = red_base + bi * bstride;
       float bv = -INFINITY;
       int bix = 0x7fffffff;
       for (int i = lane; i < rows; i += 64) {
-        const float y = gemv_row(g, red, i);
+        const float y = at(bi, i, 0);
         if (ca.logits) stg(ca.logits + (size_t)b * d.V + t.a1 + i, y);
         if (better(y, t.a1 + i, bv, bix)) { bv = y; bix = t.a1 + i; }
       }
@@ -613,15 +656,14 @@ DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const Geo &g, con
   const size_t os = (size_t)t.ostride;
   for (int idx = lane; idx < n * rows; idx += 64) {
     const int bi = idx / rows, i = idx - bi * rows;
-    const float *red = red_base + bi * bstride;
-    const float y = gemv_row(g, red, i);
+    const float y = at(bi, i, 0);
     float *dst = t.dst + (size_t)(b0 + bi) * os + i;
     switch (op) {
-      case OP_OPROJ: case OP_DOWN:  // residual add
-        sta(dst, lda(t.aux + (size_t)(b0 + bi) * os + i) + y);
+      case OP_OPROJ: case OP_DOWN:  // residual add (first pass: preloaded)
+        sta(dst, (idx < 64 ? aux0 : lda(t.aux + (size_t)(b0 + bi) * os + i)) + y);
         break;
       case OP_GATEUP: case OP_EGATEUP:  // SwiGLU of the gate and up rows
-        sta(dst, silu(y) * gemv_row(g, red, rows + i));
+        sta(dst, silu(y) * at(bi, i, 1));
         break;
       default:  // QKV, ROUTER, EDOWN
         sta(dst, y);
@@ -630,67 +672,142 @@ DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const Geo &g, con
   }
 }
 
-// One GEMV task.  `w` holds the compute waves' weights of this tile when
-// w_loaded (prefetched during the previous task).  When the next task `tn`
-// has static weights, the compute waves refill `w` with them right after
-// their dot products.  Returns false when the step is drained after an error.
-DEV bool run_gemv(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent, WState &ws,
-                  Buf &w, bool w_loaded, bool pre, const Geo &gn) {
-  const int wave = uni(tidx() >> 6), cw = wave - 1;
-  Geo g;
-  int nb = d.B, bfirst = 0;
+// ---- GEMV tasks, split by wave role ------------------------------------
+// Wave 0 (gemv_ctl) and waves 1-7 (gemv_cmp) run separate code for a GEMV
+// task and meet at the same barriers; both take every decision from the same
+// uniform data.  Keeping the two apart keeps the compute waves' code close to
+// a plain streaming loop, so the compiler holds each tile slot in one
+// register and waits for each slot's own load only.
+struct GemvShape2 {
+  Geo g;        // the first pass (static weights) or the expert tile
+  int nb, bfirst, P, rpp, bb_max;
+  bool skip;    // expert task of an empty slot or rejected expert: no work
+};
+
+// B1: compiled for plans with one slot (no slot chunks).
+template <bool B1>
+DEV GemvShape2 gemv_shape(CP &d, const CallArgs &ca, const TD &t) {
+  GemvShape2 q;
+  q.skip = false;
+  q.P = 1;
+  q.rpp = t.a2;
   if (!static_weights(t.op)) {
-    if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
-    trace_start(d, t);
-    nb = 1;
-    bfirst = t.a0;
-    if (ldg(ca.positions + t.a0) < 0 || !expert_geo(d, t, g)) {
-      // empty slot (or a rejected expert id): nothing to compute
-      if (persistent && wave == 0) {
-        trace_finish(d, t);
-        signal_done(d, t);
-      }
-      return true;
-    }
-    if (cw >= 0) load_slots(g, w, cw);
+    q.nb = 1;
+    q.bfirst = t.a0;
+    q.skip = ldg(ca.positions + t.a0) < 0 || !expert_geo(d, t, q.g);
   } else {
-    g = static_geo(t);
-    if (!w_loaded && cw >= 0) load_slots(g, w, cw);
-    if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
-    trace_start(d, t);
+    q.nb = B1 ? 1 : d.B;
+    q.bfirst = 0;
+    q.g = static_geo(t);
+    q.P = n_passes(t);
+    q.rpp = task_rpp(t.rpp, t.a2);
   }
-  const int K = g.K;
-  const int bb_max = min(kMaxBatchGemv, kLdsXBytes / (K * 4));
-  for (int b0 = 0; b0 < nb; b0 += bb_max) {
-    const int n = min(bb_max, nb - b0);
-    const bool last = b0 + n >= nb;
-    if (n < nb) ws.x_src = nullptr;  // chunked batch: no reuse
+  q.bb_max = B1 ? 1 : min(kMaxBatchGemv, kLdsXBytes / (q.g.K * 4));
+  return q;
+}
+// the planner never emits more passes x slots than the partial buffers hold
+DEV bool gemv_fits(CP &d, const TD &t, const GemvShape2 &q) {
+  if (q.P > 1 && q.P * min(q.nb, q.bb_max) > kMaxPass) {
+    if (tidx() == 0) set_error(d, DEVERR_BAD_INPUT, t.gidx, -1, (uint32_t)q.P, (uint32_t)q.nb);
+    return false;
+  }
+  return true;
+}
+
+// Control wave: dependencies, activation staging (shared), the residual
+// preload, the outputs, the completion signal.
+template <bool B1>
+DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
+                  WState &ws) {
+  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  trace_start(d, t);
+  const GemvShape2 q = gemv_shape<B1>(d, ca, t);
+  if (q.skip) {
+    if (persistent) {
+      trace_finish(d, t);
+      signal_done(d, t);
+    }
+    return true;
+  }
+  if (!gemv_fits(d, t, q)) return false;
+  const int K = q.g.K, lane = tidx() & 63;
+  for (int b0 = 0; b0 < q.nb; b0 += q.bb_max) {
+    const int n = min(q.bb_max, q.nb - b0);
+    if (n < q.nb) ws.x_src = nullptr;  // chunked batch: no reuse
     stage_x(sm, ws, t.src + (size_t)b0 * K, K, n, t.gain, d.eps);
     trace_mark(d, t, 0);
-    float *red = &sm.red[ws.par][0][0];
-    if (cw >= 0) {
-      if (n == 1) {
-        gemv_dot1(g, w, sm.xs, red, cw, pre && last, gn);
-      } else {
-        gemv_dotn(g, w, sm.xs, n, red, cw);
-        if (pre && last) load_slots(gn, w, cw);
-      }
+    // the residual of the first outputs, loaded while the compute waves work
+    float aux0 = 0.f;
+    if ((t.op == OP_OPROJ || t.op == OP_DOWN) && lane < n * t.a2) {
+      const int bi = lane / t.a2, i = lane - bi * t.a2;
+      aux0 = lda(t.aux + (size_t)(b0 + bi) * t.ostride + i);
     }
-    __syncthreads();
+    __syncthreads();  // partials complete
+    __syncthreads();  // row sums complete
     trace_mark(d, t, 1);
-    if (wave == 0) gemv_epilogue(d, ca, t, g, red, bfirst, b0, n);
-    ws.par ^= 1;
-    if (n < nb) {
+    gemv_epilogue(d, ca, t, &sm.rows[0][0], q.bfirst, b0, n, aux0, q.rpp);
+    if (n < q.nb) {
       ws.x_src = nullptr;
-      __syncthreads();  // the next batch chunk restages xs and reuses red
+      __syncthreads();  // the next slot chunk restages xs and reuses the buffers
     }
   }
-  if (persistent && wave == 0) {
+  if (persistent) {
     // The epilogue's stores are all this wave's: drain them only where the
     // run's completions are reported (the wait covers the earlier tasks too).
     if (t.a5 > 0) vm_drain();
     trace_finish(d, t);  // before the signal: consumers start after it
     signal_done(d, t);
+  }
+  return true;
+}
+
+// Compute waves: stream the task's passes through `w` (holding the first
+// pass when w_loaded), refilling each slot right after its use with the next
+// pass, and after the last pass with the first pass of the next task `gn`
+// when `pre`; then the row sums.
+template <bool B1>
+DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
+                  WState &ws, Buf &w, bool w_loaded, bool pre, const Geo &gn) {
+  const int cw = uni(tidx() >> 6) - 1;
+  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  const GemvShape2 q = gemv_shape<B1>(d, ca, t);
+  if (q.skip) return true;
+  if (!w_loaded) load_slots(q.g, w, cw);
+  if (!gemv_fits(d, t, q)) return false;
+  const int K = q.g.K;
+  auto geo_of = [&](int p) { return p == 0 ? q.g : pass_geo(t.w0, t.w1, t.a2, t.rpp, K, p); };
+  float *red = &sm.red[0][0];
+  float *rsum = &sm.rows[0][0];
+  for (int b0 = 0; b0 < q.nb; b0 += q.bb_max) {
+    const int n = min(q.bb_max, q.nb - b0);
+    const bool last = b0 + n >= q.nb;
+    if (n < q.nb) ws.x_src = nullptr;
+    stage_x(sm, ws, t.src + (size_t)b0 * K, K, n, t.gain, d.eps);
+    // The first pass was loaded before the task; waiting for all of it here
+    // lets the pass loop wait per slot for the loads it issues itself.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    for (int p = 0; p < q.P; ++p) {
+      const Geo gp = geo_of(p);
+      const bool lastp = p + 1 == q.P;
+      const Geo gq = lastp ? gn : geo_of(p + 1);
+      const bool pre_p = lastp ? (pre && last) : true;
+      if (B1 || n == 1) {
+        gemv_dot1(gp, w, sm.xs, red + p * kPartSlot, cw, pre_p, gq);
+      } else {
+        gemv_dotn(gp, w, sm.xs, n, red + p * n * kPartSlot, cw);
+        if (pre_p) load_slots(gq, w, cw);
+      }
+    }
+    __syncthreads();  // partials complete
+    for (int p = 0; p < q.P; ++p) {
+      const Geo gp = geo_of(p);
+      gemv_rows(gp, gp.units * 512 / K, red + p * n * kPartSlot, rsum + p * n * kRowSlot, n, cw);
+    }
+    __syncthreads();  // row sums complete
+    if (n < q.nb) {
+      ws.x_src = nullptr;
+      __syncthreads();
+    }
   }
   return true;
 }
@@ -1054,28 +1171,22 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
 // task has static weights (pre), their tile geometry is gn and this task
 // leaves them loading into `w`.  Returns whether it did; `alive` turns false
 // when the step is drained after an error.  Uniform across waves.
-DEV bool run_task(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent, WState &ws,
-                  Buf &w, bool w_loaded, bool pre, const Geo &gn, bool &alive) {
-  if (is_gemv(t.op)) {
-    alive = run_gemv(sm, d, ca, t, persistent, ws, w, w_loaded, pre, gn);
-    return alive && pre;
+// One task of the kernel-per-op executor (all waves of one workgroup).
+DEV void run_task_once(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws) {
+  if (!is_gemv(t.op)) {
+    run_small(sm, d, ca, t, false, ws);
+  } else if (uni(tidx() >> 6) == 0) {
+    gemv_ctl<false>(sm, d, ca, t, false, ws);
+  } else {
+    Buf w;
+    Geo gn;
+    gemv_cmp<false>(sm, d, ca, t, false, ws, w, false, false, gn);
   }
-  // The buffer holds nothing a later task reads (no task before this one
-  // prefetched for it): overwrite it so its registers are free during the
-  // small task.
-#pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) w[j] = (u32x4){0u, 0u, 0u, 0u};
-  alive = run_small(sm, d, ca, t, persistent, ws);
-  if (alive && pre) {
-    const int cw = uni(tidx() >> 6) - 1;
-    if (cw >= 0) load_slots(gn, w, cw);
-    return true;
-  }
-  return false;
 }
 
-// Geometry of the next task's tile from its descriptor words in the ring:
-// op (word 0), rows (a2, word 4), w0 / w1 (words 16-19), K (word 28).
+// Geometry of the next task's first pass from its descriptor words in the
+// ring: op (word 0), rows (a2, word 4), w0 / w1 (words 16-19), K (word 28),
+// rows per pass (word 31).
 DEV bool next_geo(const uint32_t *slot, Geo &g) {
   const int op = (int)(int16_t)(uni((int)slot[0]) & 0xffff);
   if (!static_weights(op)) return false;
@@ -1083,14 +1194,19 @@ DEV bool next_geo(const uint32_t *slot, Geo &g) {
   const uint16_t *w0 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[16]), (uint32_t)uni((int)slot[17]));
   const uint16_t *w1 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[18]), (uint32_t)uni((int)slot[19]));
   const int K = uni((int)slot[28]);
-  g = make_geo(w0, w1, rows, w1 ? 2 : 1, K);
+  const int rpp = uni((int)slot[31]);
+  g = pass_geo(w0, w1, rows, rpp, K, 0);
   return true;
 }
 
-// The persistent worker runs its queue in order.  The control wave keeps the
-// descriptors of the current and the next task in an LDS ring (loaded two
-// tasks ahead); one register tile buffer carries each task's prefetched
-// weights into the next.
+// The persistent worker runs its queue in order.  An LDS ring holds the
+// descriptors of the current and the next tasks (refilled by compute wave 1).
+// Wave 0 and waves 1-7 run separate loops over the same queue, meeting at
+// each task's barriers.  On the compute side consecutive static-weight GEMV
+// tasks form a run: one register tile buffer, local to the run, carries the
+// weights of each pass into the next, and of each task's last pass into the
+// next task's first (loaded before that task's dependency wait).
+template <bool B1>
 __global__ void __launch_bounds__(kThreads)
     mk_persistent_kernel(const DevPlan *__restrict__ dplan, CallArgs ca) {
   __shared__ Smem sm;
@@ -1098,30 +1214,65 @@ __global__ void __launch_bounds__(kThreads)
   const int wid = blockIdx.x;
   const int beg = ((const AS4 int *)d.worker_off)[wid];
   const int end = ((const AS4 int *)d.worker_off)[wid + 1];
-  const int wave = uni(tidx() >> 6), lane = tidx() & 63;
+  const int wave = uni(tidx() >> 6), lane = tidx() & 63, cw = wave - 1;
   const u32x4 *tabv = (const u32x4 *)d.tasks;  // 8 x 16 bytes per descriptor
   u32x4 pend = {0u, 0u, 0u, 0u};
-  if (wave == 0 && lane < 8) {
-    for (int i = 0; i < 2 && beg + i < end; ++i)
+  if (wave == 1 && lane < 8) {
+    for (int i = 0; i < 3 && beg + i < end; ++i)
       ((u32x4 *)sm.ring[i])[lane] = ldg(tabv + (size_t)(beg + i) * 8 + lane);
-    if (beg + 2 < end) pend = ldg(tabv + (size_t)(beg + 2) * 8 + lane);
+    if (beg + 3 < end) pend = ldg(tabv + (size_t)(beg + 3) * 8 + lane);
   }
   __syncthreads();
   WState ws;
   init_ws(ws);
-  Buf buf;
-  bool alive = true, loaded = false;
-  for (int k = beg; k < end; ++k) {
-    const int i = k - beg;
-    const TD t = td_from_ring(sm.ring[i % kRing]);
-    Geo gn;
-    const bool pre = k + 1 < end && next_geo(sm.ring[(i + 1) % kRing], gn);
-    if (wave == 0 && lane < 8) {  // ring refill, published by the task's barriers
-      if (k + 2 < end) ((u32x4 *)sm.ring[(i + 2) % kRing])[lane] = pend;
-      if (k + 3 < end) pend = ldg(tabv + (size_t)(k + 3) * 8 + lane);
+  if (wave == 0) {
+    for (int k = beg; k < end; ++k) {
+      const TD t = td_from_ring(sm.ring[(k - beg) % kRing]);
+      const bool alive = is_gemv(t.op) ? gemv_ctl<B1>(sm, d, ca, t, true, ws)
+                                       : run_small(sm, d, ca, t, true, ws);
+      if (!alive) return;
     }
-    loaded = run_task(sm, d, ca, t, true, ws, buf, loaded, pre, gn, alive);
-    if (!alive) break;
+    return;
+  }
+  // Ring refill after task k (read two tasks later, after the next task's
+  // barriers).  Compute wave 1 does it: the descriptor load, issued behind
+  // the next tile's weights, has completed by the next weight wait; the
+  // control wave's queue holds epilogue stores instead.
+  auto refill = [&](int k) {
+    if (wave == 1 && lane < 8) {
+      const int i = k - beg;
+      if (k + 3 < end) ((u32x4 *)sm.ring[(i + 3) % kRing])[lane] = pend;
+      if (k + 4 < end) pend = ldg(tabv + (size_t)(k + 4) * 8 + lane);
+    }
+  };
+  int k = beg;
+  while (k < end) {
+    TD t = td_from_ring(sm.ring[(k - beg) % kRing]);
+    if (static_weights(t.op)) {
+      Buf w;
+      load_slots(static_geo(t), w, cw);
+      for (;;) {
+        Geo gn;
+        const bool pre = k + 1 < end && next_geo(sm.ring[(k + 1 - beg) % kRing], gn);
+        if (!gemv_cmp<B1>(sm, d, ca, t, true, ws, w, true, pre, gn)) return;
+        refill(k);
+        ++k;
+        if (!pre) break;
+        t = td_from_ring(sm.ring[(k - beg) % kRing]);
+      }
+    } else {
+      bool alive;
+      if (is_gemv(t.op)) {
+        Buf w;
+        Geo gn;
+        alive = gemv_cmp<B1>(sm, d, ca, t, true, ws, w, false, false, gn);
+      } else {
+        alive = run_small(sm, d, ca, t, true, ws);
+      }
+      if (!alive) return;
+      refill(k);
+      ++k;
+    }
   }
 }
 
@@ -1133,10 +1284,7 @@ __global__ void __launch_bounds__(kThreads)
   const TD t = td_from_table(d.tasks, pos);
   WState ws;
   init_ws(ws);
-  Buf buf;
-  bool alive = true;
-  Geo gn;
-  run_task(sm, d, ca, t, false, ws, buf, false, false, gn, alive);
+  run_task_once(sm, d, ca, t, ws);
 }
 
 __global__ void mk_stage_kernel(int32_t *tok, int32_t *pos, int B, int slot,
@@ -1155,9 +1303,12 @@ __global__ void mk_zero_kernel(uint32_t *p, int n) {
 // ---------------------------------------------------------------- launch --
 // All workers must be resident at once (each may wait on any other), which a
 // cooperative launch guarantees or refuses.
-hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, hipStream_t s) {
+hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, int batch,
+                             hipStream_t s) {
   void *args[] = {(void *)&d, (void *)&ca};
-  return hipLaunchCooperativeKernel((const void *)mk_persistent_kernel, dim3(grid), dim3(kThreads),
+  const void *k = batch == 1 ? (const void *)mk_persistent_kernel<true>
+                             : (const void *)mk_persistent_kernel<false>;
+  return hipLaunchCooperativeKernel(k, dim3(grid), dim3(kThreads),
                                     args, 0, s);
 }
 

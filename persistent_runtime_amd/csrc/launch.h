@@ -8,7 +8,9 @@ namespace mk {
 
 // One decode step as a single persistent launch: `grid` workgroups (one per
 // CU) pull tickets until the task list is exhausted.  `d` is a device copy.
-hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, hipStream_t s);
+// batch: the plan's slot count (1 selects the single-slot build)
+hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, int batch,
+                             hipStream_t s);
 
 // Kernel-per-op: tasks [first, first+count) of one launch phase, one
 // workgroup per task, no counters (stream order orders the phases).

@@ -29,6 +29,9 @@ constexpr int kMaxTileUnits16 = kCW * kMaxChunks;           // 1 KiB units/tile
 constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 8;           // query heads per KV head
 constexpr int kMaxBatchGemv = 4;       // slots a GEMV tile handles at once
+// A GEMV task streams its rows in passes of at most one register tile each;
+// passes x slots per task are bounded by the LDS partial-sum buffers.
+constexpr int kMaxPass = 8;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
 constexpr int kLdsXBytes = 128 * 1024; // budget for staged activations
 
@@ -45,11 +48,13 @@ enum Op : int16_t {
 //   MERGE   a0=slot a1=kv head
 //   OPROJ/DOWN/ROUTER  a1=row0 a2=rows
 //   GATEUP  a1=row0 a2=rows per matrix (gate rows then the same up rows)
+//   (static-weight GEMVs: rpp = rows per pass; the task streams a2 rows as
+//   ceil(a2 / rpp) passes of rpp rows, the last one shorter)
 //   TOPK    a0=slot
 //   EGATEUP a0=slot a1=row0 a2=rows per matrix a3=expert slot
 //   EDOWN   a0=slot a1=row0 a2=rows a3=expert slot
 //   COMBINE a0=slot a1=row0 a2=rows
-//   LMHEAD  a1=row0 a2=rows a4=tile index
+//   LMHEAD  a1=row0 a2=rows a4=LM-head task index (argmax partial)
 //   ARGMAX  a0=slot
 // a5 (every op): how many completions this task reports to its events.  A
 // worker that runs several consecutive tasks signalling the same events
@@ -76,7 +81,7 @@ struct alignas(16) Task {
   const uint16_t *gain;
   int32_t K, ostride;
   int32_t gidx;             // the task's index in list order
-  int32_t pad;
+  int32_t rpp;              // rows per pass (static-weight GEMVs), else 0
 };
 static_assert(sizeof(Task) == 128, "task descriptor is 128 bytes");
 

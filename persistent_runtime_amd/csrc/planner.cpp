@@ -120,8 +120,9 @@ struct Builder {
   }
   void add(int op, int layer, int a0, int a1, int a2, int a3, int a4,
            std::initializer_list<int> waits, std::initializer_list<int> sigs,
-           int64_t bytes) {
+           int64_t bytes, int worker = -1, int rpp = 0) {
     Task t{};
+    t.rpp = rpp;
     t.op = (int16_t)op;
     t.layer = (int16_t)layer;
     t.a0 = a0; t.a1 = a1; t.a2 = a2; t.a3 = a3; t.a4 = a4; t.a5 = 0;
@@ -135,8 +136,61 @@ struct Builder {
     p.tasks.push_back(t);
     p.task_phase.push_back(phase);
     p.task_bytes.push_back(bytes);
+    p.task_hint.push_back(worker);
   }
 };
+
+// One contiguous row range of one weight matrix (or of the gate/up pair)
+// inside a GEMV operation, with what its tasks carry and signal.
+struct RowSeg {
+  int a0;     // QKV: matrix (0 q, 1 k, 2 v); else 0
+  int row0, rows;
+  int sig;    // event the segment's tasks signal
+};
+
+// Lower a static-weight GEMV operation: its rows (all of nseg * K bf16) are
+// cut into one contiguous, near-equal share per worker (the balance is in
+// bytes, as every row has the same length); a share becomes one task per
+// segment piece, streamed in passes of at most one register tile, at most
+// pmax passes per task.  Returns the number of tasks added, or -1 when a
+// row does not fit one register tile.
+int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int K, int nseg,
+             int n_workers, int pmax, int wait_ev, int64_t extra_bytes, int *lm_index) {
+  const int64_t row_bytes = (int64_t)nseg * K * 2;
+  int unit = 1;
+  while ((row_bytes * unit) % 1024) ++unit;
+  int R = (int)((int64_t)kMaxTileUnits16 * 1024 / row_bytes);
+  R -= R % unit;
+  if (R < unit) return -1;
+  int64_t total = 0;
+  for (auto &sg : segs) total += sg.rows;
+  int added = 0;
+  size_t si = 0;
+  int64_t seg_base = 0;  // rows before segs[si]
+  for (int w = 0; w < n_workers; ++w) {
+    int64_t lo = total * w / n_workers, hi = total * (w + 1) / n_workers;
+    lo -= lo % unit;
+    hi = (w + 1 == n_workers) ? total : hi - hi % unit;
+    while (lo < hi) {
+      while (lo >= seg_base + segs[si].rows) seg_base += segs[si++].rows;
+      const RowSeg &sg = segs[si];
+      const int64_t end = std::min<int64_t>(hi, seg_base + sg.rows);
+      int64_t n = end - lo;
+      const int64_t cap = (int64_t)pmax * R;
+      if (n > cap) n = cap;
+      const int P = (int)((n + R - 1) / R);
+      int rpp = (int)((n + P - 1) / P);
+      rpp += (unit - rpp % unit) % unit;
+      const int row0 = (int)(sg.row0 + (lo - seg_base));
+      const int a4 = lm_index ? (*lm_index)++ : 0;
+      b.add(op, layer, sg.a0, row0, (int)n, 0, a4, {wait_ev}, {sg.sig},
+            n * row_bytes + extra_bytes, w, rpp);
+      ++added;
+      lo += n;
+    }
+  }
+  return added;
+}
 
 }  // namespace
 
@@ -162,17 +216,12 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   p.S = std::max(1, std::min(std::min(want, by_len), 64));
   if (o.attn_splits > 0) p.S = std::min(o.attn_splits, 256);
 
-  // tile shapes
-  bool ok = choose_tile((long)(nq + 2 * nkv) * hd, H, 1, n_cus, hd, p.qkv) &&
-            choose_tile(H, nq * hd, 1, n_cus, 0, p.oproj) &&
-            choose_tile(c.vocab, H, 1, n_cus, 0, p.lmhead);
-  if (!moe) {
-    ok = ok && choose_tile(c.ffn_dim, H, 2, n_cus, 0, p.gateup) &&
-         choose_tile(H, c.ffn_dim, 1, n_cus, 0, p.down);
-  } else {
+  // Expert tiles (weights chosen at run time) keep one register tile per
+  // task; the static-weight operations are cut per worker below.
+  bool ok = true;
+  if (moe) {
     const int Fe = c.expert_ffn_dim;
-    ok = ok && choose_tile(c.n_experts, H, 1, n_cus, 0, p.router) &&
-         choose_tile((long)Fe * c.top_k * B, H, 2, n_cus, 0, p.egateup) &&
+    ok = ok && choose_tile((long)Fe * c.top_k * B, H, 2, n_cus, 0, p.egateup) &&
          choose_tile((long)H * c.top_k * B, Fe, 1, n_cus, 0, p.edown);
     // expert tiles must not straddle experts: round rows to divisors that
     // keep whole 1 KiB chunks
@@ -186,7 +235,14 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     if (ok) ok = fit(p.egateup, Fe, H, 2) && fit(p.edown, H, Fe, 1);
   }
   if (!ok) { err = "no tile shape fits the row lengths"; return MK_ERR_UNSUPPORTED; }
-  p.n_lm_tiles = p.lmhead.tiles;
+  // passes per task: slots x passes share the LDS partial buffers; when the
+  // slots of a step do not fit one activation stage the weights of a pass
+  // are reused across slot chunks, so such tasks keep a single pass
+  auto pmax_for = [&](int K) {
+    const int bb = std::max(1, std::min(kMaxBatchGemv, (int)(kLdsXBytes / ((int64_t)K * 4))));
+    if (B > bb) return 1;
+    return std::max(1, kMaxPass / std::min(B, kMaxBatchGemv));
+  };
 
   // scratch sizes
   p.n_x = (int64_t)(L + 1) * B * H;
@@ -202,7 +258,6 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     p.n_he = (int64_t)L * B * c.top_k * c.expert_ffn_dim;
     p.n_ye = (int64_t)L * B * c.top_k * H;
   }
-  p.n_amax = (int64_t)B * p.n_lm_tiles;
 
   Builder b(p);
   std::vector<int> x_ev(L + 1);
@@ -218,13 +273,15 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     std::vector<int> grp(nkv);
     for (int g = 0; g < nkv; ++g) grp[g] = b.ev();
     b.begin_phase();
-    const int rq = p.qkv.rows_per_tile;
-    for (int g = 0; g < nkv; ++g) {
-      for (int r = g * G * hd; r < (g + 1) * G * hd; r += rq)
-        b.add(OP_QKV, l, 0, r, rq, 0, 0, {x_ev[l]}, {grp[g]}, (int64_t)rq * H * 2);
-      for (int m = 1; m <= 2; ++m)
-        for (int r = g * hd; r < (g + 1) * hd; r += rq)
-          b.add(OP_QKV, l, m, r, rq, 0, 0, {x_ev[l]}, {grp[g]}, (int64_t)rq * H * 2);
+    {
+      std::vector<RowSeg> segs;
+      for (int g = 0; g < nkv; ++g) {
+        segs.push_back({0, g * G * hd, G * hd, grp[g]});
+        segs.push_back({1, g * hd, hd, grp[g]});
+        segs.push_back({2, g * hd, hd, grp[g]});
+      }
+      if (add_gemv(b, OP_QKV, l, segs, H, 1, n_workers, pmax_for(H), x_ev[l], 0, nullptr) < 0)
+        ok = false;
     }
     // attention splits (+ merge when split)
     int mrg = b.ev();
@@ -246,35 +303,26 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     // O projection + residual
     int xo = b.ev();
     b.begin_phase();
-    const int ro = p.oproj.rows_per_tile;
-    for (int r = 0; r < H; r += ro) {
-      int n = std::min(ro, H - r);
-      b.add(OP_OPROJ, l, 0, r, n, 0, 0, {mrg}, {xo}, (int64_t)n * nq * hd * 2);
-    }
+    if (add_gemv(b, OP_OPROJ, l, {{0, 0, H, xo}}, nq * hd, 1, n_workers, pmax_for(nq * hd), mrg,
+                 0, nullptr) < 0)
+      ok = false;
     if (!moe) {
       int hev = b.ev();
       b.begin_phase();
-      const int rg = p.gateup.rows_per_tile;
-      for (int r = 0; r < c.ffn_dim; r += rg) {
-        int n = std::min(rg, c.ffn_dim - r);
-        b.add(OP_GATEUP, l, 0, r, n, 0, 0, {xo}, {hev}, (int64_t)2 * n * H * 2);
-      }
+      if (add_gemv(b, OP_GATEUP, l, {{0, 0, c.ffn_dim, hev}}, H, 2, n_workers, pmax_for(H), xo,
+                   0, nullptr) < 0)
+        ok = false;
       b.begin_phase();
-      const int rd = p.down.rows_per_tile;
-      for (int r = 0; r < H; r += rd) {
-        int n = std::min(rd, H - r);
-        b.add(OP_DOWN, l, 0, r, n, 0, 0, {hev}, {x_ev[l + 1]},
-              (int64_t)n * c.ffn_dim * 2);
-      }
+      if (add_gemv(b, OP_DOWN, l, {{0, 0, H, x_ev[l + 1]}}, c.ffn_dim, 1, n_workers,
+                   pmax_for(c.ffn_dim), hev, 0, nullptr) < 0)
+        ok = false;
     } else {
       const int E = c.n_experts, K = c.top_k, Fe = c.expert_ffn_dim;
       int rlev = b.ev();
       b.begin_phase();
-      const int rr = p.router.rows_per_tile;
-      for (int r = 0; r < E; r += rr) {
-        int n = std::min(rr, E - r);
-        b.add(OP_ROUTER, l, 0, r, n, 0, 0, {xo}, {rlev}, (int64_t)n * H * 2);
-      }
+      if (add_gemv(b, OP_ROUTER, l, {{0, 0, E, rlev}}, H, 1, n_workers, pmax_for(H), xo, 0,
+                   nullptr) < 0)
+        ok = false;
       std::vector<int> tk(B);
       b.begin_phase();
       for (int s = 0; s < B; ++s) {
@@ -311,12 +359,13 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   // final norm + LM head (+ per-tile argmax partials), then argmax
   int lm = b.ev();
   b.begin_phase();
-  const int rl = p.lmhead.rows_per_tile;
-  int tile = 0;
-  for (int r = 0; r < c.vocab; r += rl, ++tile) {
-    int n = std::min(rl, c.vocab - r);
-    b.add(OP_LMHEAD, L, 0, r, n, 0, tile, {x_ev[L]}, {lm}, (int64_t)n * H * 2 + H * 2);
-  }
+  int n_lm = 0;
+  if (add_gemv(b, OP_LMHEAD, L, {{0, 0, c.vocab, lm}}, H, 1, n_workers, pmax_for(H), x_ev[L],
+               (int64_t)H * 2, &n_lm) < 0)
+    ok = false;
+  if (!ok) { err = "a row does not fit one register tile"; return MK_ERR_UNSUPPORTED; }
+  p.n_lm_tiles = n_lm;
+  p.n_amax = (int64_t)B * p.n_lm_tiles;
   b.begin_phase();
   for (int s = 0; s < B; ++s) b.add(OP_ARGMAX, L, s, 0, 0, 0, 0, {lm}, {}, 0);
   b.end();
@@ -340,6 +389,15 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   std::vector<int> order(n_workers);
   for (auto &ph : p.phases) {
     const int n = ph.second - ph.first;
+    if (p.task_hint[ph.first] >= 0) {  // per-worker shares chosen by the lowering
+      for (int i = ph.first; i < ph.second; ++i) {
+        const int w = p.task_hint[i];
+        q[w].push_back(i);
+        p.task_worker[i] = w;
+        load[w] += std::max<int64_t>(p.task_bytes[i], 16384);
+      }
+      continue;
+    }
     const int base = n / n_workers, extra = n % n_workers;
     // least-loaded workers take the extra tasks (ties: lower index)
     for (int w = 0; w < n_workers; ++w) order[w] = w;

@@ -28,6 +28,7 @@ struct HostPlan {
   std::vector<int32_t> task_phase;  // launch index under kernel-per-op
   std::vector<std::pair<int32_t, int32_t>> phases;  // [begin, end) per launch
   std::vector<int64_t> task_bytes;  // algorithmic bytes read per task
+  std::vector<int32_t> task_hint;   // worker chosen by the lowering, or -1
   int n_workers = 0;                // persistent workgroups (one per CU)
   std::vector<int32_t> task_worker; // worker that runs each task
   std::vector<int32_t> worker_off;  // [n_workers + 1]
@@ -35,8 +36,7 @@ struct HostPlan {
   // scratch sizes in elements
   int64_t n_x = 0, n_xmid = 0, n_q = 0, n_k = 0, n_part = 0, n_attn = 0,
           n_h = 0, n_rl = 0, n_tk = 0, n_he = 0, n_ye = 0, n_amax = 0;
-  GemvShape qkv{}, oproj{}, gateup{}, down{}, lmhead{}, router{}, egateup{},
-      edown{};
+  GemvShape egateup{}, edown{};     // expert tiles (one register tile each)
 };
 
 // Vector width (bytes per lane load) for rows of K bf16 elements, or 0 when

@@ -78,7 +78,8 @@ class mk_task_info(C.Structure):
                 ("a4", C.c_int32), ("sig_count", C.c_int32), ("n_wait", C.c_int32),
                 ("wait_ev", C.c_int32 * 3), ("n_sig", C.c_int32),
                 ("sig_ev", C.c_int32 * 2), ("phase", C.c_int32),
-                ("worker", C.c_int32), ("bytes", C.c_int64)]
+                ("worker", C.c_int32), ("rows_per_pass", C.c_int32),
+                ("bytes", C.c_int64)]
 
 
 def _load():

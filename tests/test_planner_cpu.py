@@ -230,16 +230,37 @@ def test_invalid_configs_rejected():
         mk.inspect_plan(c)
 
 
-def test_wave_quantization_drives_tile_choice():
-    """Tile counts of the 8B plan on 256 CUs: full waves where the shapes allow."""
+def test_gemv_shares_balanced_and_passes_fit():
+    """Static-weight GEMVs of the 8B plan on 256 workgroups: every worker gets
+    a contiguous share of each operation whose bytes differ from the others'
+    by at most one row, and every pass fits one register tile (7 waves x 16
+    chunks of 1 KiB), at most 8 passes per task."""
     tasks, _ = mk.inspect_plan(_cfg(LLAMA8B, maxp=40), mk.default_options(n_cus=256))
-    per_op = {}
-    for t in tasks:
-        if t.layer == 0:
-            per_op[mk.OPS[t.op]] = per_op.get(mk.OPS[t.op], 0) + 1
-    for op in ("QKV", "OPROJ", "GATEUP", "DOWN"):
-        w, tail, idle = waves(per_op[op], 256)
-        assert idle == 0, (op, per_op[op])
+    H, F, V = LLAMA8B["hidden"], LLAMA8B["ffn_dim"], LLAMA8B["vocab"]
+    row_bytes = {"QKV": H * 2, "OPROJ": H * 2, "GATEUP": 2 * H * 2, "DOWN": F * 2,
+                 "LMHEAD": H * 2}
+    for op, rb in row_bytes.items():
+        layer = LLAMA8B["n_layers"] if op == "LMHEAD" else 3
+        sel = [t for t in tasks if mk.OPS[t.op] == op and t.layer == layer]
+        per_worker = {}
+        for t in sel:
+            assert 0 < t.rows_per_pass <= t.a2
+            passes = -(-t.a2 // t.rows_per_pass)
+            assert passes <= 8, (op, passes)
+            assert t.rows_per_pass * rb <= 7 * 16 * 1024, (op, t.rows_per_pass)
+            assert (t.rows_per_pass * rb) % 1024 == 0
+            per_worker[t.worker] = per_worker.get(t.worker, 0) + t.a2 * rb
+        assert len(per_worker) == 256, (op, len(per_worker))
+        assert max(per_worker.values()) - min(per_worker.values()) <= rb, op
+    # the rows of each operation are covered exactly once
+    for op, total in (("GATEUP", F), ("DOWN", H), ("OPROJ", H), ("LMHEAD", V)):
+        layer = LLAMA8B["n_layers"] if op == "LMHEAD" else 3
+        rows = sorted((t.a1, t.a2) for t in tasks if mk.OPS[t.op] == op and t.layer == layer)
+        pos = 0
+        for r0, n in rows:
+            assert r0 == pos
+            pos += n
+        assert pos == total, op
 
 
 def test_truncated_model_plans():
