@@ -96,6 +96,14 @@ DEV float wave_sum(float v) {
   v += dpp<DPP_MIRROR>(v);  // every lane holds its 16-lane row sum
   return (lanef(v, 0) + lanef(v, 16)) + (lanef(v, 32) + lanef(v, 48));
 }
+// maximum of all 64 lanes, returned uniform
+DEV float wave_max(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
+}
 // sum over the 4 lanes of each quad (result in all 4)
 DEV float quad_sum(float v) {
   v += dpp<DPP_XOR1>(v);
@@ -499,25 +507,28 @@ DEV void gemv_dotn(const Geo &g, Buf &w, const float *xs, int n, float *part, in
   }
 }
 
-// Row sums of a tile's R rows for n slots, over the compute waves: row r is
-// the sum of its K/128 partials part[r*K/128 ..).  A group of G lanes (the
-// power of two >= K/128, at most 64) takes one row, each lane a strided share
-// of the partials, then the group adds up by butterfly exchange (fixed order:
-// deterministic).
-DEV void gemv_rows(const Geo &g, int R, const float *part, float *rows, int n, int cw) {
-  const int lane = tidx() & 63;
-  const int ne = g.K >> 7;
-  const int G = ne >= 64 ? 64 : (1 << (32 - __builtin_clz((unsigned)ne - 1u)));
-  const int per = 64 / G;
-  const int sub = lane / G, j = lane - sub * G;
-  for (int b = 0; b < n; ++b) {
-    for (int r0 = cw * per; r0 < R; r0 += kCW * per) {
-      const int r = r0 + sub;
-      float v = 0.f;
-      if (r < R)
-        for (int e = j; e < ne; e += G) v += part[b * kPartSlot + r * ne + e];
-      for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o, 64);
-      if (j == 0 && r < R) rows[b * kRowSlot + r] = v;
+// Row sums of a task's rows for n slots, over the compute waves: row r of
+// pass p is the sum of its K/128 partials part[(p*n + b)*kPartSlot + r*K/128
+// ..].  Each 16-lane DPP row takes one output row: every lane adds up a
+// strided share of the partials, then the 16 lanes reduce by DPP (fixed
+// order: deterministic).  rows_p(p) gives the rows of pass p (both segments).
+template <class RowsOf>
+DEV void gemv_rows(int K, int P, RowsOf rows_p, const float *part, float *rows, int n, int cw) {
+  const int lane = tidx() & 63, grp = lane >> 4, j = lane & 15;
+  const int ne = K >> 7;
+  for (int p = 0; p < P; ++p) {
+    const int R = rows_p(p);
+    for (int b = 0; b < n; ++b) {
+      const float *pp = part + (p * n + b) * kPartSlot;
+      float *rr = rows + (p * n + b) * kRowSlot;
+      for (int r0 = cw * 4; r0 < R; r0 += kCW * 4) {
+        const int r = r0 + grp;
+        float v = 0.f;
+        if (r < R)
+          for (int e = j; e < ne; e += 16) v += pp[r * ne + e];
+        v = row16_sum(v);
+        if (j == 0 && r < R) rr[r] = v;
+      }
     }
   }
 }
@@ -799,10 +810,7 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
       }
     }
     __syncthreads();  // partials complete
-    for (int p = 0; p < q.P; ++p) {
-      const Geo gp = geo_of(p);
-      gemv_rows(gp, gp.units * 512 / K, red + p * n * kPartSlot, rsum + p * n * kRowSlot, n, cw);
-    }
+    gemv_rows(K, q.P, [&](int p) { return geo_of(p).units * 512 / K; }, red, rsum, n, cw);
     __syncthreads();  // row sums complete
     if (n < q.nb) {
       ws.x_src = nullptr;
@@ -819,9 +827,13 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
 // current position also rotates and stores the new key/value (bf16) and
 // attends to it.  Softmax runs online in base 2 on log2(e)/sqrt(hd)-scaled
 // scores; the task leaves (max, sum, weighted values) for the merge, or the
-// normalised output when there is a single split.
+// normalised output when there is a single split.  The cached pages do not
+// depend on this step's projections: each wave loads its first page before
+// the task waits for the query/key/value tiles of its group.
+// Returns false when the step is drained after an error.
 template <int HD>
-DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
+DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
+                  WState &ws) {
   const int tix = t.gidx;
   const int l = t.layer, b = t.a0, g = t.a1, sp = t.a2;
   const int G = d.G, S = d.S, B = d.B, nkv = d.nkv, nq = d.nq;
@@ -837,7 +849,38 @@ DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
 
   const int pos = uni(ldg(ca.positions + b));
   const size_t head0 = ((size_t)l * B + b) * nq + (size_t)g * G;  // first head row
-  if (pos < 0 || pos >= d.max_pos) {
+  constexpr int DQ = HD / 4;                  // key dims per lane
+  constexpr int KV4 = DQ / 8;                 // 16-byte loads per lane
+  constexpr int VPOS = HD == 128 ? 16 : 8;    // value rows per lane
+  const int tq = lane >> 2, qd = lane & 3;
+  const int vdim = HD == 128 ? 2 * lane : 2 * (lane & 31);
+  const bool pos_ok = pos >= 0 && pos < d.max_pos;
+  const int n = pos + 1;
+  const int lo = pos_ok ? (int)((int64_t)sp * n / S) : 0;
+  const int hi = pos_ok ? (int)((int64_t)(sp + 1) * n / S) : 0;
+  const int chi = hi < pos ? hi : pos;  // cached keys [lo, chi)
+  const int blk0 = lo / kPageSize, blk1 = chi > lo ? (chi - 1) / kPageSize : -1;
+  // prefetch of this wave's first page
+  u32x4 kr[KV4];
+  uint32_t vr[VPOS];
+  int pg_first = -1;
+  if (blk0 + wave <= blk1) {
+    pg_first = uni(ldg(d.page_table + (size_t)b * d.maxp + blk0 + wave));
+    if (pg_first >= 0 && pg_first < d.npages) {
+      const size_t pbase = (((size_t)l * d.npages + pg_first) * nkv + g) * kPageSize * HD;
+#pragma unroll
+      for (int i = 0; i < KV4; ++i)
+        kr[i] = ldg((const u32x4 *)(d.k_pool + pbase + tq * HD + qd * DQ + i * 8));
+#pragma unroll
+      for (int i = 0; i < VPOS; ++i) {
+        const int tt = HD == 128 ? i : 2 * i + (lane >> 5);
+        vr[i] = ldg((const uint32_t *)(d.v_pool + pbase + tt * HD + vdim));
+      }
+    }
+  }
+  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  trace_start(d, t);
+  if (!pos_ok) {
     if (pos >= d.max_pos && tid == 0)
       set_error(d, DEVERR_BAD_INPUT, tix, -1, (uint32_t)pos, (uint32_t)d.max_pos);
     for (int idx = tid; idx < G * HD; idx += kThreads) {
@@ -850,12 +893,9 @@ DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
         if (dd == 0) { sta(pp + HD, -INFINITY); sta(pp + HD + 1, 0.f); }
       }
     }
-    return;
+    return true;
   }
-  const int n = pos + 1;
-  const int lo = (int)((int64_t)sp * n / S), hi = (int)((int64_t)(sp + 1) * n / S);
   const bool has_cur = (hi == n);
-  const int chi = hi < pos ? hi : pos;  // cached keys [lo, chi)
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
   const float *cs = d.rope_cos + (size_t)pos * (HD / 2);
   const float *sn = d.rope_sin + (size_t)pos * (HD / 2);
@@ -890,34 +930,29 @@ DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
   }
   __syncthreads();
 
-  // --- page loop: wave w takes pages blk0+w, blk0+w+kWaves, ...
+  // --- page loop: wave w takes pages blk0+w, blk0+w+kWaves, ... (the first
+  // one already loaded)
   float m[kMaxGroup], ls[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) { m[h] = -INFINITY; ls[h] = 0.f; o0[h] = 0.f; o1[h] = 0.f; }
-  constexpr int DQ = HD / 4;                  // key dims per lane
-  constexpr int KV4 = DQ / 8;                 // 16-byte loads per lane
-  constexpr int VPOS = HD == 128 ? 16 : 8;    // value rows per lane
-  const int tq = lane >> 2, qd = lane & 3;
-  const int vdim = HD == 128 ? 2 * lane : 2 * (lane & 31);
   if (chi > lo) {
-    const int blk0 = lo / kPageSize, blk1 = (chi - 1) / kPageSize;
     for (int blk = blk0 + wave; blk <= blk1; blk += kWaves) {
-      const int pg = uni(ldg(d.page_table + (size_t)b * d.maxp + blk));
+      const int pg = blk == blk0 + wave ? pg_first
+                                        : uni(ldg(d.page_table + (size_t)b * d.maxp + blk));
       if (pg < 0 || pg >= d.npages) {
         if (lane == 0) set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pg, (uint32_t)d.npages);
         break;
       }
-      const size_t pbase = (((size_t)l * d.npages + pg) * nkv + g) * kPageSize * HD;
-      const uint16_t *kb = d.k_pool + pbase;
-      const uint16_t *vb = d.v_pool + pbase;
-      u32x4 kr[KV4];
+      if (blk != blk0 + wave) {
+        const size_t pbase = (((size_t)l * d.npages + pg) * nkv + g) * kPageSize * HD;
 #pragma unroll
-      for (int i = 0; i < KV4; ++i) kr[i] = ldg((const u32x4 *)(kb + tq * HD + qd * DQ + i * 8));
-      uint32_t vr[VPOS];
+        for (int i = 0; i < KV4; ++i)
+          kr[i] = ldg((const u32x4 *)(d.k_pool + pbase + tq * HD + qd * DQ + i * 8));
 #pragma unroll
-      for (int i = 0; i < VPOS; ++i) {
-        const int tt = HD == 128 ? i : 2 * i + (lane >> 5);
-        vr[i] = ldg((const uint32_t *)(vb + tt * HD + vdim));
+        for (int i = 0; i < VPOS; ++i) {
+          const int tt = HD == 128 ? i : 2 * i + (lane >> 5);
+          vr[i] = ldg((const uint32_t *)(d.v_pool + pbase + tt * HD + vdim));
+        }
       }
       const int p = blk * kPageSize + tq;
       const bool valid = p >= lo && p < chi;
@@ -1014,28 +1049,66 @@ DEV void run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
       if (dd == 0) { sta(pp + HD, M); sta(pp + HD + 1, Ls); }
     }
   }
+  return true;
 }
 
-// Log-sum-exp merge of the S split partials of one (slot, KV head).
-DEV void run_merge(CP &d, const TD &t) {
+// Log-sum-exp merge of the S split partials (o[HD], m, l) of one (slot, KV
+// head): the group's G query heads.  One round of loads: every split's
+// (m, l) and each thread's output vector's partials of up to 8 splits are in
+// flight together; one wave per head turns (m, l) into the weights
+// 2^(m_s - M) / L in LDS; each output is the weighted sum.
+DEV void run_merge(Smem &sm, CP &d, const TD &t) {
   const int l = t.layer, b = t.a0, g = t.a1, G = d.G, S = d.S, HD = d.hd;
-  const int PS = HD + 4;
+  const int PS = HD + 4, hv = HD / 4, nvec = G * hv, npairs = G * S, s8 = min(S, 8);
+  const int tid = tidx(), lane = tid & 63, wave = uni(tid >> 6);
   const size_t head0 = ((size_t)l * d.B + b) * d.nq + (size_t)g * G;
-  for (int idx = tidx(); idx < G * HD; idx += kThreads) {
-    const int h = idx / HD, dd = idx - h * HD;
-    const float *pp = d.part + (head0 + h) * S * PS;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, lda(pp + s * PS + HD));
-    float Ls = 0.f, Os = 0.f;
-    if (M != -INFINITY)
-      for (int s = 0; s < S; ++s) {
-        const float ms = lda(pp + s * PS + HD);
-        if (ms == -INFINITY) continue;
-        const float f = exp2f(ms - M);
-        Ls = fmaf(f, lda(pp + s * PS + HD + 1), Ls);
-        Os = fmaf(f, lda(pp + s * PS + dd), Os);
-      }
-    sta(d.attn + (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f);
+  const float *part0 = d.part + head0 * S * PS;
+  const __amdgpu_buffer_rsrc_t r = rsrc(part0);
+  auto vec_at = [&](int h, int sp, int dd) {
+    return lda4(r, (uint32_t)((((size_t)h * S + sp) * PS + dd) * 4));
+  };
+  const int h = tid / hv, dd = (tid - h * hv) * 4;
+  f32x4 ov[8];
+#pragma unroll
+  for (int sp = 0; sp < 8; ++sp)
+    ov[sp] = (tid < nvec && sp < s8) ? vec_at(h, sp, dd) : (f32x4){0.f, 0.f, 0.f, 0.f};
+  float2 *ml = (float2 *)&sm.red[0][0];  // [G * S]: (m, l), then (weight, -)
+  for (int i = tid; i < npairs; i += kThreads) {
+    const float *pp = part0 + (size_t)i * PS + HD;  // pair i = head * S + split
+    ml[i] = make_float2(lda(pp), lda(pp + 1));
+  }
+  __syncthreads();
+  for (int hh = wave; hh < G; hh += kWaves) {
+    float mx = -INFINITY;
+    for (int sp = lane; sp < S; sp += 64) mx = fmaxf(mx, ml[hh * S + sp].x);
+    mx = wave_max(mx);
+    float lsum = 0.f;
+    for (int sp = lane; sp < S; sp += 64) {
+      const float2 e = ml[hh * S + sp];
+      lsum = fmaf(e.x == -INFINITY ? 0.f : exp2f(e.x - mx), e.y, lsum);
+    }
+    lsum = wave_sum(lsum);
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    for (int sp = lane; sp < S; sp += 64) {
+      const float mv = ml[hh * S + sp].x;
+      ml[hh * S + sp].x = mv == -INFINITY ? 0.f : exp2f(mv - mx) * inv;
+    }
+  }
+  __syncthreads();
+  for (int v = tid; v < nvec; v += kThreads) {
+    const int hh = v / hv, d0 = (v - hh * hv) * 4;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (v == tid) {
+#pragma unroll
+      for (int sp = 0; sp < 8; ++sp)
+        if (sp < s8) o += ml[hh * S + sp].x * ov[sp];
+    }
+    for (int sp = v == tid ? s8 : 0; sp < S; ++sp) o += ml[hh * S + sp].x * vec_at(hh, sp, d0);
+    float *dst = d.attn + (head0 + hh) * HD + d0;
+    sta(dst + 0, o.x);
+    sta(dst + 1, o.y);
+    sta(dst + 2, o.z);
+    sta(dst + 3, o.w);
   }
 }
 
@@ -1143,15 +1216,17 @@ DEV void run_argmax(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
 // Non-GEMV task (all waves): wait, run, publish (every wave drains its
 // stores, then thread 0 reports).
 DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent, WState &ws) {
-  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
-  trace_start(d, t);
+  if (t.op == OP_ATTN) {  // waits for its inputs itself, after a prefetch
+    const bool ok = d.hd == 128 ? run_attn<128>(sm, d, ca, t, persistent, ws)
+                                : run_attn<64>(sm, d, ca, t, persistent, ws);
+    if (!ok) return false;
+  } else {
+    if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+    trace_start(d, t);
+  }
   switch (t.op) {
     case OP_EMBED: run_embed(d, ca, t); break;
-    case OP_ATTN:
-      if (d.hd == 128) run_attn<128>(sm, d, ca, t);
-      else run_attn<64>(sm, d, ca, t);
-      break;
-    case OP_MERGE: run_merge(d, t); break;
+    case OP_MERGE: run_merge(sm, d, t); break;
     case OP_TOPK: run_topk(sm, d, t); break;
     case OP_COMBINE: run_combine(d, ca, t); break;
     case OP_ARGMAX: run_argmax(sm, d, ca, t); break;

@@ -214,7 +214,7 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   int want = std::max(1, n_cus / (nkv * B));
   int by_len = std::max(1, ctx / 64);
   p.S = std::max(1, std::min(std::min(want, by_len), 64));
-  if (o.attn_splits > 0) p.S = std::min(o.attn_splits, 256);
+  if (o.attn_splits > 0) p.S = std::min(o.attn_splits, 128);  // merge keeps G*S pairs in LDS
 
   // Expert tiles (weights chosen at run time) keep one register tile per
   // task; the static-weight operations are cut per worker below.
