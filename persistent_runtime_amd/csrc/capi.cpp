@@ -66,7 +66,9 @@ struct mk_plan {
   uint32_t epoch_limit = 1;
   int32_t *stage_tok = nullptr, *stage_pos = nullptr, *stage_next = nullptr;
   float *stage_logits = nullptr;
-  uint32_t *ctrl = nullptr;  // CTRL_WORDS control words then the event counters
+  uint32_t *ctrl = nullptr;  // CTRL_WORDS control words, the event counters, then
+                             // the split-attention arrival counters
+  int n_att_cnt = 0;
   int n_ctrl_words = 0;
 
   ~mk_plan() {
@@ -330,6 +332,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     // epoch limit: (epoch + 1) * max threshold must stay below 2^31
     int32_t max_thr = 1;
     for (int32_t v : hp.ev_thr) max_thr = std::max(max_thr, v);
+    max_thr = std::max(max_thr, hp.S);  // split-attention arrival counters
     p->epoch_limit = (uint32_t)(((1u << 31) - 1u) / (uint32_t)max_thr) - 2u;
 
     // device allocations
@@ -338,7 +341,8 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     int32_t *d_wq;
     if ((rc = p->alloc(&d_wq, hp.worker_off.size() + hp.worker_list.size(), "worker queues")))
       return rc;
-    p->n_ctrl_words = CTRL_WORDS + E;
+    p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads;
+    p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
     const int64_t nf = hp.n_x + hp.n_xmid + hp.n_q + 2 * hp.n_k + hp.n_part + hp.n_attn + hp.n_h +
                        hp.n_rl + hp.n_tk + hp.n_he + hp.n_ye + hp.n_amax;
@@ -415,6 +419,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.rope_sin = rope + (size_t)hp.max_pos * half;
     d.ctrl = p->ctrl;
     d.ev = p->ctrl + CTRL_WORDS;
+    d.att_cnt = d.ev + E;
     d.tasks = d_tasks;
     d.n_tasks = T;
     d.worker_off = d_wq;
@@ -465,13 +470,16 @@ static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positi
     }
     HIP_TRY(launch_persistent(plan->d_dev, ca, plan->grid, plan->hp.cfg.max_batch, s),
             "persistent launch");
-    if (++plan->epoch >= plan->epoch_limit) {
-      HIP_TRY(launch_zero_u32(d.ev, (int)plan->hp.ev_thr.size(), s), "counter reset");
-      plan->epoch = 0;
-    }
   } else {
     for (auto &ph : plan->hp.phases)
       HIP_TRY(launch_phase(plan->d_dev, ca, ph.first, ph.second - ph.first, s), "phase launch");
+  }
+  // counters are monotonic per step (both executors count split-attention
+  // arrivals); reset them before they could wrap
+  if (++plan->epoch >= plan->epoch_limit) {
+    HIP_TRY(launch_zero_u32(d.ev, (int)plan->hp.ev_thr.size() + plan->n_att_cnt, s),
+            "counter reset");
+    plan->epoch = 0;
   }
   return MK_OK;
 }

@@ -368,15 +368,16 @@ DEV void trace_mark(CP &d, const TD &t, int word) {
 }
 // Report the task's completions (a5 of them; 0 when a later task of the same
 // run reports them).  The caller (thread 0) has drained its wave's stores.
-DEV void signal_done(CP &d, const TD &t) {
-  if (tidx() == 0 && t.a5 > 0) {
+DEV void signal_count(CP &d, const TD &t, int count) {
+  if (tidx() == 0 && count > 0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       if (i < t.n_sig)
-        __hip_atomic_fetch_add(d.ev + t.sig_ev[i], (uint32_t)t.a5, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(d.ev + t.sig_ev[i], (uint32_t)count, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
   }
 }
+DEV void signal_done(CP &d, const TD &t) { signal_count(d, t, t.a5); }
 
 // ------------------------------------------------------------ GEMV tiles --
 // A tile is `nseg` blocks of `seg_rows` consecutive rows (row length K bf16)
@@ -1226,13 +1227,35 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
   }
   switch (t.op) {
     case OP_EMBED: run_embed(d, ca, t); break;
-    case OP_MERGE: run_merge(sm, d, t); break;
     case OP_TOPK: run_topk(sm, d, t); break;
     case OP_COMBINE: run_combine(d, ca, t); break;
     case OP_ARGMAX: run_argmax(sm, d, ca, t); break;
     default: break;
   }
   ws.x_src = nullptr;  // LDS reused: the activation cache is gone
+  if (t.op == OP_ATTN && d.S > 1) {
+    // Split attention: the partials are visible before this split's
+    // arrival is counted; the split that arrives last for its (slot, KV
+    // head) merges the group and reports its completion.
+    vm_drain();
+    __syncthreads();
+    if (persistent) trace_finish(d, t);
+    if (tidx() == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(
+          d.att_cnt + ((size_t)t.layer * d.B + t.a0) * d.nkv + t.a1, 1u, __ATOMIC_RELAXED,
+          __HIP_MEMORY_SCOPE_AGENT);
+      sm.imisc[1] = old == (ca.epoch + 1u) * (uint32_t)d.S - 1u;
+    }
+    __syncthreads();
+    const bool last = sm.imisc[1] != 0;
+    if (last) {
+      run_merge(sm, d, t);
+      vm_drain();
+    }
+    __syncthreads();
+    if (persistent) signal_count(d, t, last ? 1 : 0);
+    return true;
+  }
   if (persistent) vm_drain();
   __syncthreads();
   if (persistent) {

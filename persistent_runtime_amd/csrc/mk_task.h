@@ -116,6 +116,8 @@ struct DevPlan {
   const float *rope_cos, *rope_sin;                     // [max_pos][hd/2]
   // control
   uint32_t *ev;            // event counters, after CTRL_WORDS control words
+  uint32_t *att_cnt;       // split-attention arrivals per (layer, slot, KV head),
+                           // after the event counters; monotonic like them
   uint32_t *ctrl;
   const Task *tasks;           // worker-major: each worker's queue is contiguous
   int32_t n_tasks;

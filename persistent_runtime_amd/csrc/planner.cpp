@@ -152,7 +152,8 @@ struct RowSeg {
 // cut into one contiguous, near-equal share per worker (the balance is in
 // bytes, as every row has the same length); a share becomes one task per
 // segment piece, streamed in passes of at most one register tile, at most
-// pmax passes per task.  Returns the number of tasks added, or -1 when a
+// pmax passes per task.  With several segments the shares follow segment
+// boundaries instead (see below).  Returns the number of tasks added, or -1 when a
 // row does not fit one register tile.
 int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int K, int nseg,
              int n_workers, int pmax, int wait_ev, int64_t extra_bytes, int *lm_index) {
@@ -165,6 +166,54 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
   int64_t total = 0;
   for (auto &sg : segs) total += sg.rows;
   int added = 0;
+  if (segs.size() > 1 && (int64_t)segs.size() <= n_workers) {
+    // Several matrices (the q, k, v rows of each KV group): workers are
+    // shared out over the segments in proportion to their rows (largest
+    // remainder, at least one each), and each segment's rows evenly over its
+    // workers, so no worker's share straddles two matrices (one task each).
+    const int ns = (int)segs.size();
+    std::vector<int> nw(ns);
+    int given = 0;
+    for (int i = 0; i < ns; ++i) {
+      nw[i] = std::max(1, (int)((double)segs[i].rows * n_workers / (double)total));
+      given += nw[i];
+    }
+    // then one worker at a time to the segment with the largest share per
+    // worker (or away from the one whose share grows least)
+    auto share = [&](int i, int k) { return (double)segs[i].rows / k; };
+    while (given < n_workers) {
+      int bi = 0;
+      for (int i = 1; i < ns; ++i)
+        if (share(i, nw[i]) > share(bi, nw[bi])) bi = i;
+      nw[bi]++, given++;
+    }
+    while (given > n_workers) {
+      int bi = -1;
+      for (int i = 0; i < ns; ++i)
+        if (nw[i] > 1 && (bi < 0 || share(i, nw[i] - 1) < share(bi, nw[bi] - 1))) bi = i;
+      nw[bi]--, given--;
+    }
+    int w = 0;
+    for (int i = 0; i < ns; ++i) {
+      const RowSeg &sg = segs[i];
+      for (int k = 0; k < nw[i]; ++k, ++w) {
+        int64_t lo = (int64_t)sg.rows * k / nw[i], hi = (int64_t)sg.rows * (k + 1) / nw[i];
+        lo -= lo % unit;
+        hi = (k + 1 == nw[i]) ? sg.rows : hi - hi % unit;
+        while (lo < hi) {
+          int64_t n = std::min<int64_t>(hi - lo, (int64_t)pmax * R);
+          const int P = (int)((n + R - 1) / R);
+          int rpp = (int)((n + P - 1) / P);
+          rpp += (unit - rpp % unit) % unit;
+          b.add(op, layer, sg.a0, (int)(sg.row0 + lo), (int)n, 0, 0, {wait_ev}, {sg.sig},
+                n * row_bytes + extra_bytes, w, rpp);
+          ++added;
+          lo += n;
+        }
+      }
+    }
+    return added;
+  }
   size_t si = 0;
   int64_t seg_base = 0;  // rows before segs[si]
   for (int w = 0; w < n_workers; ++w) {
@@ -283,23 +332,16 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
       if (add_gemv(b, OP_QKV, l, segs, H, 1, n_workers, pmax_for(H), x_ev[l], 0, nullptr) < 0)
         ok = false;
     }
-    // attention splits (+ merge when split)
+    // attention splits; with several splits, the split that arrives last
+    // for its (slot, KV head) merges them and reports the head group's one
+    // completion (statically: the last split carries it)
     int mrg = b.ev();
-    std::vector<int> att(B * nkv, -1);
     b.begin_phase();
     for (int s = 0; s < B; ++s)
-      for (int g = 0; g < nkv; ++g) {
-        if (p.S > 1) att[s * nkv + g] = b.ev();
+      for (int g = 0; g < nkv; ++g)
         for (int sp = 0; sp < p.S; ++sp)
-          b.add(OP_ATTN, l, s, g, sp, 0, 0, {grp[g]},
-                {p.S > 1 ? att[s * nkv + g] : mrg}, 0);
-      }
-    if (p.S > 1) {
-      b.begin_phase();
-      for (int s = 0; s < B; ++s)
-        for (int g = 0; g < nkv; ++g)
-          b.add(OP_MERGE, l, s, g, 0, 0, 0, {att[s * nkv + g]}, {mrg}, 0);
-    }
+          b.add(OP_ATTN, l, s, g, sp, 0, 0, {grp[g]}, {mrg}, 0);
+    if (p.S > 1) p.ev_thr[mrg] = B * nkv;  // one merged group per (slot, KV head)
     // O projection + residual
     int xo = b.ev();
     b.begin_phase();
@@ -415,7 +457,9 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   }
   // A run of consecutive tasks in one queue that signal the same events
   // reports all its completions once, from its last task.
-  auto same_sig = [](const Task &a, const Task &b) {
+  const bool split_attn = p.S > 1;
+  auto same_sig = [&](const Task &a, const Task &b) {
+    if (split_attn && (a.op == OP_ATTN || b.op == OP_ATTN)) return false;
     if (a.n_sig != b.n_sig || a.n_sig == 0) return false;
     for (int k = 0; k < a.n_sig; ++k)
       if (a.sig_ev[k] != b.sig_ev[k]) return false;
@@ -432,6 +476,8 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
       while (j + 1 < lst.size() && same_sig(p.tasks[lst[j]], p.tasks[lst[j + 1]])) ++j;
       for (size_t m = k; m < j; ++m) p.tasks[lst[m]].a5 = 0;
       p.tasks[lst[j]].a5 = (int)(j - k + 1);
+      if (split_attn && p.tasks[lst[j]].op == OP_ATTN)
+        p.tasks[lst[j]].a5 = p.tasks[lst[j]].a2 == p.S - 1 ? 1 : 0;
       k = j + 1;
     }
     p.worker_off[w] = (int32_t)p.worker_list.size();
@@ -447,11 +493,14 @@ int validate_plan(const HostPlan &p, std::string &err) {
   std::vector<int> last_sig(E, -1), n_sig(E, 0), sig_phase(E, -1), n_wait(E, 0);
   for (int i = 0; i < T; ++i) {
     const Task &t = p.tasks[i];
+    // the splits of one (slot, KV head) report one completion between them
+    // (the last to arrive, after merging); any of them may be that one
+    const bool split = t.op == OP_ATTN && p.S > 1;
     for (int k = 0; k < t.n_sig; ++k) {
       int e = t.sig_ev[k];
       if (e < 0 || e >= E) { err = "signal of an unknown event"; return MK_ERR_PLAN; }
       last_sig[e] = i;
-      n_sig[e]++;
+      n_sig[e] += split ? (t.a2 == p.S - 1) : 1;
       sig_phase[e] = std::max(sig_phase[e], p.task_phase[i]);
     }
   }
