@@ -14,7 +14,6 @@ oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,14 +30,6 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in ("kernels.hip", "mk_task.h", "planner.cpp"):
-        with open(os.path.join(ROOT, "persistent_runtime_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def read_traffic(workload):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source (else None)."""
@@ -47,6 +38,7 @@ def read_traffic(workload):
         return None
     with open(p) as fh:
         t = json.load(fh)
+    from persistent_runtime_amd.traffic import kernel_source_hash
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("bytes_per_launch")
