@@ -190,6 +190,12 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts,
  * each.  Synchronises `stream`.  cap in tasks. */
 int mk_read_trace(mk_plan *plan, void *stream, uint32_t *out, int32_t cap);
 
+/* MoE plans: the expert ids (int32) and renormalised routing weights (fp32)
+ * the last step chose, [n_layers][max_batch][top_k] each, ids ascending per
+ * (layer, slot).  Synchronises `stream`; cap in entries; either output may be
+ * NULL.  MK_ERR_INVALID_ARG for a dense model. */
+int mk_read_routing(mk_plan *plan, void *stream, int32_t *ids, float *weights, int32_t cap);
+
 /* Number of tasks and events of a built plan, and the number of CUs it was
  * sized for. */
 int mk_plan_info(const mk_plan *plan, int32_t *n_tasks, int32_t *n_events,

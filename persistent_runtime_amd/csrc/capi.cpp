@@ -566,6 +566,19 @@ int mk_read_trace(mk_plan *plan, void *stream, uint32_t *out, int32_t cap) {
   return MK_OK;
 }
 
+int mk_read_routing(mk_plan *plan, void *stream, int32_t *ids, float *weights, int32_t cap) {
+  if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
+  if (!plan->d.tk_ids) return fail(MK_ERR_INVALID_ARG, "the plan's model has no experts");
+  DeviceGuard guard(plan->device);
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  const int64_t n = std::min<int64_t>(plan->hp.n_tk, cap);
+  if (n < 0) return fail(MK_ERR_INVALID_ARG, "negative capacity");
+  if (ids) HIP_TRY(hipMemcpy(ids, plan->d.tk_ids, (size_t)n * 4, hipMemcpyDeviceToHost), "read ids");
+  if (weights)
+    HIP_TRY(hipMemcpy(weights, plan->d.tk_w, (size_t)n * 4, hipMemcpyDeviceToHost), "read weights");
+  return MK_OK;
+}
+
 int mk_plan_info(const mk_plan *plan, int32_t *n_tasks, int32_t *n_events, int32_t *n_cus,
                  int32_t *n_phases) {
   if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");

@@ -33,7 +33,7 @@ OP_ID = {v: k for k, v in OPS.items()}
 # every function include/mk.h declares
 EXPORTS = ["mk_plan_options_default", "mk_build_plan", "mk_decode_step",
            "mk_prefill", "mk_plan_status", "mk_free", "mk_last_error",
-           "mk_inspect_plan", "mk_read_trace", "mk_plan_info"]
+           "mk_inspect_plan", "mk_read_trace", "mk_plan_info", "mk_read_routing"]
 
 
 class mk_config(C.Structure):
@@ -104,8 +104,9 @@ def _load():
                                     C.POINTER(mk_task_info), i32, pi32, pi32, i32, pi32]
     lib.mk_read_trace.argtypes = [vp, vp, C.POINTER(C.c_uint32), i32]
     lib.mk_plan_info.argtypes = [vp, pi32, pi32, pi32, pi32]
+    lib.mk_read_routing.argtypes = [vp, vp, pi32, C.POINTER(C.c_float), i32]
     for f in ("mk_build_plan", "mk_decode_step", "mk_prefill", "mk_plan_status",
-              "mk_inspect_plan", "mk_read_trace", "mk_plan_info"):
+              "mk_inspect_plan", "mk_read_trace", "mk_plan_info", "mk_read_routing"):
         getattr(lib, f).restype = C.c_int
     return lib
 
@@ -252,6 +253,18 @@ class Plan:
         buf = (C.c_uint32 * (6 * n))()
         _check(lib.mk_read_trace(self.handle, self._stream(stream), buf, n))
         return np.frombuffer(buf, dtype=np.uint32).reshape(n, 6).copy()
+
+    def read_routing(self, stream=None):
+        """Expert ids and weights of the last step: ([L, B, top_k] int32, float32)."""
+        import numpy as np
+        m = self.model
+        n = m["n_layers"] * self.cfg.max_batch * m["top_k"]
+        ids = (C.c_int32 * n)()
+        w = (C.c_float * n)()
+        _check(lib.mk_read_routing(self.handle, self._stream(stream), ids, w, n))
+        shape = (m["n_layers"], self.cfg.max_batch, m["top_k"])
+        return (np.frombuffer(ids, dtype=np.int32).reshape(shape).copy(),
+                np.frombuffer(w, dtype=np.float32).reshape(shape).copy())
 
     def free(self):
         if getattr(self, "handle", None):

@@ -84,3 +84,39 @@ def assert_ids(ids):
     for g, o, m in ids:
         if m > MARGIN:
             assert g == o, (g, o, m)
+
+
+ROUTE_TIE = 1e-3      # top-k boundary margin below which either routing is correct
+
+
+def oracle_step_matching_routes(Wt, cfg, cache, token, pos, dev_ids, slot=0):
+    """One oracle decode step whose MoE routing is reconciled with the
+    device's: a layer whose expert set differs from the oracle's is accepted
+    only when the sets differ by one expert at the top-k boundary and the
+    oracle's boundary margin is below ROUTE_TIE; the step is then re-run with
+    the device's experts forced at those layers (later layers see the forced
+    activations and are compared again).  Any other difference fails.
+    `dev_ids`: device routing [L, B, top_k].  Returns (logits, n forced)."""
+    import copy
+    snapK, snapV = list(cache.K), list(cache.V)
+    forced = {}
+    for _ in range(cfg["n_layers"] + 1):
+        cache.K, cache.V = list(snapK), list(snapV)
+        info = []
+        ref = O.decode_step(Wt, cfg, cache, token, pos, forced_experts=forced or None, info=info)
+        new = {}
+        for rec in info:
+            l = rec["layer"]
+            o_ids = sorted(int(e) for e in rec["ids"])
+            d_ids = sorted(int(e) for e in dev_ids[l, slot])
+            if o_ids == d_ids or l in forced:
+                continue
+            diff = set(o_ids) ^ set(d_ids)
+            assert len(diff) == 2 and rec["margin"] < ROUTE_TIE, (
+                f"layer {l}: device experts {d_ids} vs oracle {o_ids}, margin {rec['margin']}")
+            new[l] = d_ids
+            break  # later layers depend on this one: re-run before comparing them
+        if not new:
+            return ref, len(forced)
+        forced.update(new)
+    raise AssertionError("routing reconciliation did not converge")

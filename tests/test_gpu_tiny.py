@@ -14,7 +14,7 @@ import synth
 from persistent_runtime_amd import mk
 from synth.configs import TINY
 from tests.gpu_common import (LOGIT_TOL, Runner, assert_ids, bf16_ulp, oracle_weights,
-                              teacher_forced_run)
+                              teacher_forced_run, oracle_step_matching_routes)
 
 pytestmark = pytest.mark.gpu
 
@@ -202,7 +202,18 @@ def test_tiny_moe_teacher_forced(tiny_moe):
     Wd, Wt = tiny_moe
     cfg = TINY_MOE
     r = Runner(cfg, Wd, B=1, maxp=8)
-    worst, ids, _ = teacher_forced_run(r, Wt, _prompt(), 8)
+    worst, ids, cache = teacher_forced_run(r, Wt, _prompt(), 8)
     assert worst <= LOGIT_TOL, worst
     assert_ids(ids)
+    # a few more steps with the device's routing read back and reconciled
+    tok, pos = ids[-1][1], len(_prompt()) + 8
+    for _ in range(4):
+        g_ids, g_lg = r.step([tok], [pos])
+        dev_routes, dev_w = r.plan.read_routing()
+        assert dev_routes.shape == (cfg["n_layers"], 1, cfg["top_k"])
+        assert np.all(np.diff(dev_routes, axis=-1) > 0)  # ascending, distinct
+        assert np.allclose(dev_w.sum(-1), 1.0, atol=1e-5)
+        ref, _ = oracle_step_matching_routes(Wt, cfg, cache, tok, pos, dev_routes)
+        assert float(np.max(np.abs(g_lg[0] - ref))) <= LOGIT_TOL
+        tok, pos = O.greedy_argmax(ref), pos + 1
     r.plan.free()
