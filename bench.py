@@ -10,6 +10,10 @@ the kernel-per-op build of the same tiles on the same workload, and the CPU
 oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b]
+
+Other batch-1 workloads: moe30b (48-layer MoE, 128 experts top-8, after an
+8192-token synthetic KV context), longctx (the 8B shape after a 131072-token
+synthetic context), llama70b (80 layers, hidden 8192), tiny.
 """
 from __future__ import annotations
 
@@ -100,12 +104,42 @@ def run_decode(plan, tok_ring, pos_all, first, n, logits=None):
         plan.decode_step(tok_ring[k:k + 1], pos_all[k:k + 1], tok_ring[k + 1:k + 2], logits)
 
 
+# Batch-1 workloads: (model, how the context is made, its length).  "prompt":
+# a 39-token random prompt through mk_prefill; "synthetic": seeded N(0, sd^2)
+# bf16 keys/values written straight into the pages (the pages' 8K-context
+# MoE run and the 131072-token long-context run).
+WORKLOADS = {
+    "llama8b": ("llama8b", "prompt", PROMPT),
+    "tiny": ("tiny", "prompt", PROMPT),
+    "llama70b": ("llama70b", "prompt", PROMPT),
+    "moe30b": ("moe30b", "synthetic", 8192),
+    "longctx": ("llama8b", "synthetic", 131072),
+}
+
+
+def timed_steps(plan, tok_ring, pos_all, first, n, stream, torch):
+    """Time n steps with one event between consecutive launches on the
+    launch stream; returns (per-launch ms list, total seconds, wall seconds)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(n):
+        i = first + k
+        plan.decode_step(tok_ring[i:i + 1], pos_all[i:i + 1], tok_ring[i + 1:i + 2])
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    launch_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(n)]
+    return launch_ms, ev[0].elapsed_time(ev[n]) / 1e3, wall
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=504)
+    ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "tiny", "moe30b", "llama70b"])
+    ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOADS))
     ap.add_argument("--kpo-steps", type=int, default=64, help="kernel-per-op comparison steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kpo", action="store_true")
@@ -134,49 +168,51 @@ def main():
         print(json.dumps({"calib_copy_bytes": a.numel() * 4, "launches": 4}))
         return
 
-    model = synth.MODELS[args.workload]
-    W_, K_ = args.warmup, args.steps
-    total = PROMPT + W_ + K_
+    mname, ctx_kind, ctx0 = WORKLOADS[args.workload]
+    model = synth.MODELS[mname]
+    default_steps = {"moe30b": 248, "longctx": 56, "llama70b": 120}.get(args.workload, 504)
+    W_, K_ = args.warmup, args.steps if args.steps is not None else default_steps
+    total = ctx0 + W_ + K_
     maxp = (total + 15) // 16
-    log(f"[bench] workload={args.workload} warmup={W_} steps={K_} ctx {PROMPT}..{total - 1}")
+    log(f"[bench] workload={args.workload} warmup={W_} steps={K_} ctx {ctx0}..{total - 1}")
     t0 = time.time()
     Wd = synth.make_weights(model, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] weights generated in {time.time() - t0:.1f}s")
     kv = PagedKV(model, max_batch=1, max_pages_per_seq=maxp, device=dev)
     kv.assign(0, maxp * 16)
-    prompt = synth.make_prompt(PROMPT, model["vocab"]).to(dev)
-    pos_all = torch.arange(PROMPT, PROMPT + W_ + K_ + 1, dtype=torch.int32, device=dev)
+    if ctx_kind == "synthetic":
+        K, V = synth.make_kv_values(model, ctx0, device=dev)
+        kv.write_tokens(0, K, V)
+        del K, V
+        torch.cuda.empty_cache()
+    pos_all = torch.arange(ctx0, ctx0 + W_ + K_ + 1, dtype=torch.int32, device=dev)
 
     def build(executor):
         return mk.Plan(model, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=1,
                        opts=mk.default_options(executor=executor, planned_ctx=total))
 
+    def start(plan, ring):
+        """Context in place and the first token in ring[0]."""
+        if ctx_kind == "prompt":
+            prompt = synth.make_prompt(ctx0, model["vocab"]).to(dev)
+            plan.prefill(0, prompt, ctx0, 0, ring[0:1])
+        else:
+            ring[0] = int(synth.make_prompt(1, model["vocab"])[0])
+
     plan = build(mk.MK_EXEC_PERSISTENT)
     info = plan.info()
     tok_ring = torch.zeros(W_ + K_ + 1, dtype=torch.int32, device=dev)
-    plan.prefill(0, prompt, PROMPT, 0, tok_ring[0:1])
+    start(plan, tok_ring)
     run_decode(plan, tok_ring, pos_all, 0, W_)
     plan.check()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K_ + 1)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    ev[0].record(stream)
-    for k in range(K_):
-        i = W_ + k
-        plan.decode_step(tok_ring[i:i + 1], pos_all[i:i + 1], tok_ring[i + 1:i + 2])
-        ev[k + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
+    launch_ms, elapsed, wall = timed_steps(plan, tok_ring, pos_all, W_, K_, stream, torch)
     plan.check()
-    launch_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(K_)]
-    elapsed = ev[0].elapsed_time(ev[K_]) / 1e3
     ms_step = elapsed * 1e3 / K_
     tok_s = K_ / elapsed
     # algorithmic bytes: weights + KV of all attended positions, per step
-    ctxs = [PROMPT + W_ + k + 1 for k in range(K_)]
+    ctxs = [ctx0 + W_ + k + 1 for k in range(K_)]
     bytes_steps = [sol.step_bytes(model, [c]) for c in ctxs]
     bytes_mean = sum(bytes_steps) / K_
     avg_launch_s = sum(launch_ms) / K_ / 1e3
@@ -190,17 +226,12 @@ def main():
     if not args.no_kpo:
         plan_k = build(mk.MK_EXEC_KERNEL_PER_OP)
         ring2 = torch.zeros(W_ + K_ + 1, dtype=torch.int32, device=dev)
-        plan_k.prefill(0, prompt, PROMPT, 0, ring2[0:1])
+        start(plan_k, ring2)
         n = min(args.kpo_steps, W_ + K_)
         run_decode(plan_k, ring2, pos_all, 0, 2)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        run_decode(plan_k, ring2, pos_all, 2, n - 2)
-        e1.record(stream)
-        torch.cuda.synchronize()
+        kms_list, kel, _ = timed_steps(plan_k, ring2, pos_all, 2, n - 2, stream, torch)
         plan_k.check()
-        kms = e0.elapsed_time(e1) / (n - 2)
+        kms = kel * 1e3 / (n - 2)
         same = bool(torch.equal(ring2[:n], tok_ring[:n]))
         kpo = {"ms_per_step": round(kms, 4), "tokens_per_s": round(1e3 / kms, 2),
                "launches_per_step": plan_k.info()["n_phases"],
@@ -215,14 +246,16 @@ def main():
         cpu = cpu_baseline(model, synth.WEIGHT_SEED)
         log(f"[bench] cpu baseline {cpu['value']} tok/s in {time.time() - t0:.1f}s")
 
+    ctx_desc = (f"{ctx0}-token prompt" if ctx_kind == "prompt"
+                else f"{ctx0}-token synthetic KV context")
     out = {
         "metric": METRIC, "value": round(tok_s, 3), "unit": "tokens/s", "n_gpus": 1,
         "steps": K_, "warmup": W_, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.workload} decode, batch 1, 39-token prompt, "
-                               f"ctx {PROMPT + W_}..{total - 1}", "batch": 1,
-                   "prompt": PROMPT, "timed_steps": K_,
+        "config": {"workload": f"{mname} decode, batch 1, {ctx_desc}, "
+                               f"ctx {ctx0 + W_}..{total - 1}", "batch": 1,
+                   "context": ctx0, "timed_steps": K_,
                    "tasks_per_step": info["n_tasks"], "workgroups": info["n_cus"]},
         "sol_fraction": round(sol_frac, 4),
         "bytes_per_step": int(bytes_mean),
