@@ -139,6 +139,24 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts, mk_task_i
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Elements between consecutive experts when, in every layer and for each of
+// gate, up and down, expert e starts e * Fe * H elements after expert 0 (the
+// usual stacked [E, rows, cols] tensors); 0 otherwise.  Lets the device
+// compute an expert's address instead of reading the table.
+static int64_t expert_stride(const mk_config &c, const std::vector<const void *> &tab) {
+  const int L = c.n_layers, E = c.n_experts;
+  if (E == 0) return 0;
+  const int64_t st = (int64_t)c.hidden * c.expert_ffn_dim;
+  for (int m = 0; m < 3; ++m)
+    for (int l = 0; l < L; ++l) {
+      const size_t b = (size_t)10 * L + ((size_t)m * L + l) * E;
+      const char *p0 = (const char *)tab[b];
+      for (int e = 1; e < E; ++e)
+        if ((const char *)tab[b + e] != p0 + (size_t)e * st * 2) return 0;
+    }
+  return st;
+}
+
 // Fill the device addresses of every GEMV task (weights of its tile, input
 // activations, output and residual) once the plan's buffers exist.  `tab`
 // holds the per-layer weight pointers in check_weights' order.
@@ -149,6 +167,10 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
   const int QD = c.n_q_heads * c.head_dim, KVD = c.n_kv_heads * c.head_dim;
   const int F = c.ffn_dim, E = c.n_experts, TK = c.top_k, Fe = c.expert_ffn_dim;
   auto W = [&](int kind, int l) { return (const uint16_t *)tab[(size_t)kind * L + l]; };
+  // expert 0 of layer l of expert tensor m (0 gate, 1 up, 2 down)
+  auto EX = [&](int m, int l) {
+    return (const uint16_t *)tab[(size_t)10 * L + ((size_t)m * L + l) * E];
+  };
   for (Task &t : hp.tasks) {
     const int l = t.layer;
     t.w0 = t.w1 = nullptr;
@@ -210,17 +232,22 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
         break;
       case OP_EGATEUP: {
         const size_t bj = ((size_t)l * B + t.a0) * TK + t.a3;
+        t.w0 = EX(0, l);
+        t.w1 = EX(1, l);
         t.src = d.xmid + ((size_t)l * B + t.a0) * H;
         t.gain = W(1, l);
         t.K = H;
         t.dst = d.he + bj * Fe + t.a1;
         break;
       }
-      case OP_EDOWN: {
-        const size_t bj = ((size_t)l * B + t.a0) * TK + t.a3;
-        t.src = d.he + bj * Fe;
+      case OP_EDOWN: {  // all k routed experts of the slot, rows a1..a1+a2
+        const size_t bx = (size_t)l * B + t.a0;
+        t.w0 = EX(2, l);
+        t.src = d.he + bx * TK * Fe;
         t.K = Fe;
-        t.dst = d.ye + bj * H + t.a1;
+        t.dst = d.x + (bx + B) * H + t.a1;
+        t.aux = d.xmid + bx * H + t.a1;
+        t.ostride = H;
         break;
       }
       default:
@@ -345,7 +372,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
     const int64_t nf = hp.n_x + hp.n_xmid + hp.n_q + 2 * hp.n_k + hp.n_part + hp.n_attn + hp.n_h +
-                       hp.n_rl + hp.n_tk + hp.n_he + hp.n_ye + hp.n_amax;
+                       hp.n_rl + hp.n_tk + hp.n_he + hp.n_amax;
     float *fs;
     if ((rc = p->alloc(&fs, (size_t)nf, "activation scratch"))) return rc;
     int32_t *is;
@@ -401,6 +428,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.router = T16 + 9 * L;
     const size_t LE = (size_t)L * c.n_experts;
     d.e_gate = T16 + 10 * L; d.e_up = T16 + 10 * L + LE; d.e_down = T16 + 10 * L + 2 * LE;
+    d.e_stride = expert_stride(c, tab);
     d.k_pool = (uint16_t *)kv->k_pool;
     d.v_pool = (uint16_t *)kv->v_pool;
     d.page_table = kv->page_table;
@@ -408,7 +436,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     auto take = [&](int64_t n) { float *r = n ? f : nullptr; f += n; return r; };
     d.x = take(hp.n_x); d.xmid = take(hp.n_xmid); d.q = take(hp.n_q); d.k = take(hp.n_k);
     d.v = take(hp.n_k); d.part = take(hp.n_part); d.attn = take(hp.n_attn); d.h = take(hp.n_h);
-    d.rl = take(hp.n_rl); d.tk_w = take(hp.n_tk); d.he = take(hp.n_he); d.ye = take(hp.n_ye);
+    d.rl = take(hp.n_rl); d.tk_w = take(hp.n_tk); d.he = take(hp.n_he);
     d.amax_v = take(hp.n_amax);
     d.tk_ids = hp.n_tk ? is : nullptr;
     d.amax_i = is + hp.n_tk;

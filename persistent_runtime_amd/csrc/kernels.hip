@@ -543,6 +543,29 @@ DEV void stage_x(Smem &sm, WState &ws, const float *src, int K, int nb, const ui
   if (ws.x_src == src && ws.x_gain == gain && ws.x_K == K && ws.x_nb == nb) return;
   const int tid = tidx(), lane = tid & 63, wave = tid >> 6;
   const __amdgpu_buffer_rsrc_t r = rsrc(src);
+  if (!gain) {
+    // no normalisation: the nb rows are one flat copy, four 16-byte loads
+    // in flight per lane (K is a multiple of 256: every range test below is
+    // wave-uniform)
+    const int n4 = nb * (K / 4);
+    f32x4 *d4 = (f32x4 *)sm.xs;
+    for (int i0 = uni(wave) * 64; i0 < n4; i0 += 4 * kThreads) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * kThreads < n4)
+          v[u] = lda4(r, (uint32_t)((size_t)(i0 + u * kThreads + lane) * 16));
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * kThreads < n4) d4[i0 + u * kThreads + lane] = v[u];
+    }
+    __syncthreads();
+    ws.x_src = src;
+    ws.x_gain = gain;
+    ws.x_K = K;
+    ws.x_nb = nb;
+    return;
+  }
   const u32x2 *g2 = (const u32x2 *)gain;  // four bf16 gains per 16-byte vector
   for (int b = 0; b < nb; ++b) {
     f32x4 *d4 = (f32x4 *)(sm.xs + (size_t)b * K);
@@ -597,12 +620,13 @@ DEV void stage_x(Smem &sm, WState &ws, const float *src, int K, int nb, const ui
   ws.x_nb = nb;
 }
 
+// single-segment-input GEMV tasks (the expert down projection has its own code)
 DEV bool is_gemv(int op) {
   return op == OP_QKV || op == OP_OPROJ || op == OP_GATEUP || op == OP_DOWN ||
-         op == OP_ROUTER || op == OP_LMHEAD || op == OP_EGATEUP || op == OP_EDOWN;
+         op == OP_ROUTER || op == OP_LMHEAD || op == OP_EGATEUP;
 }
 // weights known before the task's inputs are (prefetchable)
-DEV bool static_weights(int op) { return is_gemv(op) && op != OP_EGATEUP && op != OP_EDOWN; }
+DEV bool static_weights(int op) { return is_gemv(op) && op != OP_EGATEUP; }
 // Passes of a static-weight task: rows [p*rpp, min((p+1)*rpp, a2)) of each
 // segment.
 DEV int task_rpp(int rpp, int rows) { return rpp > 0 && rpp < rows ? rpp : rows; }
@@ -617,21 +641,101 @@ DEV Geo pass_geo(const uint16_t *w0, const uint16_t *w1, int rows, int rpp, int 
 }
 DEV Geo static_geo(const TD &t) { return pass_geo(t.w0, t.w1, t.a2, t.rpp, t.K, 0); }
 
-// Expert tiles: the expert the router chose for (slot, expert slot).
-// Returns false (and flags an error) for an out-of-range id.
-DEV bool expert_geo(CP &d, const TD &t, Geo &g) {
-  const int e = uni(ldai(d.tk_ids + ((size_t)t.layer * d.B + t.a0) * d.topk + t.a3));
-  if (e < 0 || e >= d.E) {
-    if (tidx() == 0) set_error(d, DEVERR_BAD_INPUT, t.gidx, -1, (uint32_t)e, (uint32_t)d.E);
-    return false;
+// ---- MoE routing -----------------------------------------------------------
+// Order-preserving map of a float to a u32 key (a larger float has a larger
+// key); NaN maps to 0, below every number.
+DEV uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return f != f ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+}
+DEV float unkey(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// maximum / minimum of a u32 over the wave by DPP steps (rows, then across
+// rows by row broadcasts), returned uniform
+template <bool MAX> DEV uint32_t wave_ext_u32(uint32_t v) {
+  auto f = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  v = f(v, (uint32_t)dppi<DPP_XOR1>((int)v));
+  v = f(v, (uint32_t)dppi<DPP_XOR2>((int)v));
+  v = f(v, (uint32_t)dppi<DPP_HALF_MIRROR>((int)v));
+  v = f(v, (uint32_t)dppi<DPP_MIRROR>((int)v));
+  // row_bcast:15 into rows 1 and 3, then row_bcast:31 into rows 2 and 3
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k of the router logits of (layer, slot) in one wave.  The k largest
+// logits win (equal logits: the lower expert id; NaN only once no number is
+// left); the chosen experts are put in ascending id order and lane j < k ends
+// with the j-th one's id and its weight, the softmax over the k chosen
+// logits.  Each lane keeps the best of its own untaken logits; a round takes
+// the wave's best key, then the lowest id holding it, and only the lane that
+// owned it rescans.
+DEV void route_wave(CP &d, int l, int b, int &sid, float &sw) {
+  const int lane = tidx() & 63, E = d.E, K = d.topk;
+  const float *r = d.rl + ((size_t)l * d.B + b) * E;
+  constexpr int kPer = 8;  // logits per lane: E <= 512
+  uint32_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    key[i] = 0u;
+    if (i * 64 < E && i * 64 + lane < E) key[i] = fkey(lda(r + i * 64 + lane));
   }
-  const size_t le = (size_t)t.layer * d.E + e;
-  if (t.op == OP_EGATEUP)
-    g = make_geo(tab(d.e_gate, le) + (size_t)t.a1 * d.H, tab(d.e_up, le) + (size_t)t.a1 * d.H,
-                 t.a2, 2, d.H);
-  else
-    g = make_geo(tab(d.e_down, le) + (size_t)t.a1 * d.Fe, nullptr, t.a2, 1, d.Fe);
-  return true;
+  uint32_t taken = 0;
+  auto scan = [&](uint32_t &bk, uint32_t &bi) {  // best untaken (key, id) of this lane
+    bk = 0u;
+    bi = 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (i * 64 >= E) break;
+      const uint32_t e = (uint32_t)(i * 64 + lane);
+      const bool ok = e < (uint32_t)E && !((taken >> i) & 1u) && (key[i] > bk || (key[i] == bk && e < bi));
+      bk = ok ? key[i] : bk;
+      bi = ok ? e : bi;
+    }
+  };
+  uint32_t lk, li;
+  scan(lk, li);
+  int my_id = lane;
+  uint32_t my_key = 0u;
+  for (int j = 0; j < K; ++j) {
+    const uint32_t kmax = wave_ext_u32<true>(lk);
+    const uint32_t win = wave_ext_u32<false>(lk == kmax ? li : 0xffffffffu);
+    if (lane == j) { my_id = (int)win; my_key = kmax; }
+    if ((int)(win & 63u) == lane && win < (uint32_t)E) {
+      taken |= 1u << (win >> 6);
+      scan(lk, li);
+    }
+  }
+  // ascending id order: each chosen lane's rank, then a push to that lane
+  // (lanes >= k push to themselves)
+  int rank = lane;
+  if (lane < K) {
+    rank = 0;
+    for (int k2 = 0; k2 < K; ++k2) rank += __builtin_amdgcn_readlane(my_id, k2) < my_id ? 1 : 0;
+  }
+  const uint32_t okey = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)my_key);
+  const int oid = __builtin_amdgcn_ds_permute(rank * 4, my_id);
+  const float slg = lane < K ? unkey(okey) : -INFINITY;
+  const float mx = wave_max(slg);
+  const float ex = lane < K ? expf(slg - mx) : 0.f;
+  sw = ex / wave_sum(ex);
+  sid = lane < K && oid >= 0 && oid < E ? oid : 0;
+}
+
+// Expert e of layer l of expert tensor m (0 gate, 1 up, 2 down); base0 is
+// the layer's expert 0.  Uniform e (scalar table read) / per-lane e.
+DEV const uint16_t *const *expert_tab(CP &d, int m) {
+  return m == 0 ? d.e_gate : (m == 1 ? d.e_up : d.e_down);
+}
+DEV const uint16_t *expert_w_uni(CP &d, int m, int l, int e, const uint16_t *base0) {
+  if (d.e_stride) return base0 + (size_t)e * (size_t)d.e_stride;
+  return tab(expert_tab(d, m), (size_t)l * d.E + e);
+}
+DEV const uint16_t *expert_w_lane(CP &d, int m, int l, int e, const uint16_t *base0) {
+  if (d.e_stride) return base0 + (size_t)e * (size_t)d.e_stride;
+  return ldg((const uint16_t *const *)expert_tab(d, m) + (size_t)l * d.E + e);
 }
 
 // Control wave: write the outputs of rows [0, rows) for slots b0..b0+n-1.
@@ -677,7 +781,7 @@ DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const float *rsum
       case OP_GATEUP: case OP_EGATEUP:  // SwiGLU of the gate and up rows
         sta(dst, silu(y) * at(bi, i, 1));
         break;
-      default:  // QKV, ROUTER, EDOWN
+      default:  // QKV, ROUTER
         sta(dst, y);
         break;
     }
@@ -691,29 +795,49 @@ DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const float *rsum
 // a plain streaming loop, so the compiler holds each tile slot in one
 // register and waits for each slot's own load only.
 struct GemvShape2 {
-  Geo g;        // the first pass (static weights) or the expert tile
+  Geo g;        // the first pass
+  const uint16_t *w0, *w1;  // the task's first rows (experts: chosen here)
   int nb, bfirst, P, rpp, bb_max;
-  bool skip;    // expert task of an empty slot or rejected expert: no work
+  int sid;      // expert tasks: lane j < k holds the j-th routed expert id
+  float sw;     //   and its weight
+  bool skip;    // expert task of an empty slot: no work
 };
 
 // B1: compiled for plans with one slot (no slot chunks).
 template <bool B1>
-DEV GemvShape2 gemv_shape(CP &d, const CallArgs &ca, const TD &t) {
+DEV GemvShape2 gemv_shape(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
   GemvShape2 q;
   q.skip = false;
-  q.P = 1;
-  q.rpp = t.a2;
-  if (!static_weights(t.op)) {
+  q.sid = 0;
+  q.sw = 0.f;
+  q.w0 = t.w0;
+  q.w1 = t.w1;
+  if (t.op == OP_EGATEUP) {
     q.nb = 1;
     q.bfirst = t.a0;
-    q.skip = ldg(ca.positions + t.a0) < 0 || !expert_geo(d, t, q.g);
+    q.skip = ldg(ca.positions + t.a0) < 0;
+    if (!q.skip) {
+      // the control wave routes the slot; the ids reach the other waves
+      // through LDS (sm.imisc[48..] ids, sm.misc[48..] weights)
+      if (uni(tidx() >> 6) == 0) {
+        route_wave(d, t.layer, t.a0, q.sid, q.sw);
+        if ((tidx() & 63) < d.topk) {
+          sm.imisc[48 + (tidx() & 63)] = q.sid;
+          sm.misc[48 + (tidx() & 63)] = q.sw;
+        }
+      }
+      __syncthreads();
+      const int e = sm.imisc[48 + t.a3];
+      q.w0 = expert_w_uni(d, 0, t.layer, e, t.w0) + (size_t)t.a1 * t.K;
+      q.w1 = expert_w_uni(d, 1, t.layer, e, t.w1) + (size_t)t.a1 * t.K;
+    }
   } else {
     q.nb = B1 ? 1 : d.B;
     q.bfirst = 0;
-    q.g = static_geo(t);
-    q.P = n_passes(t);
-    q.rpp = task_rpp(t.rpp, t.a2);
   }
+  q.g = pass_geo(q.w0, q.w1, t.a2, t.rpp, t.K, 0);
+  q.P = n_passes(t);
+  q.rpp = task_rpp(t.rpp, t.a2);
   q.bb_max = B1 ? 1 : min(kMaxBatchGemv, kLdsXBytes / (q.g.K * 4));
   return q;
 }
@@ -733,7 +857,7 @@ DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
                   WState &ws) {
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   trace_start(d, t);
-  const GemvShape2 q = gemv_shape<B1>(d, ca, t);
+  const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t);
   if (q.skip) {
     if (persistent) {
       trace_finish(d, t);
@@ -763,6 +887,12 @@ DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
       __syncthreads();  // the next slot chunk restages xs and reuses the buffers
     }
   }
+  // the slot's routing, for the down projection and for read-back
+  if (t.op == OP_EGATEUP && t.a1 == 0 && t.a3 == 0 && lane < d.topk) {
+    const size_t o = ((size_t)t.layer * d.B + t.a0) * d.topk + lane;
+    stai(d.tk_ids + o, q.sid);
+    sta(d.tk_w + o, q.sw);
+  }
   if (persistent) {
     // The epilogue's stores are all this wave's: drain them only where the
     // run's completions are reported (the wait covers the earlier tasks too).
@@ -782,12 +912,12 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
                   WState &ws, Buf &w, bool w_loaded, bool pre, const Geo &gn) {
   const int cw = uni(tidx() >> 6) - 1;
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
-  const GemvShape2 q = gemv_shape<B1>(d, ca, t);
+  const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t);
   if (q.skip) return true;
   if (!w_loaded) load_slots(q.g, w, cw);
   if (!gemv_fits(d, t, q)) return false;
   const int K = q.g.K;
-  auto geo_of = [&](int p) { return p == 0 ? q.g : pass_geo(t.w0, t.w1, t.a2, t.rpp, K, p); };
+  auto geo_of = [&](int p) { return p == 0 ? q.g : pass_geo(q.w0, q.w1, t.a2, t.rpp, K, p); };
   float *red = &sm.red[0][0];
   float *rsum = &sm.rows[0][0];
   for (int b0 = 0; b0 < q.nb; b0 += q.bb_max) {
@@ -821,6 +951,123 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   return true;
 }
 
+// ---- MoE down projection + combine ------------------------------------------
+// Output rows [a1, a1+a2) of slot a0 over all k routed experts.  The tile is
+// k segments, segment j being rows [a1, a1+a2) of the j-th routed expert's
+// down matrix (ascending expert id), each a whole number of 1 KiB chunks, so
+// every chunk lies in one segment; segment j multiplies that expert's h,
+// staged in LDS at j*Fe.  Row sums of segment j land at rows[j*a2 + r]; the
+// control wave writes x_mid + sum_j w_j y_j (ascending expert order).
+struct DownShape {
+  int units, cpw, cps;  // 1 KiB chunks of the tile, per compute wave, per segment
+  bool skip;            // empty slot
+};
+DEV DownShape down_shape(CP &d, const CallArgs &ca, const TD &t) {
+  DownShape s;
+  s.skip = ldg(ca.positions + t.a0) < 0;
+  s.cps = (t.a2 * t.K * 2) >> 10;
+  s.units = s.cps * d.topk;
+  s.cpw = (s.units + kCW - 1) / kCW;
+  return s;
+}
+// lane j < k: the slot's j-th routed expert and its weight (written by the
+// slot's first gate/up task, which the down tasks wait for)
+DEV void routed(CP &d, const TD &t, int &id, float &w) {
+  const int lane = tidx() & 63;
+  id = 0;
+  w = 0.f;
+  if (lane < d.topk) {
+    const size_t o = ((size_t)t.layer * d.B + t.a0) * d.topk + lane;
+    id = ldai(d.tk_ids + o);
+    w = lda(d.tk_w + o);
+    if (id < 0 || id >= d.E) id = 0;
+  }
+}
+
+DEV bool down_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
+                  WState &ws) {
+  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  trace_start(d, t);
+  const DownShape s = down_shape(d, ca, t);
+  const int lane = tidx() & 63;
+  if (s.skip) {
+    for (int i = lane; i < t.a2; i += 64) sta(t.dst + i, 0.f);
+  } else {
+    int id;
+    float w;
+    routed(d, t, id, w);
+    stage_x(sm, ws, t.src, t.K, d.topk, nullptr, d.eps);
+    trace_mark(d, t, 0);
+    const float aux0 = lane < t.a2 ? lda(t.aux + lane) : 0.f;
+    __syncthreads();  // partials complete
+    __syncthreads();  // row sums complete
+    trace_mark(d, t, 1);
+    const float *rsum = &sm.rows[0][0];
+    for (int i = lane; i < t.a2; i += 64) {
+      float acc = 0.f;
+      for (int j = 0; j < d.topk; ++j) acc = fmaf(lanef(w, j), rsum[j * t.a2 + i], acc);
+      sta(t.dst + i, (i < 64 ? aux0 : lda(t.aux + i)) + acc);
+    }
+  }
+  if (persistent) {
+    if (t.a5 > 0) vm_drain();
+    trace_finish(d, t);
+    signal_done(d, t);
+  }
+  return true;
+}
+
+DEV bool down_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
+                  WState &ws) {
+  const int cw = uni(tidx() >> 6) - 1, lane = tidx() & 63;
+  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  const DownShape s = down_shape(d, ca, t);
+  if (s.skip) return true;
+  int id;
+  float wt;
+  routed(d, t, id, wt);
+  // lane j: the first row of segment j
+  const uint64_t base = (uint64_t)(expert_w_lane(d, 2, t.layer, id, t.w0) + (size_t)t.a1 * t.K);
+  const int blo = (int)(uint32_t)base, bhi = (int)(uint32_t)(base >> 32);
+  const int q0 = cw * s.cpw;
+  const int cnt = min(s.cpw, s.units - q0);
+  const uint32_t lane16 = (uint32_t)lane * 16u;
+  Buf w;
+  int sg = q0 / s.cps, rr = q0 - sg * s.cps;
+#pragma unroll
+  for (int j = 0; j < kMaxChunks; ++j) {
+    const int sj = j < cnt ? sg : 0, rj = j < cnt ? rr : 0;
+    const uint64_t b = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(bhi, sj) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane(blo, sj);
+    w[j] = ldnt((const u32x4 *)(b + (uint64_t)rj * 1024u + lane16));
+    if (j < cnt && ++rr == s.cps) { rr = 0; ++sg; }
+  }
+  stage_x(sm, ws, t.src, t.K, d.topk, nullptr, d.eps);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  const int Fe = t.K, step = 512 % Fe;
+  float *red = &sm.red[0][0];
+  int col = (int)(((uint32_t)q0 * 512u + (uint32_t)lane * 8u) % (uint32_t)Fe);
+  sg = q0 / s.cps;
+  rr = q0 - sg * s.cps;
+  float *pp = red + q0 * 4 + (lane >> 4);
+  const bool writer = (lane & 15) == 0;
+#pragma unroll
+  for (int j = 0; j < kMaxChunks; ++j) {
+    if (j < cnt) {
+      const float v = row16_sum(dot8(w[j], sm.xs + sg * Fe + col));
+      if (writer) pp[j * 4] = v;
+      col += step;
+      col = col >= Fe ? col - Fe : col;
+      if (++rr == s.cps) { rr = 0; ++sg; }
+    }
+  }
+  __syncthreads();  // partials complete
+  const int R = d.topk * t.a2;
+  gemv_rows(Fe, 1, [&](int) { return R; }, red, &sm.rows[0][0], 1, cw);
+  __syncthreads();  // row sums complete
+  return true;
+}
+
 // -------------------------------------------------------------- attention --
 // One (slot, KV head, split) task: the query heads of the group attend to
 // the cached keys of positions [lo, min(hi, pos)) of the split, read page by
@@ -828,11 +1075,16 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
 // current position also rotates and stores the new key/value (bf16) and
 // attends to it.  Softmax runs online in base 2 on log2(e)/sqrt(hd)-scaled
 // scores; the task leaves (max, sum, weighted values) for the merge, or the
-// normalised output when there is a single split.  The cached pages do not
-// depend on this step's projections: each wave loads its first page before
-// the task waits for the query/key/value tiles of its group.
+// normalised output when there is a single split.  Wave w takes the split's
+// pages w, w+8, ...: their page ids are read 64 at a time (lane i holding the
+// i-th) and two pages' keys and values are in flight while one is consumed.
+// The cached pages do not depend on this step's projections: the ids and the
+// first two pages are loaded before the task waits for the query/key/value
+// tiles of its group.
 // Returns false when the step is drained after an error.
-template <int HD>
+// GM >= G: the heads of a group are processed GM at a time as independent
+// dependency chains (heads G..GM-1, when present, compute unused values).
+template <int HD, int GM>
 DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
                   WState &ws) {
   const int tix = t.gidx;
@@ -840,8 +1092,12 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   const int G = d.G, S = d.S, B = d.B, nkv = d.nkv, nq = d.nq;
   const int tid = tidx(), lane = tid & 63, wave = uni(tid >> 6);
   constexpr int PS = HD + 4;
-  float *qs = sm.xs;                         // [G][HD]
-  float *kc = qs + kMaxGroup * HD;           // [HD]
+  // Queries: each head's row is four quarters of HD/4, a lane reading the
+  // quarter of its key dims; quarters are padded by 16 bytes so the four
+  // quarters a wave reads at once lie in different LDS banks.
+  constexpr int QQ = HD / 4 + 4, QROW = 4 * QQ;
+  float *qs = sm.xs;                         // [G][4][QQ]
+  float *kc = qs + kMaxGroup * QROW;         // [HD]
   float *vc = kc + HD;                       // [HD]
   float *wm = vc + HD;                       // [kWaves][kMaxGroup]
   float *wl = wm + kWaves * kMaxGroup;       // [kWaves][kMaxGroup]
@@ -861,23 +1117,37 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   const int hi = pos_ok ? (int)((int64_t)(sp + 1) * n / S) : 0;
   const int chi = hi < pos ? hi : pos;  // cached keys [lo, chi)
   const int blk0 = lo / kPageSize, blk1 = chi > lo ? (chi - 1) / kPageSize : -1;
-  // prefetch of this wave's first page
-  u32x4 kr[KV4];
-  uint32_t vr[VPOS];
-  int pg_first = -1;
-  if (blk0 + wave <= blk1) {
-    pg_first = uni(ldg(d.page_table + (size_t)b * d.maxp + blk0 + wave));
-    if (pg_first >= 0 && pg_first < d.npages) {
-      const size_t pbase = (((size_t)l * d.npages + pg_first) * nkv + g) * kPageSize * HD;
+  // this wave's pages: blk0 + wave + i * kWaves for i < npw
+  const int npw = blk1 >= blk0 + wave ? (blk1 - blk0 - wave) / kWaves + 1 : 0;
+  const int32_t *ptab = d.page_table + (size_t)b * d.maxp + blk0 + wave;
+  auto page_ids = [&](int c0) {  // lane i: the id of page c0 + i (or -1)
+    const int i = c0 + lane;
+    return i < npw ? ldg(ptab + (size_t)i * kWaves) : -1;
+  };
+  u32x4 kA[KV4], kB[KV4];
+  uint32_t vA[VPOS], vB[VPOS];
+  // keys (lane: position tq, dims qd*DQ ..) and values (lane: dims vdim,
+  // vdim+1 of its VPOS positions) of page i of the current id chunk
+  auto load_page = [&](int pid, int i, u32x4 *kr, uint32_t *vr) {
+    int pg = __builtin_amdgcn_readlane(pid, i);
+    pg = pg >= 0 && pg < d.npages ? pg : 0;  // a bad id is reported before use
+    const size_t pbase = (((size_t)l * d.npages + pg) * nkv + g) * kPageSize * HD;
 #pragma unroll
-      for (int i = 0; i < KV4; ++i)
-        kr[i] = ldg((const u32x4 *)(d.k_pool + pbase + tq * HD + qd * DQ + i * 8));
+    for (int k = 0; k < KV4; ++k)
+      kr[k] = ldg((const u32x4 *)(d.k_pool + pbase + tq * HD + qd * DQ + k * 8));
 #pragma unroll
-      for (int i = 0; i < VPOS; ++i) {
-        const int tt = HD == 128 ? i : 2 * i + (lane >> 5);
-        vr[i] = ldg((const uint32_t *)(d.v_pool + pbase + tt * HD + vdim));
-      }
+    for (int k = 0; k < VPOS; ++k) {
+      const int tt = HD == 128 ? k : 2 * k + (lane >> 5);
+      vr[k] = ldg((const uint32_t *)(d.v_pool + pbase + tt * HD + vdim));
     }
+  };
+  // (Everything loaded here has arrived before the page loop: the task's
+  // own input loads after the wait are waited for in order.)
+  int pid = -1;
+  if (npw > 0) {
+    pid = page_ids(0);
+    load_page(pid, 0, kA, vA);
+    if (npw > 1) load_page(pid, 1, kB, vB);
   }
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   trace_start(d, t);
@@ -906,7 +1176,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     const float a = lda(qg + h * HD + i0), c2 = lda(qg + h * HD + i0 + HD / 2);
     const float cv = ldg(cs + i0), sv = ldg(sn + i0);
     const float r = (i < HD / 2) ? a * cv - c2 * sv : a * sv + c2 * cv;
-    qs[h * HD + i] = r * scale;
+    qs[h * QROW + (i / (HD / 4)) * QQ + (i & (HD / 4 - 1))] = r * scale;
   }
   if (has_cur) {
     const size_t kvo = (((size_t)l * B + b) * nkv + g) * HD;
@@ -930,81 +1200,116 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     }
   }
   __syncthreads();
+  trace_mark(d, t, 0);
 
-  // --- page loop: wave w takes pages blk0+w, blk0+w+kWaves, ... (the first
-  // one already loaded)
-  float m[kMaxGroup], ls[kMaxGroup], o0[kMaxGroup], o1[kMaxGroup];
+  // --- page loop
+  float m[GM], ls[GM], o0[GM], o1[GM];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) { m[h] = -INFINITY; ls[h] = 0.f; o0[h] = 0.f; o1[h] = 0.f; }
-  if (chi > lo) {
-    for (int blk = blk0 + wave; blk <= blk1; blk += kWaves) {
-      const int pg = blk == blk0 + wave ? pg_first
-                                        : uni(ldg(d.page_table + (size_t)b * d.maxp + blk));
-      if (pg < 0 || pg >= d.npages) {
-        if (lane == 0) set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pg, (uint32_t)d.npages);
-        break;
+  for (int h = 0; h < GM; ++h) { m[h] = -INFINITY; ls[h] = 0.f; o0[h] = 0.f; o1[h] = 0.f; }
+  // online softmax over the 16 positions of page i of this wave; every step
+  // runs for all GM heads before the next (independent chains, no branches)
+  auto consume = [&](int i, const u32x4 *kr, const uint32_t *vr) {
+    const int p = (blk0 + wave + i * kWaves) * kPageSize + tq;
+    const bool valid = p >= lo && p < chi;
+    float sc[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      const float *qh = qs + h * QROW + qd * QQ;
+      float pk[KV4];  // one short chain per 16-byte key load
+#pragma unroll
+      for (int k = 0; k < KV4; ++k) {
+        const f32x4 x0 = *(const f32x4 *)(qh + k * 8), x1 = *(const f32x4 *)(qh + k * 8 + 4);
+        float c = bf_lo(kr[k].x) * x0.x;
+        c = fmaf(bf_hi(kr[k].x), x0.y, c);
+        c = fmaf(bf_lo(kr[k].y), x0.z, c);
+        c = fmaf(bf_hi(kr[k].y), x0.w, c);
+        c = fmaf(bf_lo(kr[k].z), x1.x, c);
+        c = fmaf(bf_hi(kr[k].z), x1.y, c);
+        c = fmaf(bf_lo(kr[k].w), x1.z, c);
+        c = fmaf(bf_hi(kr[k].w), x1.w, c);
+        pk[k] = c;
       }
-      if (blk != blk0 + wave) {
-        const size_t pbase = (((size_t)l * d.npages + pg) * nkv + g) * kPageSize * HD;
+      float a = pk[0];
 #pragma unroll
-        for (int i = 0; i < KV4; ++i)
-          kr[i] = ldg((const u32x4 *)(d.k_pool + pbase + tq * HD + qd * DQ + i * 8));
-#pragma unroll
-        for (int i = 0; i < VPOS; ++i) {
-          const int tt = HD == 128 ? i : 2 * i + (lane >> 5);
-          vr[i] = ldg((const uint32_t *)(d.v_pool + pbase + tt * HD + vdim));
-        }
-      }
-      const int p = blk * kPageSize + tq;
-      const bool valid = p >= lo && p < chi;
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h >= G) break;
-        const float *qh = qs + h * HD + qd * DQ;
-        float a = 0.f;
-#pragma unroll
-        for (int i = 0; i < KV4; ++i) {
-          const f32x4 x0 = *(const f32x4 *)(qh + i * 8), x1 = *(const f32x4 *)(qh + i * 8 + 4);
-          a = fmaf(bf_lo(kr[i].x), x0.x, a);
-          a = fmaf(bf_hi(kr[i].x), x0.y, a);
-          a = fmaf(bf_lo(kr[i].y), x0.z, a);
-          a = fmaf(bf_hi(kr[i].y), x0.w, a);
-          a = fmaf(bf_lo(kr[i].z), x1.x, a);
-          a = fmaf(bf_hi(kr[i].z), x1.y, a);
-          a = fmaf(bf_lo(kr[i].w), x1.z, a);
-          a = fmaf(bf_hi(kr[i].w), x1.w, a);
-        }
-        a = quad_sum(a);
-        const float s = valid ? a : -INFINITY;
-        const float mb = quads_max(s);
-        const float mn = fmaxf(m[h], mb);
-        if (mn == -INFINITY) continue;
-        const float alpha = exp2f(m[h] - mn);
-        const float pe = exp2f(s - mn);
-        const float psum = quads_sum(pe);
-        ls[h] = ls[h] * alpha + psum;
-        m[h] = mn;
-        float a0 = o0[h] * alpha, a1 = o1[h] * alpha;
-#pragma unroll
-        for (int i = 0; i < VPOS; ++i) {
-          float pt;
-          if (HD == 128) {
-            pt = lanef(pe, i * 4);
-          } else {  // lanes 0-31 take even positions, 32-63 odd ones
-            const float pe_even = lanef(pe, 8 * i), pe_odd = lanef(pe, 8 * i + 4);
-            pt = (lane >> 5) ? pe_odd : pe_even;
-          }
-          a0 = fmaf(pt, bf_lo(vr[i]), a0);
-          a1 = fmaf(pt, bf_hi(vr[i]), a1);
-        }
-        o0[h] = a0;
-        o1[h] = a1;
-      }
+      for (int k = 1; k < KV4; ++k) a += pk[k];
+      sc[h] = a;
+      // two heads at a time: their query slices (2 x DQ floats) stay in
+      // registers, not all GM heads' at once
+      if (h & 1) __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      const float a = quad_sum(sc[h]);
+      sc[h] = valid ? a : -INFINITY;
+    }
+    float pe[GM];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      const float mn = fmaxf(m[h], quads_max(sc[h]));
+      const bool live = mn != -INFINITY;
+      const float alpha = live ? exp2f(m[h] - mn) : 1.f;
+      pe[h] = live ? exp2f(sc[h] - mn) : 0.f;
+      m[h] = live ? mn : m[h];
+      ls[h] *= alpha;
+      o0[h] *= alpha;
+      o1[h] *= alpha;
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h) ls[h] += quads_sum(pe[h]);
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      // two chains per output (even / odd positions)
+      float a0 = o0[h], a1 = o1[h], b0 = 0.f, b1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < VPOS; ++k) {
+        float pt;
+        if (HD == 128) {
+          pt = lanef(pe[h], k * 4);
+        } else {  // lanes 0-31 take even positions, 32-63 odd ones
+          const float pe_even = lanef(pe[h], 8 * k), pe_odd = lanef(pe[h], 8 * k + 4);
+          pt = (lane >> 5) ? pe_odd : pe_even;
+        }
+        if (k & 1) {
+          b0 = fmaf(pt, bf_lo(vr[k]), b0);
+          b1 = fmaf(pt, bf_hi(vr[k]), b1);
+        } else {
+          a0 = fmaf(pt, bf_lo(vr[k]), a0);
+          a1 = fmaf(pt, bf_hi(vr[k]), a1);
+        }
+      }
+      o0[h] = a0 + b0;
+      o1[h] = a1 + b1;
+    }
+  };
+  // Inside the loop no load is skipped by a branch (a page past the end
+  // re-reads the last one): a load that a branch may skip makes the compiler
+  // wait for every load in flight instead of one buffer's.
+  for (int c0 = 0; c0 < npw; c0 += 64) {
+    const int nc = min(64, npw - c0);
+    if (c0 > 0) {
+      pid = page_ids(c0);
+      load_page(pid, 0, kA, vA);
+      load_page(pid, min(1, nc - 1), kB, vB);
+    }
+    const uint64_t bad = __ballot(lane < nc && (pid < 0 || pid >= d.npages));
+    if (bad) {
+      if (lane == (int)__builtin_ctzll(bad))
+        set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pid, (uint32_t)d.npages);
+      break;
+    }
+    int i = 0;
+    for (; i + 2 < nc; i += 2) {
+      consume(c0 + i, kA, vA);
+      load_page(pid, i + 2, kA, vA);
+      consume(c0 + i + 1, kB, vB);
+      load_page(pid, min(i + 3, nc - 1), kB, vB);
+    }
+    consume(c0 + i, kA, vA);
+    if (i + 1 < nc) consume(c0 + i + 1, kB, vB);
   }
   // per-wave state to LDS
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
+  for (int h = 0; h < GM; ++h) {
     if (h >= G) break;
     float a0 = o0[h], a1 = o1[h];
     if (HD == 64) { a0 += __shfl_xor(a0, 32, 64); a1 += __shfl_xor(a1, 32, 64); }
@@ -1016,11 +1321,13 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   }
   if (has_cur && wave < G) {  // score of the current key for head `wave`
     float a = 0.f;
-    for (int i = lane; i < HD; i += 64) a = fmaf(qs[wave * HD + i], kc[i], a);
+    for (int i = lane; i < HD; i += 64)
+      a = fmaf(qs[wave * QROW + (i / (HD / 4)) * QQ + (i & (HD / 4 - 1))], kc[i], a);
     a = wave_sum(a);
     if (lane == 0) scur[wave] = a;
   }
   __syncthreads();
+  trace_mark(d, t, 1);
   // merge the waves (fixed order) and the current key
   for (int idx = tid; idx < G * HD; idx += kThreads) {
     const int h = idx / HD, dd = idx - h * HD;
@@ -1054,25 +1361,34 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
 }
 
 // Log-sum-exp merge of the S split partials (o[HD], m, l) of one (slot, KV
-// head): the group's G query heads.  One round of loads: every split's
-// (m, l) and each thread's output vector's partials of up to 8 splits are in
-// flight together; one wave per head turns (m, l) into the weights
-// 2^(m_s - M) / L in LDS; each output is the weighted sum.
+// head): the group's G query heads.  Every thread takes one 16-byte output
+// vector and a subset of the splits (split sp goes to subset sp mod nsub);
+// its first 16 partial vectors are loaded together with every split's (m, l)
+// before anything is consumed.  One wave per head turns (m, l) into the
+// weights 2^(m_s - M) / L in LDS; each thread adds up its weighted vectors,
+// and the subsets are added in a fixed order (deterministic).
 DEV void run_merge(Smem &sm, CP &d, const TD &t) {
   const int l = t.layer, b = t.a0, g = t.a1, G = d.G, S = d.S, HD = d.hd;
-  const int PS = HD + 4, hv = HD / 4, nvec = G * hv, npairs = G * S, s8 = min(S, 8);
+  const int PS = HD + 4, hv = HD / 4, nvec = G * hv, npairs = G * S;
+  const int nsub = kThreads / nvec;
   const int tid = tidx(), lane = tid & 63, wave = uni(tid >> 6);
   const size_t head0 = ((size_t)l * d.B + b) * d.nq + (size_t)g * G;
   const float *part0 = d.part + head0 * S * PS;
   const __amdgpu_buffer_rsrc_t r = rsrc(part0);
-  auto vec_at = [&](int h, int sp, int dd) {
-    return lda4(r, (uint32_t)((((size_t)h * S + sp) * PS + dd) * 4));
-  };
-  const int h = tid / hv, dd = (tid - h * hv) * 4;
-  f32x4 ov[8];
+  const int v = tid % nvec, sub = tid / nvec;
+  const bool act = sub < nsub;
+  const int h = v / hv, dd = (v - h * hv) * 4;
+  constexpr int kBatch = 16;
+  f32x4 ov[kBatch];
+  auto load_batch = [&](int base) {
 #pragma unroll
-  for (int sp = 0; sp < 8; ++sp)
-    ov[sp] = (tid < nvec && sp < s8) ? vec_at(h, sp, dd) : (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < kBatch; ++k) {
+      const int sp = base + sub + k * nsub;
+      ov[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (act && sp < S) ov[k] = lda4(r, (uint32_t)((((size_t)h * S + sp) * PS + dd) * 4));
+    }
+  };
+  load_batch(0);
   float2 *ml = (float2 *)&sm.red[0][0];  // [G * S]: (m, l), then (weight, -)
   for (int i = tid; i < npairs; i += kThreads) {
     const float *pp = part0 + (size_t)i * PS + HD;  // pair i = head * S + split
@@ -1096,20 +1412,27 @@ DEV void run_merge(Smem &sm, CP &d, const TD &t) {
     }
   }
   __syncthreads();
-  for (int v = tid; v < nvec; v += kThreads) {
-    const int hh = v / hv, d0 = (v - hh * hv) * 4;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (v == tid) {
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < S; base += kBatch * nsub) {
+    if (base > 0) load_batch(base);
 #pragma unroll
-      for (int sp = 0; sp < 8; ++sp)
-        if (sp < s8) o += ml[hh * S + sp].x * ov[sp];
+    for (int k = 0; k < kBatch; ++k) {
+      const int sp = base + sub + k * nsub;
+      if (act && sp < S) o += ml[h * S + sp].x * ov[k];
     }
-    for (int sp = v == tid ? s8 : 0; sp < S; ++sp) o += ml[hh * S + sp].x * vec_at(hh, sp, d0);
+  }
+  f32x4 *red = (f32x4 *)sm.xs;  // [nsub][nvec]
+  if (act) red[sub * nvec + v] = o;
+  __syncthreads();
+  for (int vv = tid; vv < nvec; vv += kThreads) {
+    f32x4 sum = red[vv];
+    for (int q = 1; q < nsub; ++q) sum += red[q * nvec + vv];
+    const int hh = vv / hv, d0 = (vv - hh * hv) * 4;
     float *dst = d.attn + (head0 + hh) * HD + d0;
-    sta(dst + 0, o.x);
-    sta(dst + 1, o.y);
-    sta(dst + 2, o.z);
-    sta(dst + 3, o.w);
+    sta(dst + 0, sum.x);
+    sta(dst + 1, sum.y);
+    sta(dst + 2, sum.z);
+    sta(dst + 3, sum.w);
   }
 }
 
@@ -1129,68 +1452,6 @@ DEV void run_embed(CP &d, const CallArgs &ca, const TD &t) {
 
 // Softmax router top-k: k rounds of (max, lowest index) over the logits not
 // yet taken; weights = softmax over the chosen logits; ids ascending.
-DEV void run_topk(Smem &sm, CP &d, const TD &t) {
-  const int l = t.layer, b = t.a0, E = d.E, K = d.topk;
-  const int tid = tidx(), lane = tid & 63, wave = tid >> 6;
-  const float *r = d.rl + ((size_t)l * d.B + b) * E;
-  float *vals = sm.xs;
-  int *taken = (int *)(sm.xs + kThreads);
-  int *ids = sm.imisc + 8;            // [16]
-  float *lg = sm.misc + 32;           // [16]
-  for (int i = tid; i < E; i += kThreads) { vals[i] = lda(r + i); taken[i] = 0; }
-  __syncthreads();
-  for (int j = 0; j < K; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int i = tid; i < E; i += kThreads)
-      if (!taken[i] && better(vals[i], i, bv, bi)) { bv = vals[i]; bi = i; }
-    wave_argmax(bv, bi);
-    if (lane == 0) { sm.misc[wave] = bv; sm.imisc[32 + wave] = bi; }
-    __syncthreads();
-    if (tid == 0) {
-      float cv = sm.misc[0];
-      int ci = sm.imisc[32];
-      for (int w2 = 1; w2 < kWaves; ++w2)
-        if (better(sm.misc[w2], sm.imisc[32 + w2], cv, ci)) { cv = sm.misc[w2]; ci = sm.imisc[32 + w2]; }
-      if (ci < 0 || ci >= E) ci = 0;  // all NaN: keep indices valid
-      ids[j] = ci;
-      lg[j] = vals[ci];
-      taken[ci] = 1;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    for (int a = 1; a < K; ++a)  // insertion sort by expert id
-      for (int c = a; c > 0 && ids[c - 1] > ids[c]; --c) {
-        const int ti = ids[c]; ids[c] = ids[c - 1]; ids[c - 1] = ti;
-        const float tv = lg[c]; lg[c] = lg[c - 1]; lg[c - 1] = tv;
-      }
-    float mx = lg[0];
-    for (int j = 1; j < K; ++j) mx = fmaxf(mx, lg[j]);
-    float wsum = 0.f;
-    for (int j = 0; j < K; ++j) { sm.misc[48 + j] = expf(lg[j] - mx); wsum += sm.misc[48 + j]; }
-    const size_t o = ((size_t)l * d.B + b) * K;
-    for (int j = 0; j < K; ++j) {
-      stai(d.tk_ids + o + j, ids[j]);
-      sta(d.tk_w + o + j, sm.misc[48 + j] / wsum);
-    }
-  }
-}
-
-DEV void run_combine(CP &d, const CallArgs &ca, const TD &t) {
-  const int l = t.layer, b = t.a0, H = d.H, K = d.topk, B = d.B;
-  const bool active = ldg(ca.positions + b) >= 0;
-  const size_t xo = ((size_t)l * B + b) * H;
-  const float *w = d.tk_w + ((size_t)l * B + b) * K;
-  const float *y = d.ye + ((size_t)l * B + b) * K * H;
-  const int r0 = t.a1, r1 = t.a1 + t.a2;
-  for (int i = r0 + tidx(); i < r1; i += kThreads) {
-    float acc = 0.f;
-    for (int j = 0; j < K; ++j) acc = fmaf(lda(w + j), lda(y + (size_t)j * H + i), acc);
-    sta(d.x + xo + (size_t)B * H + i, active ? lda(d.xmid + xo + i) + acc : 0.f);
-  }
-}
-
 DEV void run_argmax(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
   const int b = t.a0, nt = d.n_lm_tiles;
   const int tid = tidx(), lane = tid & 63, wave = tid >> 6;
@@ -1218,8 +1479,9 @@ DEV void run_argmax(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
 // stores, then thread 0 reports).
 DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent, WState &ws) {
   if (t.op == OP_ATTN) {  // waits for its inputs itself, after a prefetch
-    const bool ok = d.hd == 128 ? run_attn<128>(sm, d, ca, t, persistent, ws)
-                                : run_attn<64>(sm, d, ca, t, persistent, ws);
+    const bool ok = d.hd == 128 ? (d.G <= 4 ? run_attn<128, 4>(sm, d, ca, t, persistent, ws)
+                                            : run_attn<128, 8>(sm, d, ca, t, persistent, ws))
+                                : run_attn<64, 8>(sm, d, ca, t, persistent, ws);
     if (!ok) return false;
   } else {
     if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
@@ -1227,8 +1489,6 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
   }
   switch (t.op) {
     case OP_EMBED: run_embed(d, ca, t); break;
-    case OP_TOPK: run_topk(sm, d, t); break;
-    case OP_COMBINE: run_combine(d, ca, t); break;
     case OP_ARGMAX: run_argmax(sm, d, ca, t); break;
     default: break;
   }
@@ -1271,7 +1531,12 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
 // when the step is drained after an error.  Uniform across waves.
 // One task of the kernel-per-op executor (all waves of one workgroup).
 DEV void run_task_once(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws) {
-  if (!is_gemv(t.op)) {
+  if (t.op == OP_EDOWN) {
+    if (uni(tidx() >> 6) == 0)
+      down_ctl(sm, d, ca, t, false, ws);
+    else
+      down_cmp(sm, d, ca, t, false, ws);
+  } else if (!is_gemv(t.op)) {
     run_small(sm, d, ca, t, false, ws);
   } else if (uni(tidx() >> 6) == 0) {
     gemv_ctl<false>(sm, d, ca, t, false, ws);
@@ -1326,8 +1591,9 @@ __global__ void __launch_bounds__(kThreads)
   if (wave == 0) {
     for (int k = beg; k < end; ++k) {
       const TD t = td_from_ring(sm.ring[(k - beg) % kRing]);
-      const bool alive = is_gemv(t.op) ? gemv_ctl<B1>(sm, d, ca, t, true, ws)
-                                       : run_small(sm, d, ca, t, true, ws);
+      const bool alive = t.op == OP_EDOWN ? down_ctl(sm, d, ca, t, true, ws)
+                         : is_gemv(t.op)  ? gemv_ctl<B1>(sm, d, ca, t, true, ws)
+                                          : run_small(sm, d, ca, t, true, ws);
       if (!alive) return;
     }
     return;
@@ -1360,7 +1626,9 @@ __global__ void __launch_bounds__(kThreads)
       }
     } else {
       bool alive;
-      if (is_gemv(t.op)) {
+      if (t.op == OP_EDOWN) {
+        alive = down_cmp(sm, d, ca, t, true, ws);
+      } else if (is_gemv(t.op)) {
         Buf w;
         Geo gn;
         alive = gemv_cmp<B1>(sm, d, ca, t, true, ws, w, false, false, gn);

@@ -50,10 +50,12 @@ enum Op : int16_t {
 //   GATEUP  a1=row0 a2=rows per matrix (gate rows then the same up rows)
 //   (static-weight GEMVs: rpp = rows per pass; the task streams a2 rows as
 //   ceil(a2 / rpp) passes of rpp rows, the last one shorter)
-//   TOPK    a0=slot
-//   EGATEUP a0=slot a1=row0 a2=rows per matrix a3=expert slot
-//   EDOWN   a0=slot a1=row0 a2=rows a3=expert slot
-//   COMBINE a0=slot a1=row0 a2=rows
+//   EGATEUP a0=slot a1=row0 a2=rows per matrix a3=expert slot (the j-th
+//           smallest routed expert id); rpp as for static weights
+//   EDOWN   a0=slot a1=row0 a2=rows of every routed expert (the task's tile
+//           is top_k segments, one per expert, each whole 1 KiB chunks)
+//   (TOPK, COMBINE: no longer emitted; routing runs inside EGATEUP, the
+//   combine inside EDOWN)
 //   LMHEAD  a1=row0 a2=rows a4=LM-head task index (argmax partial)
 //   ARGMAX  a0=slot
 // a5 (every op): how many completions this task reports to its events.  A
@@ -62,8 +64,8 @@ enum Op : int16_t {
 // others carry a5 = 0.
 // The second half is resolved by the C ABI once the plan's buffers exist, so
 // a task needs one scalar load and no chain of dependent table lookups:
-//   w0, w1  first weight row of the tile in segment 0 / 1 (experts: null,
-//           the expert is chosen at run time)
+//   w0, w1  first weight row of the tile in segment 0 / 1 (experts: the
+//           layer's expert 0, the expert is chosen at run time)
 //   src     activation input of slot 0 (slots are K apart)
 //   dst     output of slot 0 at the tile's first row (slots `ostride` apart)
 //   aux     residual input, indexed like dst (null when unused)
@@ -106,12 +108,16 @@ struct DevPlan {
   const uint16_t *const *w_gate, *const *w_up, *const *w_down;
   const uint16_t *const *router;                        // [L]
   const uint16_t *const *e_gate, *const *e_up, *const *e_down;  // [L*E]
+  // elements between consecutive experts of a layer when every expert table
+  // is evenly strided (expert e = expert 0 + e * e_stride), else 0 (the
+  // tables are read)
+  int64_t e_stride;
   // KV cache
   uint16_t *k_pool, *v_pool;
   const int32_t *page_table;
   // scratch (fp32 unless noted); layouts in planner.cpp
   float *x, *xmid, *q, *k, *v, *part, *attn, *h;
-  float *rl, *tk_w, *he, *ye, *amax_v;
+  float *rl, *tk_w, *he, *amax_v;
   int32_t *tk_ids, *amax_i;
   const float *rope_cos, *rope_sin;                     // [max_pos][hd/2]
   // control

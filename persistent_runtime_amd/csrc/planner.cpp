@@ -78,6 +78,8 @@ int check_config(const mk_config &c, std::string &err) {
       return bad("top_k must be in [1, min(n_experts, 16)]");
     if (c.n_experts > 512) return bad("at most 512 experts");
     if (c.expert_ffn_dim < 1) return bad("MoE model needs expert_ffn_dim > 0");
+    if ((long)c.top_k * c.expert_ffn_dim * 4 > kLdsXBytes)
+      return bad("top_k * expert_ffn_dim fp32 values must fit the LDS activation stage");
   }
   const int Ks[4] = {c.hidden, c.n_q_heads * c.head_dim,
                      c.n_experts ? c.expert_ffn_dim : c.ffn_dim, 0};
@@ -143,9 +145,10 @@ struct Builder {
 // One contiguous row range of one weight matrix (or of the gate/up pair)
 // inside a GEMV operation, with what its tasks carry and signal.
 struct RowSeg {
-  int a0;     // QKV: matrix (0 q, 1 k, 2 v); else 0
+  int a0;     // QKV: matrix (0 q, 1 k, 2 v); expert GEMVs: slot; else 0
   int row0, rows;
   int sig;    // event the segment's tasks signal
+  int a3 = 0; // expert gate/up: expert slot
 };
 
 // Lower a static-weight GEMV operation: its rows (all of nseg * K bf16) are
@@ -153,13 +156,15 @@ struct RowSeg {
 // bytes, as every row has the same length); a share becomes one task per
 // segment piece, streamed in passes of at most one register tile, at most
 // pmax passes per task.  With several segments the shares follow segment
-// boundaries instead (see below).  Returns the number of tasks added, or -1 when a
-// row does not fit one register tile.
+// boundaries instead (see below).  Row counts are multiples of `min_unit`.
+// Returns the number of tasks added, or -1 when a row does not fit one
+// register tile.
 int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int K, int nseg,
-             int n_workers, int pmax, int wait_ev, int64_t extra_bytes, int *lm_index) {
+             int n_workers, int pmax, int wait_ev, int64_t extra_bytes, int *lm_index,
+             int min_unit = 1) {
   const int64_t row_bytes = (int64_t)nseg * K * 2;
   int unit = 1;
-  while ((row_bytes * unit) % 1024) ++unit;
+  while ((row_bytes * unit) % 1024 || unit % min_unit) ++unit;
   int R = (int)((int64_t)kMaxTileUnits16 * 1024 / row_bytes);
   R -= R % unit;
   if (R < unit) return -1;
@@ -205,7 +210,7 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
           const int P = (int)((n + R - 1) / R);
           int rpp = (int)((n + P - 1) / P);
           rpp += (unit - rpp % unit) % unit;
-          b.add(op, layer, sg.a0, (int)(sg.row0 + lo), (int)n, 0, 0, {wait_ev}, {sg.sig},
+          b.add(op, layer, sg.a0, (int)(sg.row0 + lo), (int)n, sg.a3, 0, {wait_ev}, {sg.sig},
                 n * row_bytes + extra_bytes, w, rpp);
           ++added;
           lo += n;
@@ -232,7 +237,7 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
       rpp += (unit - rpp % unit) % unit;
       const int row0 = (int)(sg.row0 + (lo - seg_base));
       const int a4 = lm_index ? (*lm_index)++ : 0;
-      b.add(op, layer, sg.a0, row0, (int)n, 0, a4, {wait_ev}, {sg.sig},
+      b.add(op, layer, sg.a0, row0, (int)n, sg.a3, a4, {wait_ev}, {sg.sig},
             n * row_bytes + extra_bytes, w, rpp);
       ++added;
       lo += n;
@@ -265,25 +270,7 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   p.S = std::max(1, std::min(std::min(want, by_len), 64));
   if (o.attn_splits > 0) p.S = std::min(o.attn_splits, 128);  // merge keeps G*S pairs in LDS
 
-  // Expert tiles (weights chosen at run time) keep one register tile per
-  // task; the static-weight operations are cut per worker below.
   bool ok = true;
-  if (moe) {
-    const int Fe = c.expert_ffn_dim;
-    ok = ok && choose_tile((long)Fe * c.top_k * B, H, 2, n_cus, 0, p.egateup) &&
-         choose_tile((long)H * c.top_k * B, Fe, 1, n_cus, 0, p.edown);
-    // expert tiles must not straddle experts: round rows to divisors that
-    // keep whole 1 KiB chunks
-    auto fit = [&](GemvShape &s, int rows, int K, int nseg) {
-      int r = std::min(s.rows_per_tile, rows);
-      while (r > 1 && (rows % r || ((long)nseg * r * K) % 512)) --r;
-      s.rows_per_tile = r;
-      s.tiles = rows / r;
-      return rows % r == 0 && ((long)nseg * r * K) % 512 == 0;
-    };
-    if (ok) ok = fit(p.egateup, Fe, H, 2) && fit(p.edown, H, Fe, 1);
-  }
-  if (!ok) { err = "no tile shape fits the row lengths"; return MK_ERR_UNSUPPORTED; }
   // passes per task: slots x passes share the LDS partial buffers; when the
   // slots of a step do not fit one activation stage the weights of a pass
   // are reused across slot chunks, so such tasks keep a single pass
@@ -305,7 +292,6 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     p.n_rl = (int64_t)L * B * c.n_experts;
     p.n_tk = (int64_t)L * B * c.top_k;
     p.n_he = (int64_t)L * B * c.top_k * c.expert_ffn_dim;
-    p.n_ye = (int64_t)L * B * c.top_k * H;
   }
 
   Builder b(p);
@@ -359,43 +345,36 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
                    pmax_for(c.ffn_dim), hev, 0, nullptr) < 0)
         ok = false;
     } else {
+      // MoE: router logits; every expert gate/up task selects the top-k
+      // itself from them (no separate routing task); the down projection of
+      // a row range covers all k experts and adds their weighted sum to the
+      // residual (no separate combine task).
       const int E = c.n_experts, K = c.top_k, Fe = c.expert_ffn_dim;
       int rlev = b.ev();
       b.begin_phase();
       if (add_gemv(b, OP_ROUTER, l, {{0, 0, E, rlev}}, H, 1, n_workers, pmax_for(H), xo, 0,
                    nullptr) < 0)
         ok = false;
-      std::vector<int> tk(B);
+      int eh = b.ev();
       b.begin_phase();
-      for (int s = 0; s < B; ++s) {
-        tk[s] = b.ev();
-        b.add(OP_TOPK, l, s, 0, 0, 0, 0, {rlev}, {tk[s]}, 0);
-      }
-      std::vector<int> eh(B * K), ey(B);
-      b.begin_phase();
-      const int re = p.egateup.rows_per_tile;
-      for (int s = 0; s < B; ++s)
-        for (int j = 0; j < K; ++j) {
-          eh[s * K + j] = b.ev();
-          for (int r = 0; r < Fe; r += re)
-            b.add(OP_EGATEUP, l, s, r, re, j, 0, {tk[s]}, {eh[s * K + j]},
-                  (int64_t)2 * re * H * 2);
-        }
-      b.begin_phase();
-      const int rdn = p.edown.rows_per_tile;
-      for (int s = 0; s < B; ++s) {
-        ey[s] = b.ev();
-        for (int j = 0; j < K; ++j)
-          for (int r = 0; r < H; r += rdn)
-            b.add(OP_EDOWN, l, s, r, rdn, j, 0, {eh[s * K + j]}, {ey[s]},
-                  (int64_t)rdn * Fe * 2);
+      {
+        std::vector<RowSeg> segs;
+        for (int s = 0; s < B; ++s)
+          for (int j = 0; j < K; ++j) segs.push_back({s, 0, Fe, eh, j});
+        if (add_gemv(b, OP_EGATEUP, l, segs, H, 2, n_workers, pmax_for(H), rlev, 0, nullptr) < 0)
+          ok = false;
       }
       b.begin_phase();
-      const int rc2 = std::max(256, H / 8);
-      for (int s = 0; s < B; ++s)
-        for (int r = 0; r < H; r += rc2)
-          b.add(OP_COMBINE, l, s, r, std::min(rc2, H - r), 0, 0, {ey[s]},
-                {x_ev[l + 1]}, 0);
+      {
+        // k segments per task (one per expert), each a whole number of 1 KiB
+        // chunks: rows * Fe * 2 bytes divisible by 1024
+        int unit = 1;
+        while (((int64_t)unit * Fe * 2) % 1024) ++unit;
+        std::vector<RowSeg> segs;
+        for (int s = 0; s < B; ++s) segs.push_back({s, 0, H, x_ev[l + 1]});
+        if (add_gemv(b, OP_EDOWN, l, segs, Fe, K, n_workers, 1, eh, 0, nullptr, unit) < 0)
+          ok = false;
+      }
     }
   }
   // final norm + LM head (+ per-tile argmax partials), then argmax

@@ -35,8 +35,7 @@ struct HostPlan {
   std::vector<int32_t> worker_list; // task indices per worker, in list order
   // scratch sizes in elements
   int64_t n_x = 0, n_xmid = 0, n_q = 0, n_k = 0, n_part = 0, n_attn = 0,
-          n_h = 0, n_rl = 0, n_tk = 0, n_he = 0, n_ye = 0, n_amax = 0;
-  GemvShape egateup{}, edown{};     // expert tiles (one register tile each)
+          n_h = 0, n_rl = 0, n_tk = 0, n_he = 0, n_amax = 0;
 };
 
 // Vector width (bytes per lane load) for rows of K bf16 elements, or 0 when

@@ -58,11 +58,13 @@ def _check_graph(model, tasks, thr, B):
     cover = {}
     for t in tasks:
         op = mk.OPS[t.op]
-        if op in ("QKV", "OPROJ", "GATEUP", "DOWN", "ROUTER", "LMHEAD"):
-            key = (op, t.layer, t.a0 if op == "QKV" else 0)
-            cover.setdefault(key, []).append((t.a1, t.a1 + t.a2))
+        if op in ("QKV", "OPROJ", "GATEUP", "DOWN", "ROUTER", "LMHEAD", "EGATEUP", "EDOWN"):
+            m = (t.a0 if op == "QKV" else (t.a0, t.a3) if op == "EGATEUP"
+                 else t.a0 if op == "EDOWN" else 0)
+            cover.setdefault((op, t.layer, m), []).append((t.a1, t.a1 + t.a2))
     want = {"OPROJ": H, "LMHEAD": model["vocab"], "DOWN": H,
-            "GATEUP": model["ffn_dim"], "ROUTER": model["n_experts"]}
+            "GATEUP": model["ffn_dim"], "ROUTER": model["n_experts"],
+            "EGATEUP": model["expert_ffn_dim"], "EDOWN": H}
     for (op, l, m), rr in cover.items():
         rr.sort()
         n = (nq * hd if m == 0 else nkv * hd) if op == "QKV" else want[op]
@@ -120,21 +122,19 @@ def _regions(model, t, B, S):
         for b in allb:
             R.append(("xmid", l, b, 0, 0, H))
             W.append(("rl", l, b, 0, t.a1, t.a1 + t.a2))
-    elif op == "TOPK":
-        R.append(("rl", l, t.a0, 0, 0, E))
-        W.append(("tk", l, t.a0, 0, 0, K))
     elif op == "EGATEUP":
+        # routes the slot itself from the router logits; the slot's first
+        # task also publishes the routing (ids and weights)
         b, j = t.a0, t.a3
-        R += [("tk", l, b, 0, 0, K), ("xmid", l, b, 0, 0, H)]
+        R += [("rl", l, b, 0, 0, E), ("xmid", l, b, 0, 0, H)]
         W.append(("he", l, b, j, t.a1, t.a1 + t.a2))
+        if t.a1 == 0 and j == 0:
+            W.append(("tk", l, b, 0, 0, K))
     elif op == "EDOWN":
-        b, j = t.a0, t.a3
-        R += [("tk", l, b, 0, 0, K), ("he", l, b, j, 0, Fe)]
-        W.append(("ye", l, b, j, t.a1, t.a1 + t.a2))
-    elif op == "COMBINE":
+        # rows a1..a1+a2 of every routed expert, weighted sum + residual
         b = t.a0
         R += [("tk", l, b, 0, 0, K), ("xmid", l, b, 0, t.a1, t.a1 + t.a2)]
-        R += [("ye", l, b, j, t.a1, t.a1 + t.a2) for j in range(K)]
+        R += [("he", l, b, j, 0, Fe) for j in range(K)]
         W.append(("x", l + 1, b, 0, t.a1, t.a1 + t.a2))
     elif op == "LMHEAD":
         for b in allb:
