@@ -134,12 +134,126 @@ def timed_steps(plan, tok_ring, pos_all, first, n, stream, torch):
     return launch_ms, ev[0].elapsed_time(ev[n]) / 1e3, wall
 
 
+def run_ragged(args, torch):
+    """Continuous batching on the 8B shape: B slots, each holding a sequence
+    with a synthetic cached context uniform in [128, 16384]; every step each
+    sequence retires with probability 1/32 and a new one (fresh context and
+    KV) joins its slot.  Only the decode launches are timed (HIP events on
+    the launch stream around each step); page-table edits and the joining
+    sequences' KV writes happen between them.  Prints one JSON line per
+    batch size."""
+    import synth
+    from persistent_runtime_amd import mk, sol
+    from persistent_runtime_amd.kvcache import PagedKV
+
+    dev = torch.device("cuda:0")
+    model = synth.MODELS["llama8b"]
+    Wd = synth.make_weights(model, device=dev)
+    stream = torch.cuda.current_stream()
+    batches = [int(b) for b in args.batches.split(",")]
+    W_, K_ = args.warmup, args.steps if args.steps is not None else 128
+    for B in batches:
+        n = W_ + K_
+        sched = synth.ragged_schedule(B, n)
+        ctx_hi = 16384
+        maxp = (ctx_hi + n + 1 + 15) // 16
+        in_use = max(sum((p + 1 + 15) // 16 for p in sched["pos"][k]) for k in range(n))
+        kv = PagedKV(model, max_batch=B, max_pages_per_seq=maxp, n_pages=in_use + B, device=dev)
+        t0 = time.time()
+        for b in range(B):
+            K, V = synth.make_kv_values(model, sched["ctx0"][b], stream_id=sched["sid0"][b],
+                                        device=dev)
+            kv.write_tokens(b, K, V)
+            del K, V
+        torch.cuda.synchronize()
+        log(f"[bench] ragged B={B}: {sum(sched['ctx0'])} cached tokens in {kv.n_pages} pages "
+            f"({time.time() - t0:.1f}s)")
+        opts = {} if args.attn_splits is None else {"attn_splits": args.attn_splits}
+
+        def run(plan, k0, k1, timed):
+            tok = torch.as_tensor(synth.make_prompt(B, model["vocab"], seed=7 + k0),
+                                  dtype=torch.int32).to(dev)
+            nxt = torch.zeros(B, dtype=torch.int32, device=dev)
+            ms, nbytes = [], []
+            for k in range(k0, k1):
+                for (b, c, sid) in sched["joins"][k]:  # retire first, then join
+                    kv.release(b, upload=False)
+                for (b, c, sid) in sched["joins"][k]:
+                    K, V = synth.make_kv_values(model, c, stream_id=sid, device=dev)
+                    kv.write_tokens(b, K, V)
+                    del K, V
+                    tok[b] = int(synth.make_prompt(1, model["vocab"], seed=1000 + sid)[0])
+                pos = sched["pos"][k]
+                added = False
+                for b in range(B):
+                    added |= kv.assign(b, pos[b] + 1, upload=False)
+                if added or sched["joins"][k]:
+                    kv.upload()
+                pos_d = torch.as_tensor(pos, dtype=torch.int32).to(dev)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                plan.decode_step(tok, pos_d, nxt)
+                e1.record(stream)
+                tok, nxt = nxt, tok
+                if timed:
+                    ms.append((e0, e1))
+                    nbytes.append(sol.step_bytes(model, [p + 1 for p in pos]))
+            plan.check()
+            torch.cuda.synchronize()
+            return [a.elapsed_time(b) for a, b in ms], nbytes
+
+        plan = mk.Plan(model, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=B,
+                       opts=mk.default_options(planned_ctx=ctx_hi, **opts))
+        info = plan.info()
+        run(plan, 0, W_, False)
+        kk = K_ if args.no_kpo else K_ // 2
+        ms, nbytes = run(plan, W_, W_ + kk, True)
+        plan.free()
+        t_ms = sum(ms)
+        tok_s = B * kk / (t_ms / 1e3)
+        achieved = sum(nbytes) / (t_ms / 1e3) / 1e9
+        kpo = None
+        if not args.no_kpo:
+            plan_k = mk.Plan(model, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=B,
+                             opts=mk.default_options(planned_ctx=ctx_hi,
+                                                     executor=mk.MK_EXEC_KERNEL_PER_OP, **opts))
+            ms_k, _ = run(plan_k, W_ + kk, n, True)
+            kpo = {"ms_per_step": round(sum(ms_k) / len(ms_k), 4),
+                   "launches_per_step": plan_k.info()["n_phases"]}
+            plan_k.free()
+            kpo["persistent_speedup"] = round(kpo["ms_per_step"] / (t_ms / kk), 3)
+        log(f"[bench] ragged B={B}: {t_ms / kk:.3f} ms/step, {tok_s:.1f} tok/s, "
+            f"{achieved:.0f} GB/s" + (f"; kernel-per-op {kpo['ms_per_step']:.3f} ms/step" if kpo else ""))
+        out = {
+            "metric": "decode tokens/s, continuous batching", "value": round(tok_s, 2),
+            "unit": "tokens/s", "n_gpus": 1, "steps": kk, "warmup": W_,
+            "ms_per_step": round(t_ms / kk, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"llama8b ragged decode, batch {B}, contexts U[128,16384], "
+                                   f"16-token shuffled pages, retire/join p=1/32 per step",
+                       "batch": B, "attn_splits": args.attn_splits,
+                       "tasks_per_step": info["n_tasks"]},
+            "sol_fraction": round(achieved / 8000.0, 4),
+            "bytes_per_step": int(sum(nbytes) / kk),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0,
+                         "unit": "GB/s", "frac": round(achieved / 8000.0, 4), "traffic": None,
+                         "kernel": "mk_persistent_kernel"},
+            "kernel_per_op": kpo,
+        }
+        print(json.dumps(out), flush=True)
+        del kv
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOADS) + ["ragged"])
+    ap.add_argument("--batches", default="4,16,64", help="ragged: batch sizes")
+    ap.add_argument("--attn-splits", type=int, default=None, help="ragged: KV splits per sequence")
     ap.add_argument("--kpo-steps", type=int, default=64, help="kernel-per-op comparison steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kpo", action="store_true")
@@ -168,6 +282,9 @@ def main():
         print(json.dumps({"calib_copy_bytes": a.numel() * 4, "launches": 4}))
         return
 
+    if args.workload == "ragged":
+        run_ragged(args, torch)
+        return
     mname, ctx_kind, ctx0 = WORKLOADS[args.workload]
     model = synth.MODELS[mname]
     default_steps = {"moe30b": 248, "longctx": 56, "llama70b": 120}.get(args.workload, 504)

@@ -31,23 +31,36 @@ class PagedKV:
         self.page_table = self.table_host.to(device)
         self.device = device
 
-    def assign(self, slot: int, n_tokens: int):
-        """Give slot enough pages for n_tokens positions (keeps existing ones)."""
+    def assign(self, slot: int, n_tokens: int, upload: bool = True) -> bool:
+        """Give slot enough pages for n_tokens positions (keeps existing ones).
+        Returns whether a page was added; `upload=False` leaves the device
+        copy of the table to a later `upload()`."""
         need = (n_tokens + PAGE - 1) // PAGE
         if need > self.maxp:
             raise ValueError("sequence longer than max_pages_per_seq * 16")
         row = self.table_host[slot]
+        added = False
         for j in range(need):
             if int(row[j]) < 0:
+                if not self.free_pages:
+                    raise RuntimeError("page pool exhausted")
                 row[j] = self.free_pages.pop()
-        self.page_table.copy_(self.table_host)
+                added = True
+        if upload and added:
+            self.upload()
+        return added
 
-    def release(self, slot: int):
+    def release(self, slot: int, upload: bool = True):
+        """Return the slot's pages to the pool (the slot retires)."""
         row = self.table_host[slot]
         for j in range(self.maxp):
             if int(row[j]) >= 0:
                 self.free_pages.append(int(row[j]))
                 row[j] = -1
+        if upload:
+            self.upload()
+
+    def upload(self):
         self.page_table.copy_(self.table_host)
 
     def write_tokens(self, slot: int, K, V, start: int = 0):

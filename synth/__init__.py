@@ -20,7 +20,7 @@ from .configs import (MODELS, WORKLOADS, PAGE_SIZE, WEIGHT_SEED, PROMPT_SEED,
 __all__ = ["MODELS", "WORKLOADS", "PAGE_SIZE", "WEIGHT_SEED", "PROMPT_SEED",
            "KV_SEED", "truncated", "make_weights", "make_prompt",
            "make_kv_values", "weight_shapes", "tensor_seed", "bf16_to_f32_np",
-           "to_numpy_bf16"]
+           "to_numpy_bf16", "ragged_schedule"]
 
 # kind index -> name; the index enters the per-tensor seed
 _KINDS = ["embed", "lm_head", "wq", "wk", "wv", "wo", "w_gate", "w_up",
@@ -126,3 +126,41 @@ def bf16_to_f32_np(a):
     """numpy uint16 bf16 bit patterns -> float32 with identical values."""
     import numpy as np
     return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def ragged_schedule(B: int, steps: int, ctx_lo: int = 128, ctx_hi: int = 16384,
+                    retire_p: float = 1.0 / 32.0, seed: int = KV_SEED) -> dict:
+    """Seeded continuous-batching schedule for B slots over `steps` steps.
+
+    Every slot starts with a sequence whose cached context is uniform in
+    [ctx_lo, ctx_hi] (inclusive).  Before each step after the first, every
+    slot's sequence retires with probability retire_p and a new sequence with
+    a fresh uniform context joins the same slot.  Each sequence has its own
+    stream id (its synthetic KV draws: `make_kv_values(..., stream_id=sid)`).
+
+    Returns {"ctx0": [B] initial contexts, "sid0": [B] stream ids,
+    "joins": [steps] lists of (slot, context, stream id), "pos": [steps][B]
+    the position each slot feeds at each step (its cached length)}.
+    """
+    g = torch.Generator()
+    g.manual_seed((int(seed) << 20) + 0x5A17 + int(B))
+    def draw_ctx():
+        return int(torch.randint(ctx_lo, ctx_hi + 1, (1,), generator=g))
+    ctx = [draw_ctx() for _ in range(B)]
+    sid = list(range(B))
+    nxt = B
+    out = {"ctx0": list(ctx), "sid0": list(sid), "joins": [], "pos": []}
+    for k in range(steps):
+        joins = []
+        if k > 0:
+            u = torch.rand(B, generator=g)
+            for b in range(B):
+                if float(u[b]) < retire_p:
+                    ctx[b] = draw_ctx()
+                    sid[b] = nxt
+                    nxt += 1
+                    joins.append((b, ctx[b], sid[b]))
+        out["joins"].append(joins)
+        out["pos"].append(list(ctx))
+        ctx = [c + 1 for c in ctx]
+    return out
