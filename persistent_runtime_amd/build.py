@@ -21,6 +21,10 @@ def command(out=LIB, extra=()):
     return [HIPCC, "-std=c++17", "-O3", "-fPIC", "-shared", f"--offload-arch={ARCH}",
             # keep the compiler from emitting packed fp32 VALU instructions
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # multiply-adds fused only where one source expression asks for it,
+            # so every executor (differently inlined copies of the same tile
+            # code) rounds identically
+            "-ffp-contract=on",
             "-Wno-unused-command-line-argument",
             "-I", os.path.join(ROOT, "include"),
             *[os.path.join(CSRC, s) for s in SOURCES], "-o", out, *extra]

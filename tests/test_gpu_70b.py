@@ -1,0 +1,49 @@
+"""Parity of the Llama-70B shape (hidden 8192, 64 q / 8 KV heads, FFN 28672,
+vocab 128256) at its real per-layer sizes, depth-truncated to 4 layers with
+the full LM head so the CPU oracle stays within seconds per step; the device
+runs it in the benchmark's launch configuration (persistent executor, one
+workgroup per CU).  Prefill of the 39-token prompt, then three
+teacher-forced decode steps.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from synth.configs import LLAMA70B
+from tests.gpu_common import LOGIT_TOL, MARGIN, Runner, oracle_weights
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+@pytest.mark.timeout(900)
+def test_llama70b_shapes_truncated_teacher_forced():
+    cfg = synth.truncated(LLAMA70B, 4)
+    print("70B/4: generating weights", flush=True)
+    Wd = synth.make_weights(cfg, device="cuda")
+    total = 39 + 512
+    r = Runner(cfg, Wd, B=1, maxp=(total + 15) // 16, planned_ctx=total)
+    prompt = synth.make_prompt(39, cfg["vocab"]).tolist()
+    g_tok, g_lg = r.prefill(0, prompt)
+    print("70B/4: device prefill done; oracle full forward", flush=True)
+    Wt = oracle_weights(Wd, cfg)
+    logits, cache = O.forward_full(Wt, cfg, prompt, return_cache=True)
+    ref = logits[-1]
+    worst = float(np.max(np.abs(g_lg - ref)))
+    ids = [(g_tok, O.greedy_argmax(ref), O.top2_margin(ref))]
+    for i in range(3):
+        t = O.greedy_argmax(ref)
+        g_ids, lg = r.step([t], [39 + i])
+        ref = O.decode_step(Wt, cfg, cache, t, 39 + i)
+        worst = max(worst, float(np.max(np.abs(lg[0] - ref))))
+        ids.append((int(g_ids[0]), O.greedy_argmax(ref), O.top2_margin(ref)))
+        print(f"70B/4: step {i} max|dlogit| so far {worst:.3e}", flush=True)
+    assert worst <= LOGIT_TOL, worst
+    for g, o, m in ids:
+        if m > MARGIN:
+            assert g == o, (g, o, m)
+    r.plan.free()

@@ -195,6 +195,23 @@ def test_deterministic_bitwise(tiny):
     assert np.array_equal(out[0], out[1])
 
 
+def test_executors_bitwise_equal(tiny):
+    """The persistent and the kernel-per-op executors run the same tile code
+    and round identically: their logits agree bit for bit (batch 3, split
+    attention)."""
+    Wd, _ = tiny
+    out = []
+    for ex in (mk.MK_EXEC_PERSISTENT, mk.MK_EXEC_KERNEL_PER_OP):
+        r = Runner(TINY, Wd, B=3, maxp=8, attn_splits=3, executor=ex)
+        for b in range(3):
+            r.prefill(b, _prompt()[: 20 + 5 * b])
+        ids, lg = r.step([7, 8, 9], [20, 25, 30])
+        out.append((ids.copy(), lg.copy()))
+        r.plan.free()
+    assert np.array_equal(out[0][0], out[1][0])
+    assert np.array_equal(out[0][1], out[1][1])
+
+
 def test_tiny_moe_teacher_forced(tiny_moe):
     """MoE routing: ids equal the oracle's except at a top-k boundary closer
     than 1e-3, where the step is re-checked against the oracle forced to the
