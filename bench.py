@@ -246,6 +246,46 @@ def run_ragged(args, torch):
         torch.cuda.empty_cache()
 
 
+def kpo_graph_ms(build, start, tok_ring, pos_all, n, stream, torch):
+    """Kernel-per-op step captured in a HIP graph (counters cleared by a
+    kernel inside the step, so the graph replays): one replay feeds the
+    previous token and the next position, as the eager runs do.  Returns the
+    mean ms per replay over n - 2 replays after 2 warm-up replays."""
+    from persistent_runtime_amd import mk
+    plan = build(mk.MK_EXEC_KERNEL_PER_OP, graph_replay=1)
+    dev = tok_ring.device
+    ring = torch.zeros(2, dtype=torch.int32, device=dev)
+    start(plan, ring)
+    tok = ring[0:1].clone()
+    pos = pos_all[0:1].clone()
+    nxt = torch.zeros(1, dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # eager warm-up on the capture stream
+        plan.decode_step(tok, pos, nxt)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.decode_step(tok, pos, nxt)
+        tok.copy_(nxt)
+        pos.add_(1)
+    pos.copy_(pos_all[1:2])
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n - 2):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plan.check()
+    plan.free()
+    return e0.elapsed_time(e1) / (n - 2)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,9 +345,10 @@ def main():
         torch.cuda.empty_cache()
     pos_all = torch.arange(ctx0, ctx0 + W_ + K_ + 1, dtype=torch.int32, device=dev)
 
-    def build(executor):
+    def build(executor, graph_replay=0):
         return mk.Plan(model, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=1,
-                       opts=mk.default_options(executor=executor, planned_ctx=total))
+                       opts=mk.default_options(executor=executor, planned_ctx=total,
+                                               graph_replay=graph_replay))
 
     def start(plan, ring):
         """Context in place and the first token in ring[0]."""
@@ -356,6 +397,11 @@ def main():
                "same_tokens_first_steps": same}
         log(f"[bench] kernel-per-op: {kms:.3f} ms/step ({kpo['launches_per_step']} launches)")
         plan_k.free()
+        # the same launches captured once in a HIP graph and replayed
+        gms = kpo_graph_ms(build, start, tok_ring, pos_all, n, stream, torch)
+        kpo["graph_ms_per_step"] = round(gms, 4)
+        kpo["persistent_speedup_vs_graph"] = round(gms / ms_step, 3)
+        log(f"[bench] kernel-per-op in a HIP graph: {gms:.3f} ms/step")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -115,7 +115,11 @@ typedef struct {
   int32_t device;        /* HIP device ordinal; -1 = current device            */
   int64_t spin_budget;   /* dependency-wait budget in 100 MHz ticks; 0 = 1 s   */
   int32_t n_cus;         /* override the CU count used for tile sizing; 0 = query */
-  int32_t reserved[7];
+  int32_t graph_replay;  /* 1: every step first clears the plan's counters with a
+                            kernel and counts from zero, so a step captured in a
+                            HIP graph can be replayed; 0: counters stay
+                            monotonic across steps (no clearing launch)       */
+  int32_t reserved[6];
 } mk_plan_options;
 
 typedef struct mk_plan mk_plan;

@@ -64,6 +64,7 @@ struct mk_plan {
   std::vector<void *> allocs;
   uint32_t epoch = 0;
   uint32_t epoch_limit = 1;
+  bool graph_replay = false;
   int32_t *stage_tok = nullptr, *stage_pos = nullptr, *stage_next = nullptr;
   float *stage_logits = nullptr;
   uint32_t *ctrl = nullptr;  // CTRL_WORDS control words, the event counters, then
@@ -343,6 +344,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     std::unique_ptr<mk_plan> p(new mk_plan());
     p->device = dev;
     p->executor = o.executor;
+    p->graph_replay = o.graph_replay != 0;
     p->trace = o.debug_trace != 0;
     const int hw_cus = prop.multiProcessorCount;
     const int n_cus = o.n_cus > 0 ? o.n_cus : hw_cus;
@@ -490,6 +492,12 @@ static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positi
   ca.positions = positions;
   ca.next_tokens = next;
   ca.logits = logits;
+  if (plan->graph_replay) {
+    // a replayable step: counters from zero, no state carried on the host
+    HIP_TRY(launch_zero_u32(d.ev, (int)plan->hp.ev_thr.size() + plan->n_att_cnt, s),
+            "counter clear");
+    plan->epoch = 0;
+  }
   ca.epoch = plan->epoch;
   if (plan->executor == MK_EXEC_PERSISTENT) {
     if (plan->trace) {
@@ -504,7 +512,7 @@ static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positi
   }
   // counters are monotonic per step (both executors count split-attention
   // arrivals); reset them before they could wrap
-  if (++plan->epoch >= plan->epoch_limit) {
+  if (!plan->graph_replay && ++plan->epoch >= plan->epoch_limit) {
     HIP_TRY(launch_zero_u32(d.ev, (int)plan->hp.ev_thr.size() + plan->n_att_cnt, s),
             "counter reset");
     plan->epoch = 0;

@@ -69,7 +69,7 @@ class mk_plan_options(C.Structure):
                 ("attn_splits", C.c_int32), ("planned_ctx", C.c_int32),
                 ("debug_trace", C.c_int32), ("device", C.c_int32),
                 ("spin_budget", C.c_int64), ("n_cus", C.c_int32),
-                ("reserved", C.c_int32 * 7)]
+                ("graph_replay", C.c_int32), ("reserved", C.c_int32 * 6)]
 
 
 class mk_task_info(C.Structure):

@@ -212,6 +212,40 @@ def test_executors_bitwise_equal(tiny):
     assert np.array_equal(out[0][1], out[1][1])
 
 
+@pytest.mark.parametrize("executor", [mk.MK_EXEC_PERSISTENT, mk.MK_EXEC_KERNEL_PER_OP],
+                         ids=["persistent", "kernel_per_op"])
+def test_graph_replay_matches_eager(tiny, executor):
+    """A step captured in a HIP graph (graph_replay plans clear their counters
+    with a kernel each step) replays to the eager step's logits, bit for bit,
+    replay after replay, with eager work and synchronisations in between."""
+    Wd, _ = tiny
+    r = Runner(TINY, Wd, B=2, maxp=8, attn_splits=3, executor=executor, graph_replay=1)
+    r.prefill(0, _prompt()[:30])
+    r.prefill(1, _prompt()[:17])
+    r.tok.copy_(torch.tensor([5, 6], dtype=torch.int32))
+    r.pos.copy_(torch.tensor([30, 17], dtype=torch.int32))
+    r.plan.decode_step(r.tok, r.pos, r.nxt, r.logits)
+    r.plan.check()
+    eager = r.logits.cpu().numpy().copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        r.plan.decode_step(r.tok, r.pos, r.nxt, r.logits)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        r.plan.decode_step(r.tok, r.pos, r.nxt, r.logits)
+    for i in range(4):
+        r.logits.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        r.plan.check()
+        assert np.array_equal(r.logits.cpu().numpy(), eager), i
+        r.step([5, 6], [30, 17])  # eager work between replays
+    r.plan.free()
+
+
 def test_tiny_moe_teacher_forced(tiny_moe):
     """MoE routing: ids equal the oracle's except at a top-k boundary closer
     than 1e-3, where the step is re-checked against the oracle forced to the
