@@ -119,7 +119,11 @@ typedef struct {
                             kernel and counts from zero, so a step captured in a
                             HIP graph can be replayed; 0: counters stay
                             monotonic across steps (no clearing launch)       */
-  int32_t reserved[6];
+  int32_t batched_mfma;  /* static-weight GEMVs as bf16 matrix-core tiles for
+                            batches of 16..64 slots: 0 = auto (on when
+                            max_batch >= 16 and every row count is a multiple
+                            of 16), -1 = off (vector path)                   */
+  int32_t reserved[5];
 } mk_plan_options;
 
 typedef struct mk_plan mk_plan;

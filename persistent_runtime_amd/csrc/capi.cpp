@@ -419,6 +419,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.F = c.ffn_dim; d.V = c.vocab; d.E = c.n_experts; d.topk = c.top_k;
     d.Fe = c.expert_ffn_dim; d.B = B; d.maxp = c.max_pages_per_seq; d.npages = c.n_pages;
     d.S = hp.S; d.G = hp.G; d.max_pos = hp.max_pos; d.n_lm_tiles = hp.n_lm_tiles;
+    d.mfma = hp.mfma ? 1 : 0;
     d.eps = c.rms_eps;
     d.embed = (const uint16_t *)w->embed;
     d.lm_head = (const uint16_t *)w->lm_head;
@@ -504,7 +505,8 @@ static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positi
       HIP_TRY(launch_zero_u32(d.trace, (int)plan->hp.tasks.size() * 6, s), "trace reset");
       HIP_TRY(launch_zero_u32(plan->ctrl + CTRL_CLOCK, 1, s), "trace reset");
     }
-    HIP_TRY(launch_persistent(plan->d_dev, ca, plan->grid, plan->hp.cfg.max_batch, s),
+    const int mode = plan->hp.mfma ? 2 : (plan->hp.cfg.max_batch == 1 ? 1 : 0);
+    HIP_TRY(launch_persistent(plan->d_dev, ca, plan->grid, mode, s),
             "persistent launch");
   } else {
     for (auto &ph : plan->hp.phases)

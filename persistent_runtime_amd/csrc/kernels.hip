@@ -1068,6 +1068,361 @@ DEV bool down_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   return true;
 }
 
+// ------------------------------------------------- batched GEMV, matrix cores --
+// For 16..64 slots the static-weight GEMVs run on v_mfma_f32_16x16x32_bf16.
+// A task covers NGs 16-row groups of each of its nseg matrices (gate and up
+// share a task) and all K.  Compute wave cw owns row slot cw of each matrix
+// (and slot cw + 7 of a single matrix with more than 7 groups) and streams
+// its groups along K in slices of Ks columns, one slice per pass.  A 1 KiB
+// chunk is 16 rows x 32 columns, loaded as one 16-byte load per lane in the
+// instruction's A layout (lane l: row l%16, columns 8(l/16)..+8), so loads
+// feed the matrix cores without reshuffling.  The control wave stages each
+// slice of activations (all slots) into LDS in the B layout (lane l: slot
+// l%16 of a 16-slot tile, the same 8 columns), split into a bf16 value and
+// a bf16 remainder: two products per tile keep about 16 bits of the fp32
+// activation.  Slices are double-buffered, one barrier per pass.  With a
+// gain the staged values are x*g and the outputs are scaled by 1/rms of
+// their slot at the end; the sums of squares are accumulated while staging.
+// The accumulators (16 rows x 16 slots per tile) go to LDS after the last
+// pass and the control wave writes the outputs.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+struct MGeo {
+  const uint16_t *s0, *s1;
+  int K, NGs, nseg, Ks, nkb, P, B16;
+};
+DEV MGeo mgeo(const uint16_t *w0, const uint16_t *w1, int rows, int K, int B) {
+  MGeo g;
+  g.s0 = w0;
+  g.s1 = w1;
+  g.K = K;
+  g.NGs = rows >> 4;
+  g.nseg = w1 ? 2 : 1;
+  g.B16 = (B + 15) >> 4;
+  const int maxg = (g.nseg == 2 || g.NGs > kCW) ? 2 : 1;
+  int ks = (kMaxChunks / maxg) * 32;                       // register slots
+  ks = min(ks, kLdsXBytes / (2 * g.B16 * 16 * 4));         // two slices of hi+lo bf16
+  ks = min(ks, K);
+  g.Ks = ks;
+  g.nkb = ks >> 5;
+  g.P = (K + ks - 1) / ks;
+  return g;
+}
+DEV MGeo mgeo_of(CP &d, const TD &t) { return mgeo(t.w0, t.w1, t.a2, t.K, d.B); }
+
+// matrix and row slot of wave cw's gi-th group; false when it has none
+DEV bool mgroup(const MGeo &g, int cw, int gi, int &seg, int &slot) {
+  if (g.nseg == 2) {
+    seg = gi;
+    slot = cw;
+    return cw < g.NGs;
+  }
+  seg = 0;
+  slot = cw + gi * kCW;
+  return slot < g.NGs;
+}
+
+// Address of lane's 16 bytes of register slot j (group j / NKB, k-block
+// j % NKB) of wave cw in pass p; slots without a chunk read the first chunk.
+template <int NKB>
+DEV uint64_t maddr(const MGeo &g, int cw, int j, int p) {
+  const int lane = tidx() & 63;
+  const int gi = j / NKB, kb = j % NKB;
+  int seg = 0, slot = 0;
+  const int k = p * g.Ks + kb * 32;
+  const bool ok = gi < 2 && mgroup(g, cw, gi, seg, slot) && kb < g.nkb && k < g.K;
+  const uint16_t *base = ok && seg ? g.s1 : g.s0;
+  const int row = (ok ? slot * 16 : 0) + (lane & 15);
+  const int col = (ok ? k : 0) + 8 * (lane >> 4);
+  return (uint64_t)(base + (size_t)row * g.K + col);
+}
+DEV uint64_t maddr_any(const MGeo &g, int cw, int j, int p) {
+  return g.nkb >= 16 ? maddr<16>(g, cw, j, p) : maddr<8>(g, cw, j, p);
+}
+DEV void mload(const MGeo &g, Buf &w, int cw) {
+#pragma unroll
+  for (int j = 0; j < kMaxChunks; ++j) w[j] = ldnt((const u32x4 *)maddr_any(g, cw, j, 0));
+}
+
+// One pass of wave cw: the products of its chunks with the staged slice
+// `xb`; each register slot is refilled right after use with the same chunk
+// of the next pass, or (after the last pass) of the next task's first pass.
+template <int NKB>
+DEV void mpass(const MGeo &g, Buf &w, f32x4 (&acc)[2][4], const char *xb, int cw, int p,
+               bool pre, const MGeo &gn) {
+  const int lane = tidx() & 63;
+  const int B16 = g.B16;
+  const char *xlo = xb + g.nkb * B16 * 1024;
+  const bool last = p + 1 == g.P;
+#pragma unroll
+  for (int j = 0; j < kMaxChunks; ++j) {
+    const int gi = j / NKB, kb = j % NKB;
+    int seg, slot;
+    const bool ok = gi < 2 && mgroup(g, cw, gi, seg, slot) && kb < g.nkb &&
+                    p * g.Ks + kb * 32 < g.K;
+    if (ok) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, w[j]);
+      // value parts of every slot tile, then the remainders: consecutive
+      // products accumulate into different tiles
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const char *src = half ? xlo : xb;
+        bf16x8 xv[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          if (st < B16) xv[st] = *(const bf16x8 *)(src + ((kb * B16 + st) * 64 + lane) * 16);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          if (st < B16)
+            acc[gi][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xv[st], acc[gi][st], 0, 0, 0);
+      }
+    }
+    const uint64_t na = !last ? maddr<NKB>(g, cw, j, p + 1)
+                              : (pre ? maddr_any(gn, cw, j, 0) : maddr<NKB>(g, cw, kMaxChunks, 0));
+    w[j] = ldnt((const u32x4 *)na);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Staging of slice p of the activations (all slots) into LDS buffer pb, by
+// all eight waves: the slice's units (k-block kb, 16-slot tile st) are dealt
+// round-robin over the waves, at most four per wave.  A unit is 64 lanes x 8
+// columns of one slot (lane l: slot st*16 + l%16, columns 8(l/16)..+8 of the
+// k-block), times the gain, stored as bf16 value + bf16 remainder in the B
+// layout.  Every load is issued (out-of-range units read unit 0 and are not
+// stored), which keeps the compiler's waits per load instead of for the
+// whole queue.
+struct XStage {
+  f32x4 v[4][2];
+  u32x4 g[4];
+};
+DEV int mx_units(const MGeo &g, int p) { return (min(g.Ks, g.K - p * g.Ks) >> 5) * g.B16; }
+DEV void mx_load(CP &d, const MGeo &g, const TD &t, int p, XStage &xs) {
+  const int lane = tidx() & 63, wave = uni(tidx() >> 6);
+  const int nu = mx_units(g, p), B = d.B;
+  const __amdgpu_buffer_rsrc_t r = rsrc(t.src);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int u = wave + kWaves * q;
+    u = u < nu ? u : 0;
+    const int kb = u / g.B16, st = u - kb * g.B16;
+    const int col = p * g.Ks + kb * 32 + 8 * (lane >> 4);
+    int b = st * 16 + (lane & 15);
+    b = b < B ? b : 0;
+    xs.g[q] = t.gain ? ldg((const u32x4 *)(t.gain + col))
+                     : (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    const uint32_t off = (uint32_t)(((size_t)b * g.K + col) * 4);
+    xs.v[q][0] = lda4(r, off);
+    xs.v[q][1] = lda4(r, off + 16);
+  }
+}
+DEV void mx_store(Smem &sm, CP &d, const MGeo &g, int p, int pb, const XStage &xs,
+                  float (&ssl)[4]) {
+  const int lane = tidx() & 63, wave = uni(tidx() >> 6);
+  const int nu = mx_units(g, p), B16 = g.B16;
+  char *xb = (char *)sm.xs + pb * (g.nkb * B16 * 2048);
+  char *xlo = xb + g.nkb * B16 * 1024;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int u = wave + kWaves * q;
+    if (u >= nu) break;
+    const int kb = u / B16, st = u - kb * B16;
+    const bool live = st * 16 + (lane & 15) < d.B;
+    const u32x4 gq = xs.g[q];
+    const f32x8 gf = {bf_lo(gq.x), bf_hi(gq.x), bf_lo(gq.y), bf_hi(gq.y),
+                      bf_lo(gq.z), bf_hi(gq.z), bf_lo(gq.w), bf_hi(gq.w)};
+    f32x8 x = {xs.v[q][0].x, xs.v[q][0].y, xs.v[q][0].z, xs.v[q][0].w,
+               xs.v[q][1].x, xs.v[q][1].y, xs.v[q][1].z, xs.v[q][1].w};
+    x = live ? x : (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+      if (s2 == st) ssl[s2] += ss;
+    const f32x8 v = x * gf;
+    const bf16x8 h = __builtin_convertvector(v, bf16x8);
+    const bf16x8 lo = __builtin_convertvector(v - __builtin_convertvector(h, f32x8), bf16x8);
+    const int o = ((kb * B16 + st) * 64 + lane) * 16;
+    *(bf16x8 *)(xb + o) = h;
+    *(bf16x8 *)(xlo + o) = lo;
+  }
+}
+// Every wave's sums of squares to LDS (sm.red as [wave][lane][tile]); after
+// a barrier, 1/rms of slot b is reduced from the lanes holding its shares.
+DEV void mss_publish(Smem &sm, const float (&ssl)[4]) {
+  const int lane = tidx() & 63, wave = uni(tidx() >> 6);
+  f32x4 *dst = (f32x4 *)&sm.red[0][0];
+  dst[wave * 64 + lane] = (f32x4){ssl[0], ssl[1], ssl[2], ssl[3]};
+}
+DEV void mss_rms(Smem &sm, CP &d, const MGeo &g, float *rs) {
+  const int lane = tidx() & 63;
+  const f32x4 *src = (const f32x4 *)&sm.red[0][0];
+  if (lane < g.B16 * 16) {
+    const int st = lane >> 4, l16 = lane & 15;
+    float s = 0.f;
+    for (int w = 0; w < kWaves; ++w)
+      for (int m = 0; m < 4; ++m) s += src[w * 64 + m * 16 + l16][st];
+    rs[lane] = 1.0f / sqrtf(s / (float)g.K + d.eps);
+  }
+}
+
+// Control wave: outputs of a matrix-core task from out[row][slot] (LDS),
+// scaled by the slots' 1/rms (rs) when the input was normalised.
+DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, const MGeo &g, const float *out,
+                   const float *rs) {
+  const int lane = tidx() & 63;
+  const int R = g.NGs * 16, Bp = g.B16 * 16, B = d.B, op = t.op;
+  const size_t os = (size_t)t.ostride;
+  auto y_at = [&](int row, int b) { return out[row * Bp + b] * (t.gain ? rs[b] : 1.f); };
+  if (op == OP_LMHEAD) {
+    for (int b = 0; b < B; ++b) {
+      float bv = -INFINITY;
+      int bix = 0x7fffffff;
+      for (int i = lane; i < R; i += 64) {
+        const float y = y_at(i, b);
+        if (ca.logits) stg(ca.logits + (size_t)b * d.V + t.a1 + i, y);
+        if (better(y, t.a1 + i, bv, bix)) { bv = y; bix = t.a1 + i; }
+      }
+      wave_argmax(bv, bix);
+      if (lane == 0) {
+        const size_t o = (size_t)b * d.n_lm_tiles + t.a4;
+        sta(d.amax_v + o, bv);
+        stai(d.amax_i + o, bix);
+      }
+    }
+    return;
+  }
+  // eight outputs per lane in flight: residual loads first, then the stores
+  const int n = B * R;
+  for (int i0 = 0; i0 < n; i0 += 8 * 64) {
+    float a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = i0 + u * 64 + lane;
+      a[u] = 0.f;
+      if ((op == OP_OPROJ || op == OP_DOWN) && idx < n) {
+        const int b = idx / R, i = idx - b * R;
+        a[u] = lda(t.aux + (size_t)b * os + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = i0 + u * 64 + lane;
+      if (idx >= n) break;
+      const int b = idx / R, i = idx - b * R;
+      const float y = y_at(i, b);
+      float *dst = t.dst + (size_t)b * os + i;
+      if (op == OP_GATEUP)
+        sta(dst, silu(y) * y_at(R + i, b));
+      else
+        sta(dst, a[u] + y);  // QKV and ROUTER add zero
+    }
+  }
+}
+
+DEV bool gemv_mfma_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
+                       WState &ws) {
+  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  trace_start(d, t);
+  const MGeo g = mgeo_of(d, t);
+  float ssl[4] = {0.f, 0.f, 0.f, 0.f};
+  XStage xs;
+  mx_load(d, g, t, 0, xs);
+  mx_store(sm, d, g, 0, 0, xs, ssl);
+  trace_mark(d, t, 0);
+  __syncthreads();  // slice 0 staged
+  for (int p = 0; p < g.P; ++p) {
+    if (p + 1 < g.P) {
+      mx_load(d, g, t, p + 1, xs);
+      mx_store(sm, d, g, p + 1, (p + 1) & 1, xs, ssl);
+    }
+    __syncthreads();  // pass p done, slice p + 1 staged
+  }
+  mss_publish(sm, ssl);
+  __syncthreads();  // accumulators and sums of squares in LDS
+  trace_mark(d, t, 1);
+  float *rs = &sm.rows[0][0];
+  if (t.gain) mss_rms(sm, d, g, rs);  // this wave's own LDS writes: no barrier needed
+  mepilogue(d, ca, t, g, sm.xs, rs);
+  if (persistent) {
+    if (t.a5 > 0) vm_drain();
+    trace_finish(d, t);
+    signal_done(d, t);
+  }
+  __syncthreads();  // LDS free for the next task
+  ws.x_src = nullptr;
+  return true;
+}
+
+DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
+                       WState &ws, Buf &w, bool w_loaded, bool pre, const MGeo &gn) {
+  const int cw = uni(tidx() >> 6) - 1, lane = tidx() & 63;
+  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  const MGeo g = mgeo_of(d, t);
+  if (!w_loaded) mload(g, w, cw);
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float ssl[4] = {0.f, 0.f, 0.f, 0.f};
+  XStage xs;
+  mx_load(d, g, t, 0, xs);
+  mx_store(sm, d, g, 0, 0, xs, ssl);
+  __syncthreads();  // slice 0 staged
+  for (int p = 0; p < g.P; ++p) {
+    const char *xb = (const char *)sm.xs + (p & 1) * (g.nkb * g.B16 * 2048);
+    const bool more = p + 1 < g.P;
+    if (g.nkb >= 16)
+      mpass<16>(g, w, acc, xb, cw, p, pre, gn);
+    else
+      mpass<8>(g, w, acc, xb, cw, p, pre, gn);
+    // the next slice's loads queue behind this pass's refills (the next
+    // pass's weights), so they arrive with them
+    if (more) {
+      mx_load(d, g, t, p + 1, xs);
+      mx_store(sm, d, g, p + 1, (p + 1) & 1, xs, ssl);
+    }
+    __syncthreads();  // pass p done, slice p + 1 staged
+  }
+  mss_publish(sm, ssl);
+  // accumulators to out[row][slot]: row = matrix*NGs*16 + slot*16 + 4(l/16) + e
+  const int Bp = g.B16 * 16;
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    int seg, slot;
+    if (!mgroup(g, cw, gi, seg, slot)) continue;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (st >= g.B16) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = seg * g.NGs * 16 + slot * 16 + 4 * (lane >> 4) + e;
+        sm.xs[row * Bp + st * 16 + (lane & 15)] = acc[gi][st][e];
+      }
+    }
+  }
+  __syncthreads();  // accumulators and sums of squares in LDS
+  __syncthreads();  // outputs written: LDS free for the next task
+  ws.x_src = nullptr;
+  return true;
+}
+
+// Geometry of the next task's first pass (matrix-core mode) from its
+// descriptor words in the ring.
+DEV bool next_mgeo(CP &d, const uint32_t *slot, MGeo &g) {
+  const int op = (int)(int16_t)(uni((int)slot[0]) & 0xffff);
+  if (!static_weights(op)) return false;
+  const int rows = uni((int)slot[4]);
+  const uint16_t *w0 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[16]), (uint32_t)uni((int)slot[17]));
+  const uint16_t *w1 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[18]), (uint32_t)uni((int)slot[19]));
+  const int K = uni((int)slot[28]);
+  g = mgeo(w0, w1, rows, K, d.B);
+  return true;
+}
+
 // -------------------------------------------------------------- attention --
 // One (slot, KV head, split) task: the query heads of the group attend to
 // the cached keys of positions [lo, min(hi, pos)) of the split, read page by
@@ -1536,6 +1891,14 @@ DEV void run_task_once(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState 
       down_ctl(sm, d, ca, t, false, ws);
     else
       down_cmp(sm, d, ca, t, false, ws);
+  } else if (d.mfma && static_weights(t.op)) {
+    if (uni(tidx() >> 6) == 0) {
+      gemv_mfma_ctl(sm, d, ca, t, false, ws);
+    } else {
+      Buf w;
+      MGeo gn;
+      gemv_mfma_cmp(sm, d, ca, t, false, ws, w, false, false, gn);
+    }
   } else if (!is_gemv(t.op)) {
     run_small(sm, d, ca, t, false, ws);
   } else if (uni(tidx() >> 6) == 0) {
@@ -1569,9 +1932,12 @@ DEV bool next_geo(const uint32_t *slot, Geo &g) {
 // tasks form a run: one register tile buffer, local to the run, carries the
 // weights of each pass into the next, and of each task's last pass into the
 // next task's first (loaded before that task's dependency wait).
-template <bool B1>
+// MODE 0: any batch on the vector path; 1: one slot; 2: matrix-core GEMVs
+// (batches of 16..64 slots).
+template <int MODE>
 __global__ void __launch_bounds__(kThreads)
     mk_persistent_kernel(const DevPlan *__restrict__ dplan, CallArgs ca) {
+  constexpr bool B1 = MODE == 1;
   __shared__ Smem sm;
   CP &d = *(CP *)dplan;
   const int wid = blockIdx.x;
@@ -1591,9 +1957,11 @@ __global__ void __launch_bounds__(kThreads)
   if (wave == 0) {
     for (int k = beg; k < end; ++k) {
       const TD t = td_from_ring(sm.ring[(k - beg) % kRing]);
-      const bool alive = t.op == OP_EDOWN ? down_ctl(sm, d, ca, t, true, ws)
-                         : is_gemv(t.op)  ? gemv_ctl<B1>(sm, d, ca, t, true, ws)
-                                          : run_small(sm, d, ca, t, true, ws);
+      const bool alive =
+          t.op == OP_EDOWN                      ? down_ctl(sm, d, ca, t, true, ws)
+          : (MODE == 2 && static_weights(t.op)) ? gemv_mfma_ctl(sm, d, ca, t, true, ws)
+          : is_gemv(t.op)                       ? gemv_ctl<B1>(sm, d, ca, t, true, ws)
+                                                : run_small(sm, d, ca, t, true, ws);
       if (!alive) return;
     }
     return;
@@ -1612,7 +1980,19 @@ __global__ void __launch_bounds__(kThreads)
   int k = beg;
   while (k < end) {
     TD t = td_from_ring(sm.ring[(k - beg) % kRing]);
-    if (static_weights(t.op)) {
+    if (MODE == 2 && static_weights(t.op)) {
+      Buf w;
+      mload(mgeo_of(d, t), w, cw);
+      for (;;) {
+        MGeo gn;
+        const bool pre = k + 1 < end && next_mgeo(d, sm.ring[(k + 1 - beg) % kRing], gn);
+        if (!gemv_mfma_cmp(sm, d, ca, t, true, ws, w, true, pre, gn)) return;
+        refill(k);
+        ++k;
+        if (!pre) break;
+        t = td_from_ring(sm.ring[(k - beg) % kRing]);
+      }
+    } else if (static_weights(t.op)) {
       Buf w;
       load_slots(static_geo(t), w, cw);
       for (;;) {
@@ -1669,11 +2049,12 @@ __global__ void mk_zero_kernel(uint32_t *p, int n) {
 // ---------------------------------------------------------------- launch --
 // All workers must be resident at once (each may wait on any other), which a
 // cooperative launch guarantees or refuses.
-hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, int batch,
+hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, int mode,
                              hipStream_t s) {
   void *args[] = {(void *)&d, (void *)&ca};
-  const void *k = batch == 1 ? (const void *)mk_persistent_kernel<true>
-                             : (const void *)mk_persistent_kernel<false>;
+  const void *k = mode == 1   ? (const void *)mk_persistent_kernel<1>
+                  : mode == 2 ? (const void *)mk_persistent_kernel<2>
+                              : (const void *)mk_persistent_kernel<0>;
   return hipLaunchCooperativeKernel(k, dim3(grid), dim3(kThreads),
                                     args, 0, s);
 }

@@ -8,8 +8,9 @@ namespace mk {
 
 // One decode step as a single persistent launch: `grid` workgroups (one per
 // CU) pull tickets until the task list is exhausted.  `d` is a device copy.
-// batch: the plan's slot count (1 selects the single-slot build)
-hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, int batch,
+// mode: 0 any batch on the vector path, 1 a single slot, 2 matrix-core
+// GEMVs (batches of 16..64 slots)
+hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, int mode,
                              hipStream_t s);
 
 // Kernel-per-op: tasks [first, first+count) of one launch phase, one

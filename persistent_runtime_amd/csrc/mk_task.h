@@ -32,6 +32,10 @@ constexpr int kMaxBatchGemv = 4;       // slots a GEMV tile handles at once
 // A GEMV task streams its rows in passes of at most one register tile each;
 // passes x slots per task are bounded by the LDS partial-sum buffers.
 constexpr int kMaxPass = 8;
+// Batched decode (16..64 slots) runs the static-weight GEMVs as bf16
+// matrix-core tiles: 16-row groups, at most kMfmaGroups per task.
+constexpr int kMfmaGroups = 14;
+constexpr int kMfmaMaxBatch = 64;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
 constexpr int kLdsXBytes = 128 * 1024; // budget for staged activations
 
@@ -100,6 +104,7 @@ struct DevPlan {
   // shape
   int32_t L, H, nq, nkv, hd, F, V, E, topk, Fe, B, maxp, npages, S, G;
   int32_t max_pos, n_lm_tiles;
+  int32_t mfma;            // static GEMVs as matrix-core tiles (batch 16..64)
   float eps;
   // weights (bf16 as uint16)
   const uint16_t *embed, *lm_head, *final_norm;

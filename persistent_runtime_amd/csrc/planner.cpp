@@ -167,6 +167,14 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
   while ((row_bytes * unit) % 1024 || unit % min_unit) ++unit;
   int R = (int)((int64_t)kMaxTileUnits16 * 1024 / row_bytes);
   R -= R % unit;
+  if (b.p.mfma && op != OP_EGATEUP && op != OP_EDOWN) {
+    // matrix-core tiles: whole 16-row groups, at most kMfmaGroups per task
+    // (gate/up: at most half of them per matrix); the device streams each
+    // task along K in slices, so a task has one row pass
+    unit = 16;
+    R = (nseg == 2 ? kMfmaGroups / 2 : kMfmaGroups) * 16;
+    pmax = 1;
+  }
   if (R < unit) return -1;
   int64_t total = 0;
   for (auto &sg : segs) total += sg.rows;
@@ -271,6 +279,13 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   if (o.attn_splits > 0) p.S = std::min(o.attn_splits, 128);  // merge keeps G*S pairs in LDS
 
   bool ok = true;
+  // batched decode: matrix-core GEMV tiles when every static row count is a
+  // whole number of 16-row groups
+  {
+    const bool rows16 = H % 16 == 0 && (nq * hd) % 16 == 0 && hd % 16 == 0 &&
+                        c.vocab % 16 == 0 && (moe ? c.n_experts % 16 == 0 : c.ffn_dim % 16 == 0);
+    p.mfma = o.batched_mfma >= 0 && B >= 16 && B <= kMfmaMaxBatch && rows16;
+  }
   // passes per task: slots x passes share the LDS partial buffers; when the
   // slots of a step do not fit one activation stage the weights of a pass
   // are reused across slot chunks, so such tasks keep a single pass

@@ -246,6 +246,37 @@ def test_graph_replay_matches_eager(tiny, executor):
     r.plan.free()
 
 
+@pytest.mark.parametrize("mfma", [0, -1], ids=["matrix_cores", "vector"])
+def test_tiny_batch16(tiny, mfma):
+    """16 slots (the matrix-core GEMV tiles by default, the vector path when
+    switched off): every slot's logits against the oracle decoding that slot
+    alone, over prompts of different lengths and three teacher-forced steps;
+    one slot stays empty throughout."""
+    Wd, Wt = tiny
+    B = 16
+    r = Runner(TINY, Wd, B=B, maxp=8, batched_mfma=mfma)
+    prompts = [synth.make_prompt(10 + 3 * b, TINY["vocab"], seed=100 + b).tolist() for b in range(B)]
+    caches, refs = {}, {}
+    for b in range(B - 1):
+        r.prefill(b, prompts[b])
+        caches[b] = O.KVCache(TINY)
+        for p, tk in enumerate(prompts[b]):
+            refs[b] = O.decode_step(Wt, TINY, caches[b], int(tk), p)
+    worst = 0.0
+    for step in range(3):
+        toks = [O.greedy_argmax(refs[b]) if b in refs else 0 for b in range(B)]
+        poss = [len(prompts[b]) + step if b in refs else -1 for b in range(B)]
+        ids, lg = r.step(toks, poss)
+        assert ids[B - 1] == -1
+        for b in range(B - 1):
+            refs[b] = O.decode_step(Wt, TINY, caches[b], toks[b], poss[b])
+            worst = max(worst, float(np.max(np.abs(lg[b] - refs[b]))))
+            if O.top2_margin(refs[b]) > 0.05:
+                assert ids[b] == O.greedy_argmax(refs[b]), (step, b)
+    assert worst <= LOGIT_TOL, worst
+    r.plan.free()
+
+
 def test_tiny_moe_teacher_forced(tiny_moe):
     """MoE routing: ids equal the oracle's except at a top-k boundary closer
     than 1e-3, where the step is re-checked against the oracle forced to the

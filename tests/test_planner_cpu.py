@@ -280,3 +280,18 @@ def test_gemv_shares_balanced_and_passes_fit():
 def test_truncated_model_plans():
     tasks, _ = mk.inspect_plan(_cfg(truncated(LLAMA8B, 2), maxp=40))
     assert sum(1 for t in tasks if mk.OPS[t.op] == "LMHEAD") > 0
+
+
+def test_batched_plans_use_16_row_groups():
+    """Batches of 16..64 slots: every static-weight GEMV task covers whole
+    16-row groups, at most 14 per task (7 per matrix for gate/up); the
+    dependency structure stays valid."""
+    for model in (LLAMA8B, TINY):
+        for B in (16, 64):
+            tasks, thr = mk.inspect_plan(_cfg(model, B=B, maxp=8), mk.default_options(n_cus=256))
+            _check_graph(model, tasks, thr, B)
+            for t in tasks:
+                op = mk.OPS[t.op]
+                if op in ("QKV", "OPROJ", "GATEUP", "DOWN", "LMHEAD"):
+                    assert t.a1 % 16 == 0 and t.a2 % 16 == 0, (op, t.a1, t.a2)
+                    assert t.a2 // 16 <= (7 if op == "GATEUP" else 14), (op, t.a2)
