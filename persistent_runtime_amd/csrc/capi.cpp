@@ -64,6 +64,7 @@ struct mk_plan {
   std::vector<void *> allocs;
   uint32_t epoch = 0;
   uint32_t epoch_limit = 1;
+  uint32_t tag = 0;          // data tag of the last step (never 0 once used)
   bool graph_replay = false;
   int32_t *stage_tok = nullptr, *stage_pos = nullptr, *stage_next = nullptr;
   float *stage_logits = nullptr;
@@ -123,9 +124,9 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts, mk_task_i
       q.op = t.op; q.layer = t.layer;
       q.a0 = t.a0; q.a1 = t.a1; q.a2 = t.a2; q.a3 = t.a3; q.a4 = t.a4; q.sig_count = t.a5;
       q.n_wait = t.n_wait;
-      for (int k = 0; k < 3; ++k) q.wait_ev[k] = k < t.n_wait ? t.wait_ev[k] : -1;
+      for (int k = 0; k < 3; ++k) q.wait_ev[k] = k < t.n_wait ? t.wait_ev[k] & ~kDataEdge : -1;
       q.n_sig = t.n_sig;
-      for (int k = 0; k < 2; ++k) q.sig_ev[k] = k < t.n_sig ? t.sig_ev[k] : -1;
+      for (int k = 0; k < 2; ++k) q.sig_ev[k] = k < t.n_sig ? t.sig_ev[k] & ~kDataEdge : -1;
       q.phase = hp.task_phase[i];
       q.worker = hp.task_worker[i];
       q.rows_per_pass = t.rpp;
@@ -168,6 +169,8 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
   const int QD = c.n_q_heads * c.head_dim, KVD = c.n_kv_heads * c.head_dim;
   const int F = c.ffn_dim, E = c.n_experts, TK = c.top_k, Fe = c.expert_ffn_dim;
   auto W = [&](int kind, int l) { return (const uint16_t *)tab[(size_t)kind * L + l]; };
+  // element e of a tagged (value, tag) vector buffer
+  auto TG = [](float *base, size_t e) { return base + 2 * e; };
   // expert 0 of layer l of expert tensor m (0 gate, 1 up, 2 down)
   auto EX = [&](int m, int l) {
     return (const uint16_t *)tab[(size_t)10 * L + ((size_t)m * L + l) * E];
@@ -185,7 +188,7 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
         const int Nm = t.a0 == 0 ? QD : KVD;
         float *base = t.a0 == 0 ? d.q : (t.a0 == 1 ? d.k : d.v);
         t.w0 = W(2 + t.a0, l) + (size_t)t.a1 * H;
-        t.src = d.x + (size_t)l * B * H;
+        t.src = TG(d.x, (size_t)l * B * H);
         t.gain = W(0, l);
         t.K = H;
         t.dst = base + (size_t)l * B * Nm + t.a1;
@@ -194,32 +197,32 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
       }
       case OP_OPROJ:
         t.w0 = W(5, l) + (size_t)t.a1 * QD;
-        t.src = d.attn + (size_t)l * B * QD;
+        t.src = TG(d.attn, (size_t)l * B * QD);
         t.K = QD;
-        t.dst = d.xmid + (size_t)l * B * H + t.a1;
-        t.aux = d.x + (size_t)l * B * H + t.a1;
+        t.dst = TG(d.xmid, (size_t)l * B * H + t.a1);
+        t.aux = TG(d.x, (size_t)l * B * H + t.a1);
         t.ostride = H;
         break;
       case OP_GATEUP:
         t.w0 = W(6, l) + (size_t)t.a1 * H;
         t.w1 = W(7, l) + (size_t)t.a1 * H;
-        t.src = d.xmid + (size_t)l * B * H;
+        t.src = TG(d.xmid, (size_t)l * B * H);
         t.gain = W(1, l);
         t.K = H;
-        t.dst = d.h + (size_t)l * B * F + t.a1;
+        t.dst = TG(d.h, (size_t)l * B * F + t.a1);
         t.ostride = F;
         break;
       case OP_DOWN:
         t.w0 = W(8, l) + (size_t)t.a1 * F;
-        t.src = d.h + (size_t)l * B * F;
+        t.src = TG(d.h, (size_t)l * B * F);
         t.K = F;
-        t.dst = d.x + (size_t)(l + 1) * B * H + t.a1;
-        t.aux = d.xmid + (size_t)l * B * H + t.a1;
+        t.dst = TG(d.x, (size_t)(l + 1) * B * H + t.a1);
+        t.aux = TG(d.xmid, (size_t)l * B * H + t.a1);
         t.ostride = H;
         break;
       case OP_ROUTER:
         t.w0 = W(9, l) + (size_t)t.a1 * H;
-        t.src = d.xmid + (size_t)l * B * H;
+        t.src = TG(d.xmid, (size_t)l * B * H);
         t.gain = W(1, l);
         t.K = H;
         t.dst = d.rl + (size_t)l * B * E + t.a1;
@@ -227,7 +230,7 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
         break;
       case OP_LMHEAD:
         t.w0 = (const uint16_t *)w.lm_head + (size_t)t.a1 * H;
-        t.src = d.x + (size_t)L * B * H;
+        t.src = TG(d.x, (size_t)L * B * H);
         t.gain = (const uint16_t *)w.final_norm;
         t.K = H;
         break;
@@ -235,7 +238,7 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
         const size_t bj = ((size_t)l * B + t.a0) * TK + t.a3;
         t.w0 = EX(0, l);
         t.w1 = EX(1, l);
-        t.src = d.xmid + ((size_t)l * B + t.a0) * H;
+        t.src = TG(d.xmid, ((size_t)l * B + t.a0) * H);
         t.gain = W(1, l);
         t.K = H;
         t.dst = d.he + bj * Fe + t.a1;
@@ -246,8 +249,8 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
         t.w0 = EX(2, l);
         t.src = d.he + bx * TK * Fe;
         t.K = Fe;
-        t.dst = d.x + (bx + B) * H + t.a1;
-        t.aux = d.xmid + bx * H + t.a1;
+        t.dst = TG(d.x, (bx + B) * H + t.a1);
+        t.aux = TG(d.xmid, bx * H + t.a1);
         t.ostride = H;
         break;
       }
@@ -373,7 +376,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads;
     p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
-    const int64_t nf = hp.n_x + hp.n_xmid + hp.n_q + 2 * hp.n_k + hp.n_part + hp.n_attn + hp.n_h +
+    const int64_t nf = 2 * (hp.n_x + hp.n_xmid + hp.n_attn + hp.n_h) + hp.n_q + 2 * hp.n_k + hp.n_part +
                        hp.n_rl + hp.n_tk + hp.n_he + hp.n_amax;
     float *fs;
     if ((rc = p->alloc(&fs, (size_t)nf, "activation scratch"))) return rc;
@@ -437,8 +440,9 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.page_table = kv->page_table;
     float *f = fs;
     auto take = [&](int64_t n) { float *r = n ? f : nullptr; f += n; return r; };
-    d.x = take(hp.n_x); d.xmid = take(hp.n_xmid); d.q = take(hp.n_q); d.k = take(hp.n_k);
-    d.v = take(hp.n_k); d.part = take(hp.n_part); d.attn = take(hp.n_attn); d.h = take(hp.n_h);
+    d.x = take(2 * hp.n_x); d.xmid = take(2 * hp.n_xmid); d.q = take(hp.n_q); d.k = take(hp.n_k);
+    d.v = take(hp.n_k); d.part = take(hp.n_part); d.attn = take(2 * hp.n_attn);
+    d.h = take(2 * hp.n_h);
     d.rl = take(hp.n_rl); d.tk_w = take(hp.n_tk); d.he = take(hp.n_he);
     d.amax_v = take(hp.n_amax);
     d.tk_ids = hp.n_tk ? is : nullptr;
@@ -494,10 +498,16 @@ static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positi
   ca.next_tokens = next;
   ca.logits = logits;
   if (plan->graph_replay) {
-    // a replayable step: counters from zero, no state carried on the host
+    // a replayable step: counters from zero and a data tag bumped on the
+    // device, no state carried on the host
     HIP_TRY(launch_zero_u32(d.ev, (int)plan->hp.ev_thr.size() + plan->n_att_cnt, s),
             "counter clear");
+    HIP_TRY(launch_bump_tag(plan->ctrl + CTRL_TAG, s), "tag bump");
     plan->epoch = 0;
+    ca.tag = 0;
+  } else {
+    if (++plan->tag == 0) plan->tag = 1;
+    ca.tag = plan->tag;
   }
   ca.epoch = plan->epoch;
   if (plan->executor == MK_EXEC_PERSISTENT) {

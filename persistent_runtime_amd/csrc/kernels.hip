@@ -164,6 +164,14 @@ DEV int ldai(const int32_t *p) {
 DEV void stai(int32_t *p, int32_t v) {
   __hip_atomic_store((AS1 int32_t *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Element i of a tagged vector (value, tag pairs): one 8-byte store, so a
+// reader that sees the tag sees the value; the value alone for readers whose
+// ordering is already established.
+DEV void stt(float *pairs, size_t i, float v, uint32_t tag) {
+  __hip_atomic_store((AS1 uint64_t *)pairs + i, ((uint64_t)tag << 32) | __float_as_uint(v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DEV float ldv(const float *pairs, size_t i) { return lda(pairs + 2 * i); }
 constexpr int kCpolSc1 = 16;  // cache-policy bit: device-scope coherent
 DEV __amdgpu_buffer_rsrc_t rsrc(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
@@ -296,6 +304,7 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws)
   for (int i = 0; i < 3; ++i) {
     if (i >= t.n_wait) break;
     const int e = t.wait_ev[i];
+    if (e & kDataEdge) continue;  // the staged data carries its own readiness
     const uint32_t want = (ca.epoch + 1u) * (uint32_t)t.wait_thr[i];
     const bool seen = (ws.sat_ev[0] == e && ws.sat_want[0] == want) ||
                       (ws.sat_ev[1] == e && ws.sat_want[1] == want);
@@ -307,6 +316,7 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws)
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       if (i >= t.n_wait || !ok) break;
+      if (t.wait_ev[i] & kDataEdge) continue;
       uint32_t *c = d.ev + t.wait_ev[i];
       const uint32_t want = (ca.epoch + 1u) * (uint32_t)t.wait_thr[i];
       uint32_t seen = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -333,6 +343,7 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws)
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       if (i >= t.n_wait) break;
+      if (t.wait_ev[i] & kDataEdge) continue;
       ws.sat_ev[1] = ws.sat_ev[0];
       ws.sat_want[1] = ws.sat_want[0];
       ws.sat_ev[0] = t.wait_ev[i];
@@ -372,12 +383,15 @@ DEV void signal_count(CP &d, const TD &t, int count) {
   if (tidx() == 0 && count > 0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      if (i < t.n_sig)
+      if (i < t.n_sig && !(t.sig_ev[i] & kDataEdge))
         __hip_atomic_fetch_add(d.ev + t.sig_ev[i], (uint32_t)count, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 DEV void signal_done(CP &d, const TD &t) { signal_count(d, t, t.a5); }
+DEV bool signals_counter(const TD &t) {
+  return (t.n_sig > 0 && !(t.sig_ev[0] & kDataEdge)) || (t.n_sig > 1 && !(t.sig_ev[1] & kDataEdge));
+}
 
 // ------------------------------------------------------------ GEMV tiles --
 // A tile is `nseg` blocks of `seg_rows` consecutive rows (row length K bf16)
@@ -620,6 +634,94 @@ DEV void stage_x(Smem &sm, WState &ws, const float *src, int K, int nb, const ui
   ws.x_nb = nb;
 }
 
+// A lane whose 16-byte load (two value/tag pairs of a tagged vector) shows
+// an older tag loads it again until both tags are this step's, the spin
+// budget runs out or another worker has failed; sm.imisc[2] = tag marks a
+// failure for the workgroup.
+DEV u32x4 wait_pairs(Smem &sm, CP &d, const CallArgs &ca, const TD &t,
+                     __amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  const uint32_t tag = ca.tag;
+  const uint64_t t0 = wall_clock64();
+  while (v.y != tag || v.w != tag) {
+    if (error_set(d)) {
+      sm.imisc[2] = (int)tag;
+      break;
+    }
+    if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
+      set_error(d, DEVERR_TIMEOUT, t.gidx, -4, v.y != tag ? v.y : v.w, tag);
+      sm.imisc[2] = (int)tag;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = __builtin_bit_cast(u32x4, lda4(r, off));
+  }
+  return v;
+}
+
+// Stage nb rows of a tagged vector into LDS exactly as stage_x does (x*g,
+// then 1/rms).  The tags stand in for the dependency wait: the rows are
+// complete once every element carries this step's tag.  Returns false (in
+// every wave) when the step is abandoned.
+DEV bool stage_xt(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws, const float *src,
+                  int K, int nb, const uint16_t *gain) {
+  if (ws.x_src == src && ws.x_gain == gain && ws.x_K == K && ws.x_nb == nb) return true;
+  const int tid = tidx(), lane = tid & 63, wave = tid >> 6;
+  const __amdgpu_buffer_rsrc_t r = rsrc(src);
+  const int K2 = K / 2;                         // 16-byte loads per row
+  const uint32_t *g1 = (const uint32_t *)gain;  // two bf16 gains per load
+  for (int b = 0; b < nb; ++b) {
+    float2 *d2 = (float2 *)(sm.xs + (size_t)b * K);
+    float ss = 0.f;
+    // K is a multiple of 256: every range test below is wave-uniform
+    for (int i0 = uni(wave) * 64; i0 < K2; i0 += 4 * kThreads) {
+      u32x4 v[4];
+      uint32_t gv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        gv[u] = 0x3f803f80u;  // bf16 ones
+        if (i0 + u * kThreads < K2) {
+          const int i = i0 + u * kThreads + lane;
+          v[u] = __builtin_bit_cast(u32x4, lda4(r, (uint32_t)(((size_t)b * K2 + i) * 16)));
+          if (gain) gv[u] = ldg(g1 + i);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (i0 + u * kThreads < K2) {
+          const int i = i0 + u * kThreads + lane;
+          if (v[u].y != ca.tag || v[u].w != ca.tag)
+            v[u] = wait_pairs(sm, d, ca, t, r, (uint32_t)(((size_t)b * K2 + i) * 16), v[u]);
+          const float x0 = __uint_as_float(v[u].x), x1 = __uint_as_float(v[u].z);
+          ss = fmaf(x0, x0, ss);
+          ss = fmaf(x1, x1, ss);
+          d2[i] = make_float2(x0 * bf_lo(gv[u]), x1 * bf_hi(gv[u]));
+        }
+      }
+    }
+    if (gain) {
+      ss = wave_sum(ss);
+      if (lane == 0) sm.misc[b * kWaves + wave] = ss;
+    }
+  }
+  __syncthreads();
+  if (sm.imisc[2] == (int)ca.tag) return false;
+  if (gain) {
+    for (int b = 0; b < nb; ++b) {
+      float tot = 0.f;
+      for (int w = 0; w < kWaves; ++w) tot += sm.misc[b * kWaves + w];
+      const float rs = 1.0f / sqrtf(tot / (float)K + d.eps);
+      f32x4 *xb = (f32x4 *)(sm.xs + (size_t)b * K);
+      for (int i = tid; i < K / 4; i += kThreads) xb[i] = xb[i] * rs;
+    }
+    __syncthreads();
+  }
+  ws.x_src = src;
+  ws.x_gain = gain;
+  ws.x_K = K;
+  ws.x_nb = nb;
+  return true;
+}
+
 // single-segment-input GEMV tasks (the expert down projection has its own code)
 DEV bool is_gemv(int op) {
   return op == OP_QKV || op == OP_OPROJ || op == OP_GATEUP || op == OP_DOWN ||
@@ -773,16 +875,19 @@ DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const float *rsum
   for (int idx = lane; idx < n * rows; idx += 64) {
     const int bi = idx / rows, i = idx - bi * rows;
     const float y = at(bi, i, 0);
-    float *dst = t.dst + (size_t)(b0 + bi) * os + i;
+    const size_t e = (size_t)(b0 + bi) * os + i;  // output element (slot b0+bi, row i)
     switch (op) {
-      case OP_OPROJ: case OP_DOWN:  // residual add (first pass: preloaded)
-        sta(dst, (idx < 64 ? aux0 : lda(t.aux + (size_t)(b0 + bi) * os + i)) + y);
+      case OP_OPROJ: case OP_DOWN:  // residual add (first outputs: preloaded); tagged
+        stt(t.dst, e, (idx < 64 ? aux0 : ldv(t.aux, e)) + y, ca.tag);
         break;
-      case OP_GATEUP: case OP_EGATEUP:  // SwiGLU of the gate and up rows
-        sta(dst, silu(y) * at(bi, i, 1));
+      case OP_GATEUP:  // SwiGLU of the gate and up rows; tagged
+        stt(t.dst, e, silu(y) * at(bi, i, 1), ca.tag);
+        break;
+      case OP_EGATEUP:
+        sta(t.dst + e, silu(y) * at(bi, i, 1));
         break;
       default:  // QKV, ROUTER
-        sta(dst, y);
+        sta(t.dst + e, y);
         break;
     }
   }
@@ -856,10 +961,10 @@ template <bool B1>
 DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
                   WState &ws) {
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
-  trace_start(d, t);
   const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t);
   if (q.skip) {
     if (persistent) {
+      trace_start(d, t);
       trace_finish(d, t);
       signal_done(d, t);
     }
@@ -870,17 +975,19 @@ DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   for (int b0 = 0; b0 < q.nb; b0 += q.bb_max) {
     const int n = min(q.bb_max, q.nb - b0);
     if (n < q.nb) ws.x_src = nullptr;  // chunked batch: no reuse
-    stage_x(sm, ws, t.src + (size_t)b0 * K, K, n, t.gain, d.eps);
+    if (!stage_xt(sm, d, ca, t, ws, t.src + 2 * (size_t)b0 * K, K, n, t.gain)) return false;
+    if (b0 == 0) trace_start(d, t);  // inputs complete
     trace_mark(d, t, 0);
     // the residual of the first outputs, loaded while the compute waves work
     float aux0 = 0.f;
     if ((t.op == OP_OPROJ || t.op == OP_DOWN) && lane < n * t.a2) {
       const int bi = lane / t.a2, i = lane - bi * t.a2;
-      aux0 = lda(t.aux + (size_t)(b0 + bi) * t.ostride + i);
+      aux0 = ldv(t.aux, (size_t)(b0 + bi) * t.ostride + i);
     }
     __syncthreads();  // partials complete
     __syncthreads();  // row sums complete
     trace_mark(d, t, 1);
+    if (persistent && b0 == 0) trace_finish(d, t);  // before the outputs: consumers start after
     gemv_epilogue(d, ca, t, &sm.rows[0][0], q.bfirst, b0, n, aux0, q.rpp);
     if (n < q.nb) {
       ws.x_src = nullptr;
@@ -895,9 +1002,9 @@ DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   }
   if (persistent) {
     // The epilogue's stores are all this wave's: drain them only where the
-    // run's completions are reported (the wait covers the earlier tasks too).
-    if (t.a5 > 0) vm_drain();
-    trace_finish(d, t);  // before the signal: consumers start after it
+    // run's completions are reported to a counter (the wait covers the
+    // earlier tasks too); tagged outputs need neither.
+    if (t.a5 > 0 && signals_counter(t)) vm_drain();
     signal_done(d, t);
   }
   return true;
@@ -924,7 +1031,7 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     const int n = min(q.bb_max, q.nb - b0);
     const bool last = b0 + n >= q.nb;
     if (n < q.nb) ws.x_src = nullptr;
-    stage_x(sm, ws, t.src + (size_t)b0 * K, K, n, t.gain, d.eps);
+    if (!stage_xt(sm, d, ca, t, ws, t.src + 2 * (size_t)b0 * K, K, n, t.gain)) return false;
     // The first pass was loaded before the task; waiting for all of it here
     // lets the pass loop wait per slot for the loads it issues itself.
     __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -991,27 +1098,28 @@ DEV bool down_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   const DownShape s = down_shape(d, ca, t);
   const int lane = tidx() & 63;
   if (s.skip) {
-    for (int i = lane; i < t.a2; i += 64) sta(t.dst + i, 0.f);
+    if (persistent) trace_finish(d, t);
+    for (int i = lane; i < t.a2; i += 64) stt(t.dst, i, 0.f, ca.tag);
   } else {
     int id;
     float w;
     routed(d, t, id, w);
     stage_x(sm, ws, t.src, t.K, d.topk, nullptr, d.eps);
     trace_mark(d, t, 0);
-    const float aux0 = lane < t.a2 ? lda(t.aux + lane) : 0.f;
+    const float aux0 = lane < t.a2 ? ldv(t.aux, lane) : 0.f;
     __syncthreads();  // partials complete
     __syncthreads();  // row sums complete
     trace_mark(d, t, 1);
+    if (persistent) trace_finish(d, t);  // before the outputs: consumers start after
     const float *rsum = &sm.rows[0][0];
     for (int i = lane; i < t.a2; i += 64) {
       float acc = 0.f;
       for (int j = 0; j < d.topk; ++j) acc = fmaf(lanef(w, j), rsum[j * t.a2 + i], acc);
-      sta(t.dst + i, (i < 64 ? aux0 : lda(t.aux + i)) + acc);
+      stt(t.dst, i, (i < 64 ? aux0 : ldv(t.aux, i)) + acc, ca.tag);
     }
   }
   if (persistent) {
-    if (t.a5 > 0) vm_drain();
-    trace_finish(d, t);
+    if (t.a5 > 0 && signals_counter(t)) vm_drain();
     signal_done(d, t);
   }
   return true;
@@ -1194,7 +1302,7 @@ DEV void mpass(const MGeo &g, Buf &w, f32x4 (&acc)[2][4], const char *xb, int cw
 // stored), which keeps the compiler's waits per load instead of for the
 // whole queue.
 struct XStage {
-  f32x4 v[4][2];
+  u32x4 v[4][4];   // 8 (value, tag) pairs per unit
   u32x4 g[4];
 };
 DEV int mx_units(const MGeo &g, int p) { return (min(g.Ks, g.K - p * g.Ks) >> 5) * g.B16; }
@@ -1212,9 +1320,9 @@ DEV void mx_load(CP &d, const MGeo &g, const TD &t, int p, XStage &xs) {
     b = b < B ? b : 0;
     xs.g[q] = t.gain ? ldg((const u32x4 *)(t.gain + col))
                      : (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-    const uint32_t off = (uint32_t)(((size_t)b * g.K + col) * 4);
-    xs.v[q][0] = lda4(r, off);
-    xs.v[q][1] = lda4(r, off + 16);
+    const uint32_t off = (uint32_t)(((size_t)b * g.K + col) * 8);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xs.v[q][m] = __builtin_bit_cast(u32x4, lda4(r, off + 16 * m));
   }
 }
 DEV void mx_store(Smem &sm, CP &d, const MGeo &g, int p, int pb, const XStage &xs,
@@ -1232,8 +1340,11 @@ DEV void mx_store(Smem &sm, CP &d, const MGeo &g, int p, int pb, const XStage &x
     const u32x4 gq = xs.g[q];
     const f32x8 gf = {bf_lo(gq.x), bf_hi(gq.x), bf_lo(gq.y), bf_hi(gq.y),
                       bf_lo(gq.z), bf_hi(gq.z), bf_lo(gq.w), bf_hi(gq.w)};
-    f32x8 x = {xs.v[q][0].x, xs.v[q][0].y, xs.v[q][0].z, xs.v[q][0].w,
-               xs.v[q][1].x, xs.v[q][1].y, xs.v[q][1].z, xs.v[q][1].w};
+    // (matrix-core batches keep the counters: the tags are current here)
+    f32x8 x = {__uint_as_float(xs.v[q][0].x), __uint_as_float(xs.v[q][0].z),
+               __uint_as_float(xs.v[q][1].x), __uint_as_float(xs.v[q][1].z),
+               __uint_as_float(xs.v[q][2].x), __uint_as_float(xs.v[q][2].z),
+               __uint_as_float(xs.v[q][3].x), __uint_as_float(xs.v[q][3].z)};
     x = live ? x : (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
 #pragma unroll
@@ -1304,7 +1415,7 @@ DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, const MGeo &g, const 
       a[u] = 0.f;
       if ((op == OP_OPROJ || op == OP_DOWN) && idx < n) {
         const int b = idx / R, i = idx - b * R;
-        a[u] = lda(t.aux + (size_t)b * os + i);
+        a[u] = ldv(t.aux, (size_t)b * os + i);
       }
     }
 #pragma unroll
@@ -1313,11 +1424,13 @@ DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, const MGeo &g, const 
       if (idx >= n) break;
       const int b = idx / R, i = idx - b * R;
       const float y = y_at(i, b);
-      float *dst = t.dst + (size_t)b * os + i;
+      const size_t e = (size_t)b * os + i;
       if (op == OP_GATEUP)
-        sta(dst, silu(y) * y_at(R + i, b));
+        stt(t.dst, e, silu(y) * y_at(R + i, b), ca.tag);
+      else if (op == OP_OPROJ || op == OP_DOWN)
+        stt(t.dst, e, a[u] + y, ca.tag);
       else
-        sta(dst, a[u] + y);  // QKV and ROUTER add zero
+        sta(t.dst + e, y);  // QKV, ROUTER
     }
   }
 }
@@ -1509,10 +1622,11 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   if (!pos_ok) {
     if (pos >= d.max_pos && tid == 0)
       set_error(d, DEVERR_BAD_INPUT, tix, -1, (uint32_t)pos, (uint32_t)d.max_pos);
+    if (S == 1 && persistent) trace_finish(d, t);  // before the (tagged) outputs
     for (int idx = tid; idx < G * HD; idx += kThreads) {
       const int h = idx / HD, dd = idx - h * HD;
       if (S == 1) {
-        sta(d.attn + (head0 + h) * HD + dd, 0.f);
+        stt(d.attn, (head0 + h) * HD + dd, 0.f, ca.tag);
       } else {
         float *pp = d.part + ((head0 + h) * S + sp) * PS;
         sta(pp + dd, 0.f);
@@ -1683,6 +1797,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   }
   __syncthreads();
   trace_mark(d, t, 1);
+  if (S == 1 && persistent) trace_finish(d, t);  // before the (tagged) outputs
   // merge the waves (fixed order) and the current key
   for (int idx = tid; idx < G * HD; idx += kThreads) {
     const int h = idx / HD, dd = idx - h * HD;
@@ -1705,7 +1820,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
       }
     }
     if (S == 1) {
-      sta(d.attn + (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f);
+      stt(d.attn, (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f, ca.tag);
     } else {
       float *pp = d.part + ((head0 + h) * S + sp) * PS;
       sta(pp + dd, Os);
@@ -1722,7 +1837,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
 // before anything is consumed.  One wave per head turns (m, l) into the
 // weights 2^(m_s - M) / L in LDS; each thread adds up its weighted vectors,
 // and the subsets are added in a fixed order (deterministic).
-DEV void run_merge(Smem &sm, CP &d, const TD &t) {
+DEV void run_merge(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
   const int l = t.layer, b = t.a0, g = t.a1, G = d.G, S = d.S, HD = d.hd;
   const int PS = HD + 4, hv = HD / 4, nvec = G * hv, npairs = G * S;
   const int nsub = kThreads / nvec;
@@ -1783,11 +1898,11 @@ DEV void run_merge(Smem &sm, CP &d, const TD &t) {
     f32x4 sum = red[vv];
     for (int q = 1; q < nsub; ++q) sum += red[q * nvec + vv];
     const int hh = vv / hv, d0 = (vv - hh * hv) * 4;
-    float *dst = d.attn + (head0 + hh) * HD + d0;
-    sta(dst + 0, sum.x);
-    sta(dst + 1, sum.y);
-    sta(dst + 2, sum.z);
-    sta(dst + 3, sum.w);
+    const size_t e = (head0 + hh) * HD + d0;
+    stt(d.attn, e + 0, sum.x, ca.tag);
+    stt(d.attn, e + 1, sum.y, ca.tag);
+    stt(d.attn, e + 2, sum.z, ca.tag);
+    stt(d.attn, e + 3, sum.w, ca.tag);
   }
 }
 
@@ -1800,9 +1915,9 @@ DEV void run_embed(CP &d, const CallArgs &ca, const TD &t) {
   const bool ok = pos >= 0 && tok >= 0 && tok < d.V;
   if (pos >= 0 && !ok && tidx() == 0)
     set_error(d, DEVERR_BAD_INPUT, tix, -3, (uint32_t)tok, (uint32_t)d.V);
-  float *x = d.x + (size_t)b * H;
   const uint16_t *e = d.embed + (size_t)(ok ? tok : 0) * H;
-  for (int i = tidx(); i < H; i += kThreads) sta(x + i, ok ? bf1(ldg(e + i)) : 0.f);
+  for (int i = tidx(); i < H; i += kThreads)
+    stt(d.x, (size_t)b * H + i, ok ? bf1(ldg(e + i)) : 0.f, ca.tag);
 }
 
 // Softmax router top-k: k rounds of (max, lowest index) over the logits not
@@ -1843,7 +1958,10 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
     trace_start(d, t);
   }
   switch (t.op) {
-    case OP_EMBED: run_embed(d, ca, t); break;
+    case OP_EMBED:
+      if (persistent) trace_finish(d, t);  // before the (tagged) outputs
+      run_embed(d, ca, t);
+      break;
     case OP_ARGMAX: run_argmax(sm, d, ca, t); break;
     default: break;
   }
@@ -1864,17 +1982,19 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
     __syncthreads();
     const bool last = sm.imisc[1] != 0;
     if (last) {
-      run_merge(sm, d, t);
-      vm_drain();
+      run_merge(sm, d, ca, t);
+      if (signals_counter(t)) vm_drain();
     }
     __syncthreads();
     if (persistent) signal_count(d, t, last ? 1 : 0);
     return true;
   }
-  if (persistent) vm_drain();
+  if (persistent && signals_counter(t)) vm_drain();
   __syncthreads();
   if (persistent) {
-    trace_finish(d, t);
+    // (embeddings and single-split attention recorded theirs before the
+    // outputs)
+    if (t.op != OP_EMBED && !(t.op == OP_ATTN && d.S == 1)) trace_finish(d, t);
     signal_done(d, t);
   }
   return true;
@@ -1932,14 +2052,23 @@ DEV bool next_geo(const uint32_t *slot, Geo &g) {
 // tasks form a run: one register tile buffer, local to the run, carries the
 // weights of each pass into the next, and of each task's last pass into the
 // next task's first (loaded before that task's dependency wait).
+// The step's data tag: the launch argument, or for graph-replayed steps the
+// device word that a kernel bumped before this one.
+DEV CallArgs resolve_args(CP &d, CallArgs ca) {
+  if (ca.tag == 0u) ca.tag = (uint32_t)uni((int)ldg(d.ctrl + CTRL_TAG));
+  return ca;
+}
+
 // MODE 0: any batch on the vector path; 1: one slot; 2: matrix-core GEMVs
 // (batches of 16..64 slots).
 template <int MODE>
 __global__ void __launch_bounds__(kThreads)
-    mk_persistent_kernel(const DevPlan *__restrict__ dplan, CallArgs ca) {
+    mk_persistent_kernel(const DevPlan *__restrict__ dplan, CallArgs ca_in) {
   constexpr bool B1 = MODE == 1;
   __shared__ Smem sm;
   CP &d = *(CP *)dplan;
+  const CallArgs ca = resolve_args(d, ca_in);
+  if (tidx() == 0) sm.imisc[2] = 0;  // no tagged-data failure (the tag is never 0)
   const int wid = blockIdx.x;
   const int beg = ((const AS4 int *)d.worker_off)[wid];
   const int end = ((const AS4 int *)d.worker_off)[wid + 1];
@@ -2023,9 +2152,12 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 __global__ void __launch_bounds__(kThreads)
-    mk_phase_kernel(const DevPlan *__restrict__ dplan, CallArgs ca, int first) {
+    mk_phase_kernel(const DevPlan *__restrict__ dplan, CallArgs ca_in, int first) {
   __shared__ Smem sm;
   CP &d = *(CP *)dplan;
+  const CallArgs ca = resolve_args(d, ca_in);
+  if (tidx() == 0) sm.imisc[2] = 0;
+  __syncthreads();
   const int pos = ((const AS4 int *)d.task_pos)[first + (int)blockIdx.x];
   const TD t = td_from_table(d.tasks, pos);
   WState ws;
@@ -2039,6 +2171,13 @@ __global__ void mk_stage_kernel(int32_t *tok, int32_t *pos, int B, int slot,
   if (b >= B) return;
   tok[b] = b == slot ? tokens[i] : 0;
   pos[b] = b == slot ? start + i : -1;
+}
+
+__global__ void mk_bump_kernel(uint32_t *p) {
+  if (threadIdx.x == 0) {
+    const uint32_t v = p[0] + 1u;
+    p[0] = v ? v : 1u;
+  }
 }
 
 __global__ void mk_zero_kernel(uint32_t *p, int n) {
@@ -2069,6 +2208,11 @@ hipError_t launch_stage(int32_t *stage_tok, int32_t *stage_pos, int B, int slot,
                         const int32_t *tokens, int i, int start, hipStream_t s) {
   hipLaunchKernelGGL(mk_stage_kernel, dim3((B + 255) / 256), dim3(256), 0, s, stage_tok,
                      stage_pos, B, slot, tokens, i, start);
+  return hipGetLastError();
+}
+
+hipError_t launch_bump_tag(uint32_t *p, hipStream_t s) {
+  hipLaunchKernelGGL(mk_bump_kernel, dim3(1), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -24,6 +24,9 @@ hipError_t launch_stage(int32_t *stage_tok, int32_t *stage_pos, int B, int slot,
                         const int32_t *tokens, int i, int start, hipStream_t s);
 
 // Zero n words (counter reset between epochs).
+// p[0] += 1, skipping 0 (the data tag of graph-replayed steps)
+hipError_t launch_bump_tag(uint32_t *p, hipStream_t s);
+
 hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t s);
 
 // Resource use of the persistent kernel (for reports).

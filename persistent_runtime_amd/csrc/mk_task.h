@@ -95,6 +95,7 @@ static_assert(sizeof(Task) == 128, "task descriptor is 128 bytes");
 enum Ctrl {
   CTRL_TICKET = 0, CTRL_DONE = 1, CTRL_ERR = 2, CTRL_ERR_TASK = 3,
   CTRL_ERR_EV = 4, CTRL_ERR_SEEN = 5, CTRL_ERR_WANT = 6, CTRL_CLOCK = 7,
+  CTRL_TAG = 8,    // data tag of graph-replayed steps (bumped by a kernel per step)
   CTRL_WORDS = 16
 };
 enum DevErr { DEVERR_NONE = 0, DEVERR_TIMEOUT = 1, DEVERR_BAD_INPUT = 2 };
@@ -121,7 +122,7 @@ struct DevPlan {
   uint16_t *k_pool, *v_pool;
   const int32_t *page_table;
   // scratch (fp32 unless noted); layouts in planner.cpp
-  float *x, *xmid, *q, *k, *v, *part, *attn, *h;
+  float *x, *xmid, *q, *k, *v, *part, *attn, *h;   // x, xmid, attn, h: tagged pairs
   float *rl, *tk_w, *he, *amax_v;
   int32_t *tk_ids, *amax_i;
   const float *rope_cos, *rope_sin;                     // [max_pos][hd/2]
@@ -146,7 +147,18 @@ struct CallArgs {
   int32_t *next_tokens;
   float *logits;
   uint32_t epoch;
+  uint32_t tag;   // this step's data tag (nonzero); 0: read CTRL_TAG (graph replay)
 };
+
+// Tagged activations.  The vectors that one operation writes and the next
+// reads in full (x, xmid, attn, h) hold (value, tag) pairs: each element is
+// one 8-byte store of its fp32 value and the step's tag, so a reader that
+// sees the current tag has the value too.  An edge into a task that reads
+// such a vector is a data edge: the reader loads until every tag is
+// current instead of waiting for an event counter, and the writer signals
+// nothing (no drain, no atomic).  Event ids with kDataEdge set are data
+// edges; the task lists keep them so the graph can be checked.
+constexpr int32_t kDataEdge = 1 << 30;
 
 // scratch sizes (elements), shared by planner and device code
 inline int64_t part_stride(int hd) { return hd + 4; }  // o[hd], m, l, pad

@@ -312,6 +312,9 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   Builder b(p);
   std::vector<int> x_ev(L + 1);
   for (int l = 0; l <= L; ++l) x_ev[l] = b.ev();
+  // events of edges into tasks that read a whole tagged vector (x, attn,
+  // xmid, h): data edges unless the batch runs on matrix cores
+  std::vector<int> data_ev(x_ev);
 
   b.begin_phase();
   for (int s = 0; s < B; ++s)
@@ -345,12 +348,15 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     if (p.S > 1) p.ev_thr[mrg] = B * nkv;  // one merged group per (slot, KV head)
     // O projection + residual
     int xo = b.ev();
+    data_ev.push_back(mrg);
+    data_ev.push_back(xo);
     b.begin_phase();
     if (add_gemv(b, OP_OPROJ, l, {{0, 0, H, xo}}, nq * hd, 1, n_workers, pmax_for(nq * hd), mrg,
                  0, nullptr) < 0)
       ok = false;
     if (!moe) {
       int hev = b.ev();
+      data_ev.push_back(hev);
       b.begin_phase();
       if (add_gemv(b, OP_GATEUP, l, {{0, 0, c.ffn_dim, hev}}, H, 2, n_workers, pmax_for(H), xo,
                    0, nullptr) < 0)
@@ -478,7 +484,22 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     p.worker_list.insert(p.worker_list.end(), lst.begin(), lst.end());
   }
   p.worker_off[n_workers] = (int32_t)p.worker_list.size();
-  return validate_plan(p, err);
+  rc = validate_plan(p, err);
+  if (rc != MK_OK) return rc;
+  // Data edges: the reader checks the tags of the vector it stages instead of
+  // waiting for the counter, and the writers do not signal.  (Matrix-core
+  // batches stage their activations in slices, so they keep the counters.)
+  if (!p.mfma) {
+    std::vector<char> is_data(p.ev_thr.size(), 0);
+    for (int e : data_ev) is_data[e] = 1;
+    for (auto &t : p.tasks) {
+      for (int i = 0; i < t.n_wait; ++i)
+        if (is_data[t.wait_ev[i]]) t.wait_ev[i] |= kDataEdge;
+      for (int i = 0; i < t.n_sig; ++i)
+        if (is_data[t.sig_ev[i]]) t.sig_ev[i] |= kDataEdge;
+    }
+  }
+  return MK_OK;
 }
 
 int validate_plan(const HostPlan &p, std::string &err) {
