@@ -191,7 +191,7 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
         t.src = TG(d.x, (size_t)l * B * H);
         t.gain = W(0, l);
         t.K = H;
-        t.dst = base + (size_t)l * B * Nm + t.a1;
+        t.dst = TG(base, (size_t)l * B * Nm + t.a1);
         t.ostride = Nm;
         break;
       }
@@ -376,7 +376,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads;
     p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
-    const int64_t nf = 2 * (hp.n_x + hp.n_xmid + hp.n_attn + hp.n_h) + hp.n_q + 2 * hp.n_k + hp.n_part +
+    const int64_t nf = 2 * (hp.n_x + hp.n_xmid + hp.n_attn + hp.n_h + hp.n_q + 2 * hp.n_k) + hp.n_part +
                        hp.n_rl + hp.n_tk + hp.n_he + hp.n_amax;
     float *fs;
     if ((rc = p->alloc(&fs, (size_t)nf, "activation scratch"))) return rc;
@@ -440,8 +440,9 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.page_table = kv->page_table;
     float *f = fs;
     auto take = [&](int64_t n) { float *r = n ? f : nullptr; f += n; return r; };
-    d.x = take(2 * hp.n_x); d.xmid = take(2 * hp.n_xmid); d.q = take(hp.n_q); d.k = take(hp.n_k);
-    d.v = take(hp.n_k); d.part = take(hp.n_part); d.attn = take(2 * hp.n_attn);
+    d.x = take(2 * hp.n_x); d.xmid = take(2 * hp.n_xmid); d.q = take(2 * hp.n_q);
+    d.k = take(2 * hp.n_k); d.v = take(2 * hp.n_k); d.part = take(hp.n_part);
+    d.attn = take(2 * hp.n_attn);
     d.h = take(2 * hp.n_h);
     d.rl = take(hp.n_rl); d.tk_w = take(hp.n_tk); d.he = take(hp.n_he);
     d.amax_v = take(hp.n_amax);

@@ -658,6 +658,30 @@ DEV u32x4 wait_pairs(Smem &sm, CP &d, const CallArgs &ca, const TD &t,
   return v;
 }
 
+// Value of element i of a tagged vector, loaded until it carries this step's
+// tag (or the step is abandoned: sm.imisc[2] = tag).
+DEV float ldt_wait(Smem &sm, CP &d, const CallArgs &ca, const TD &t, const float *pairs, size_t i) {
+  const AS1 uint64_t *p = (const AS1 uint64_t *)pairs + i;
+  uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((uint32_t)(v >> 32) != ca.tag) {
+    const uint64_t t0 = wall_clock64();
+    while ((uint32_t)(v >> 32) != ca.tag) {
+      if (error_set(d)) {
+        sm.imisc[2] = (int)ca.tag;
+        break;
+      }
+      if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
+        set_error(d, DEVERR_TIMEOUT, t.gidx, -4, (uint32_t)(v >> 32), ca.tag);
+        sm.imisc[2] = (int)ca.tag;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  return __uint_as_float((uint32_t)v);
+}
+
 // Stage nb rows of a tagged vector into LDS exactly as stage_x does (x*g,
 // then 1/rms).  The tags stand in for the dependency wait: the rows are
 // complete once every element carries this step's tag.  Returns false (in
@@ -886,7 +910,10 @@ DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const float *rsum
       case OP_EGATEUP:
         sta(t.dst + e, silu(y) * at(bi, i, 1));
         break;
-      default:  // QKV, ROUTER
+      case OP_QKV:  // tagged
+        stt(t.dst, e, y, ca.tag);
+        break;
+      default:  // ROUTER
         sta(t.dst + e, y);
         break;
     }
@@ -1427,10 +1454,10 @@ DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, const MGeo &g, const 
       const size_t e = (size_t)b * os + i;
       if (op == OP_GATEUP)
         stt(t.dst, e, silu(y) * y_at(R + i, b), ca.tag);
-      else if (op == OP_OPROJ || op == OP_DOWN)
-        stt(t.dst, e, a[u] + y, ca.tag);
+      else if (op == OP_OPROJ || op == OP_DOWN || op == OP_QKV)
+        stt(t.dst, e, a[u] + y, ca.tag);  // QKV adds zero
       else
-        sta(t.dst + e, y);  // QKV, ROUTER
+        sta(t.dst + e, y);  // ROUTER
     }
   }
 }
@@ -1618,8 +1645,8 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     if (npw > 1) load_page(pid, 1, kB, vB);
   }
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
-  trace_start(d, t);
   if (!pos_ok) {
+    trace_start(d, t);
     if (pos >= d.max_pos && tid == 0)
       set_error(d, DEVERR_BAD_INPUT, tix, -1, (uint32_t)pos, (uint32_t)d.max_pos);
     if (S == 1 && persistent) trace_finish(d, t);  // before the (tagged) outputs
@@ -1639,10 +1666,12 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
   const float *cs = d.rope_cos + (size_t)pos * (HD / 2);
   const float *sn = d.rope_sin + (size_t)pos * (HD / 2);
-  const float *qg = d.q + head0 * HD;
+  // q, k, v are tagged: the loads double as the wait for the projections
+  const size_t q0 = head0 * HD;
   for (int idx = tid; idx < G * HD; idx += kThreads) {
     const int h = idx / HD, i = idx - h * HD, i0 = i & (HD / 2 - 1);
-    const float a = lda(qg + h * HD + i0), c2 = lda(qg + h * HD + i0 + HD / 2);
+    const float a = ldt_wait(sm, d, ca, t, d.q, q0 + h * HD + i0);
+    const float c2 = ldt_wait(sm, d, ca, t, d.q, q0 + h * HD + i0 + HD / 2);
     const float cv = ldg(cs + i0), sv = ldg(sn + i0);
     const float r = (i < HD / 2) ? a * cv - c2 * sv : a * sv + c2 * cv;
     qs[h * QROW + (i / (HD / 4)) * QQ + (i & (HD / 4 - 1))] = r * scale;
@@ -1654,10 +1683,11 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     if (!pg_ok && tid == 0) set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pg, (uint32_t)d.npages);
     for (int i = tid; i < HD; i += kThreads) {
       const int i0 = i & (HD / 2 - 1);
-      const float a = lda(d.k + kvo + i0), c2 = lda(d.k + kvo + i0 + HD / 2);
+      const float a = ldt_wait(sm, d, ca, t, d.k, kvo + i0);
+      const float c2 = ldt_wait(sm, d, ca, t, d.k, kvo + i0 + HD / 2);
       const float cv = ldg(cs + i0), sv = ldg(sn + i0);
       const float kr = (i < HD / 2) ? a * cv - c2 * sv : a * sv + c2 * cv;
-      const uint16_t kb = f2bf(kr), vb = f2bf(lda(d.v + kvo + i));
+      const uint16_t kb = f2bf(kr), vb = f2bf(ldt_wait(sm, d, ca, t, d.v, kvo + i));
       kc[i] = bf1(kb);
       vc[i] = bf1(vb);
       if (pg_ok) {
@@ -1669,6 +1699,8 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     }
   }
   __syncthreads();
+  if (sm.imisc[2] == (int)ca.tag) return false;  // projections never arrived
+  trace_start(d, t);  // inputs complete
   trace_mark(d, t, 0);
 
   // --- page loop

@@ -122,7 +122,7 @@ struct DevPlan {
   uint16_t *k_pool, *v_pool;
   const int32_t *page_table;
   // scratch (fp32 unless noted); layouts in planner.cpp
-  float *x, *xmid, *q, *k, *v, *part, *attn, *h;   // x, xmid, attn, h: tagged pairs
+  float *x, *xmid, *q, *k, *v, *part, *attn, *h;   // all but part: tagged pairs
   float *rl, *tk_w, *he, *amax_v;
   int32_t *tk_ids, *amax_i;
   const float *rope_cos, *rope_sin;                     // [max_pos][hd/2]
@@ -151,7 +151,8 @@ struct CallArgs {
 };
 
 // Tagged activations.  The vectors that one operation writes and the next
-// reads in full (x, xmid, attn, h) hold (value, tag) pairs: each element is
+// reads in full (x, xmid, attn, h; q, k, v for attention) hold (value, tag)
+// pairs: each element is
 // one 8-byte store of its fp32 value and the step's tag, so a reader that
 // sees the current tag has the value too.  An edge into a task that reads
 // such a vector is a data edge: the reader loads until every tag is

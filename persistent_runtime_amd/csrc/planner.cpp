@@ -324,7 +324,10 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   for (int l = 0; l < L; ++l) {
     // QKV, group by group so a KV head's attention can start early
     std::vector<int> grp(nkv);
-    for (int g = 0; g < nkv; ++g) grp[g] = b.ev();
+    for (int g = 0; g < nkv; ++g) {
+      grp[g] = b.ev();
+      data_ev.push_back(grp[g]);  // q, k, v are tagged
+    }
     b.begin_phase();
     {
       std::vector<RowSeg> segs;
