@@ -398,7 +398,8 @@ def main():
         log(f"[bench] kernel-per-op: {kms:.3f} ms/step ({kpo['launches_per_step']} launches)")
         plan_k.free()
         # the same launches captured once in a HIP graph and replayed
-        gms = kpo_graph_ms(build, start, tok_ring, pos_all, n, stream, torch)
+        # the graph's eager warm-up takes position 0, its replays 1..n_g
+        gms = kpo_graph_ms(build, start, tok_ring, pos_all, min(n, W_ + K_ - 1), stream, torch)
         kpo["graph_ms_per_step"] = round(gms, 4)
         kpo["persistent_speedup_vs_graph"] = round(gms / ms_step, 3)
         log(f"[bench] kernel-per-op in a HIP graph: {gms:.3f} ms/step")

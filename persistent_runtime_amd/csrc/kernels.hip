@@ -335,6 +335,10 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws)
         }
       }
     }
+    // Matrix-core plans read their inputs through the L2 (every CU of an
+    // XCD stages the same activations): acquire at agent scope, which
+    // drops lines the XCD's L2 may hold from before the producers wrote.
+    if (ok && d.mfma) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     sm.imisc[0] = ok;
   }
   __syncthreads();
@@ -1348,8 +1352,11 @@ DEV void mx_load(CP &d, const MGeo &g, const TD &t, int p, XStage &xs) {
     xs.g[q] = t.gain ? ldg((const u32x4 *)(t.gain + col))
                      : (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
     const uint32_t off = (uint32_t)(((size_t)b * g.K + col) * 8);
+    // cached loads: the task's dependency wait ended with an agent-scope
+    // acquire (persistent) or the launch boundary did (kernel-per-op)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) xs.v[q][m] = __builtin_bit_cast(u32x4, lda4(r, off + 16 * m));
+    for (int m = 0; m < 4; ++m)
+      xs.v[q][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * m, 0, 0));
   }
 }
 DEV void mx_store(Smem &sm, CP &d, const MGeo &g, int p, int pb, const XStage &xs,
