@@ -69,8 +69,8 @@ struct mk_plan {
   int32_t *stage_tok = nullptr, *stage_pos = nullptr, *stage_next = nullptr;
   float *stage_logits = nullptr;
   uint32_t *ctrl = nullptr;  // CTRL_WORDS control words, the event counters, then
-                             // the split-attention arrival counters
-  int n_att_cnt = 0;
+                             // the split-attention and split-K arrival counters
+  int n_att_cnt = 0;         // arrival counters (both kinds)
   int n_ctrl_words = 0;
 
   ~mk_plan() {
@@ -365,6 +365,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     int32_t max_thr = 1;
     for (int32_t v : hp.ev_thr) max_thr = std::max(max_thr, v);
     max_thr = std::max(max_thr, hp.S);  // split-attention arrival counters
+    max_thr = std::max(max_thr, kMaxKSplit);  // split-K arrival counters
     p->epoch_limit = (uint32_t)(((1u << 31) - 1u) / (uint32_t)max_thr) - 2u;
 
     // device allocations
@@ -373,11 +374,12 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     int32_t *d_wq;
     if ((rc = p->alloc(&d_wq, hp.worker_off.size() + hp.worker_list.size(), "worker queues")))
       return rc;
-    p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads;
+    p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads + hp.n_kcnt;
     p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
+    const int64_t n_kpart = hp.n_kpart * kpart_slot(B);
     const int64_t nf = 2 * (hp.n_x + hp.n_xmid + hp.n_attn + hp.n_h + hp.n_q + 2 * hp.n_k) + hp.n_part +
-                       hp.n_rl + hp.n_tk + hp.n_he + hp.n_amax;
+                       hp.n_rl + hp.n_tk + hp.n_he + hp.n_amax + n_kpart;
     float *fs;
     if ((rc = p->alloc(&fs, (size_t)nf, "activation scratch"))) return rc;
     int32_t *is;
@@ -446,6 +448,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.h = take(2 * hp.n_h);
     d.rl = take(hp.n_rl); d.tk_w = take(hp.n_tk); d.he = take(hp.n_he);
     d.amax_v = take(hp.n_amax);
+    d.kpart = take(n_kpart);
     d.tk_ids = hp.n_tk ? is : nullptr;
     d.amax_i = is + hp.n_tk;
     p->stage_tok = is + hp.n_tk + hp.n_amax;
@@ -456,6 +459,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.ctrl = p->ctrl;
     d.ev = p->ctrl + CTRL_WORDS;
     d.att_cnt = d.ev + E;
+    d.kcnt = d.att_cnt + c.n_layers * c.max_batch * c.n_kv_heads;
     d.tasks = d_tasks;
     d.n_tasks = T;
     d.worker_off = d_wq;

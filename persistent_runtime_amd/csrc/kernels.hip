@@ -1227,15 +1227,20 @@ DEV bool down_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
+// A matrix-core tile: NGs 16-row groups per matrix (nseg matrices) times K
+// columns starting at column k0 of rows ld elements long (split-K tiles
+// cover part of the row; s0/s1 point at column k0 of the first row).
 struct MGeo {
   const uint16_t *s0, *s1;
-  int K, NGs, nseg, Ks, nkb, P, B16;
+  int K, NGs, nseg, Ks, nkb, P, B16, ld, k0;
 };
-DEV MGeo mgeo(const uint16_t *w0, const uint16_t *w1, int rows, int K, int B) {
+DEV MGeo mgeo(const uint16_t *w0, const uint16_t *w1, int rows, int K, int B, int ld, int k0) {
   MGeo g;
-  g.s0 = w0;
-  g.s1 = w1;
+  g.s0 = w0 + k0;
+  g.s1 = w1 ? w1 + k0 : nullptr;
   g.K = K;
+  g.ld = ld;
+  g.k0 = k0;
   g.NGs = rows >> 4;
   g.nseg = w1 ? 2 : 1;
   g.B16 = (B + 15) >> 4;
@@ -1248,7 +1253,12 @@ DEV MGeo mgeo(const uint16_t *w0, const uint16_t *w1, int rows, int K, int B) {
   g.P = (K + ks - 1) / ks;
   return g;
 }
-DEV MGeo mgeo_of(CP &d, const TD &t) { return mgeo(t.w0, t.w1, t.a2, t.K, d.B); }
+// Split-K tiles carry rpp = kc | rb << 16 with kc < K; whole-row tiles rpp = K.
+DEV int ksplit_kc(int rpp, int K) { return min(rpp & 0xffff, K); }
+DEV MGeo mgeo_of(CP &d, const TD &t) {
+  const int kc = ksplit_kc(t.rpp, t.K);
+  return mgeo(t.w0, t.w1, t.a2, min(kc, t.K - t.a3), d.B, t.K, t.a3);
+}
 
 // matrix and row slot of wave cw's gi-th group; false when it has none
 DEV bool mgroup(const MGeo &g, int cw, int gi, int &seg, int &slot) {
@@ -1274,7 +1284,7 @@ DEV uint64_t maddr(const MGeo &g, int cw, int j, int p) {
   const uint16_t *base = ok && seg ? g.s1 : g.s0;
   const int row = (ok ? slot * 16 : 0) + (lane & 15);
   const int col = (ok ? k : 0) + 8 * (lane >> 4);
-  return (uint64_t)(base + (size_t)row * g.K + col);
+  return (uint64_t)(base + (size_t)row * g.ld + col);
 }
 DEV uint64_t maddr_any(const MGeo &g, int cw, int j, int p) {
   return g.nkb >= 16 ? maddr<16>(g, cw, j, p) : maddr<8>(g, cw, j, p);
@@ -1324,61 +1334,61 @@ DEV void mpass(const MGeo &g, Buf &w, f32x4 (&acc)[2][4], const char *xb, int cw
   }
 }
 
-// Staging of slice p of the activations (all slots) into LDS buffer pb, by
-// all eight waves: the slice's units (k-block kb, 16-slot tile st) are dealt
-// round-robin over the waves, at most four per wave.  A unit is 64 lanes x 8
-// columns of one slot (lane l: slot st*16 + l%16, columns 8(l/16)..+8 of the
-// k-block), times the gain, stored as bf16 value + bf16 remainder in the B
-// layout.  Every load is issued (out-of-range units read unit 0 and are not
-// stored), which keeps the compiler's waits per load instead of for the
-// whole queue.
-struct XStage {
-  u32x4 v[4][4];   // 8 (value, tag) pairs per unit
-  u32x4 g[4];
+// Staging of slice p of the activations (all slots) into LDS buffer pb.  A
+// unit is 64 lanes x 8 columns of one slot (lane l: slot st*16 + l%16,
+// columns 8(l/16)..+8 of k-block kb), times the gain, stored as bf16 value +
+// bf16 remainder in the B layout.  Every load is issued (units beyond the
+// slice read unit 0 and are not stored), which keeps the compiler's waits
+// per load instead of for the whole queue.
+template <int NQ> struct XStage {
+  uint32_t v[NQ][8];   // the 8 values of a unit (their tags are not read)
+  u32x4 g[NQ];
 };
 DEV int mx_units(const MGeo &g, int p) { return (min(g.Ks, g.K - p * g.Ks) >> 5) * g.B16; }
-DEV void mx_load(CP &d, const MGeo &g, const TD &t, int p, XStage &xs) {
-  const int lane = tidx() & 63, wave = uni(tidx() >> 6);
+// Units u0 .. u0+NQ-1 of slice p.
+template <int NQ>
+DEV void mx_load(CP &d, const MGeo &g, const TD &t, int p, int u0, XStage<NQ> &xs) {
+  const int lane = tidx() & 63;
   const int nu = mx_units(g, p), B = d.B;
   const __amdgpu_buffer_rsrc_t r = rsrc(t.src);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int u = wave + kWaves * q;
+  for (int q = 0; q < NQ; ++q) {
+    int u = u0 + q;
     u = u < nu ? u : 0;
     const int kb = u / g.B16, st = u - kb * g.B16;
-    const int col = p * g.Ks + kb * 32 + 8 * (lane >> 4);
+    const int col = g.k0 + p * g.Ks + kb * 32 + 8 * (lane >> 4);
     int b = st * 16 + (lane & 15);
     b = b < B ? b : 0;
     xs.g[q] = t.gain ? ldg((const u32x4 *)(t.gain + col))
                      : (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-    const uint32_t off = (uint32_t)(((size_t)b * g.K + col) * 8);
-    // cached loads: the task's dependency wait ended with an agent-scope
-    // acquire (persistent) or the launch boundary did (kernel-per-op)
+    const uint32_t off = (uint32_t)(((size_t)b * g.ld + col) * 8);
+    // cached loads of the values alone: the task's dependency wait ended
+    // with an agent-scope acquire (persistent) or the launch boundary did
+    // (kernel-per-op), and matrix-core plans do not check tags
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      xs.v[q][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * m, 0, 0));
+    for (int e = 0; e < 8; ++e) xs.v[q][e] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 8 * e, 0, 0);
   }
 }
-DEV void mx_store(Smem &sm, CP &d, const MGeo &g, int p, int pb, const XStage &xs,
+template <int NQ>
+DEV void mx_store(Smem &sm, CP &d, const MGeo &g, int p, int pb, int u0, const XStage<NQ> &xs,
                   float (&ssl)[4]) {
-  const int lane = tidx() & 63, wave = uni(tidx() >> 6);
+  const int lane = tidx() & 63;
   const int nu = mx_units(g, p), B16 = g.B16;
   char *xb = (char *)sm.xs + pb * (g.nkb * B16 * 2048);
   char *xlo = xb + g.nkb * B16 * 1024;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int u = wave + kWaves * q;
+  for (int q = 0; q < NQ; ++q) {
+    const int u = u0 + q;
     if (u >= nu) break;
     const int kb = u / B16, st = u - kb * B16;
     const bool live = st * 16 + (lane & 15) < d.B;
     const u32x4 gq = xs.g[q];
     const f32x8 gf = {bf_lo(gq.x), bf_hi(gq.x), bf_lo(gq.y), bf_hi(gq.y),
                       bf_lo(gq.z), bf_hi(gq.z), bf_lo(gq.w), bf_hi(gq.w)};
-    // (matrix-core batches keep the counters: the tags are current here)
-    f32x8 x = {__uint_as_float(xs.v[q][0].x), __uint_as_float(xs.v[q][0].z),
-               __uint_as_float(xs.v[q][1].x), __uint_as_float(xs.v[q][1].z),
-               __uint_as_float(xs.v[q][2].x), __uint_as_float(xs.v[q][2].z),
-               __uint_as_float(xs.v[q][3].x), __uint_as_float(xs.v[q][3].z)};
+    f32x8 x = {__uint_as_float(xs.v[q][0]), __uint_as_float(xs.v[q][1]),
+               __uint_as_float(xs.v[q][2]), __uint_as_float(xs.v[q][3]),
+               __uint_as_float(xs.v[q][4]), __uint_as_float(xs.v[q][5]),
+               __uint_as_float(xs.v[q][6]), __uint_as_float(xs.v[q][7])};
     x = live ? x : (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
 #pragma unroll
@@ -1392,6 +1402,16 @@ DEV void mx_store(Smem &sm, CP &d, const MGeo &g, int p, int pb, const XStage &x
     const int o = ((kb * B16 + st) * 64 + lane) * 16;
     *(bf16x8 *)(xb + o) = h;
     *(bf16x8 *)(xlo + o) = lo;
+  }
+}
+// Control wave: the whole slice, eight units per round.  The compute waves
+// never wait for these loads: their queues hold weight loads only.
+DEV void mx_stage(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb, float (&ssl)[4]) {
+  const int nu = mx_units(g, p);
+  for (int u0 = 0; u0 < nu; u0 += 8) {
+    XStage<8> xs;
+    mx_load<8>(d, g, t, p, u0, xs);
+    mx_store<8>(sm, d, g, p, pb, u0, xs, ssl);
   }
 }
 // Every wave's sums of squares to LDS (sm.red as [wave][lane][tile]); after
@@ -1409,16 +1429,18 @@ DEV void mss_rms(Smem &sm, CP &d, const MGeo &g, float *rs) {
     float s = 0.f;
     for (int w = 0; w < kWaves; ++w)
       for (int m = 0; m < 4; ++m) s += src[w * 64 + m * 16 + l16][st];
-    rs[lane] = 1.0f / sqrtf(s / (float)g.K + d.eps);
+    rs[lane] = 1.0f / sqrtf(s / (float)g.ld + d.eps);
   }
 }
 
-// Control wave: outputs of a matrix-core task from out[row][slot] (LDS),
-// scaled by the slots' 1/rms (rs) when the input was normalised.
-DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, const MGeo &g, const float *out,
-                   const float *rs) {
+// Control wave: outputs of rows r0 .. r0+R of a matrix-core task from
+// out[row][slot] (LDS, Bp slots per row; gate/up: the R gate rows, then the
+// same up rows), scaled by the slots' 1/rms (rs) when the input was
+// normalised.
+DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, int R, int Bp, int r0,
+                   const float *out, const float *rs) {
   const int lane = tidx() & 63;
-  const int R = g.NGs * 16, Bp = g.B16 * 16, B = d.B, op = t.op;
+  const int B = d.B, op = t.op;
   const size_t os = (size_t)t.ostride;
   auto y_at = [&](int row, int b) { return out[row * Bp + b] * (t.gain ? rs[b] : 1.f); };
   if (op == OP_LMHEAD) {
@@ -1449,7 +1471,7 @@ DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, const MGeo &g, const 
       a[u] = 0.f;
       if ((op == OP_OPROJ || op == OP_DOWN) && idx < n) {
         const int b = idx / R, i = idx - b * R;
-        a[u] = ldv(t.aux, (size_t)b * os + i);
+        a[u] = ldv(t.aux, (size_t)b * os + r0 + i);
       }
     }
 #pragma unroll
@@ -1458,7 +1480,7 @@ DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, const MGeo &g, const 
       if (idx >= n) break;
       const int b = idx / R, i = idx - b * R;
       const float y = y_at(i, b);
-      const size_t e = (size_t)b * os + i;
+      const size_t e = (size_t)b * os + r0 + i;
       if (op == OP_GATEUP)
         stt(t.dst, e, silu(y) * y_at(R + i, b), ca.tag);
       else if (op == OP_OPROJ || op == OP_DOWN || op == OP_QKV)
@@ -1469,30 +1491,157 @@ DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, const MGeo &g, const 
   }
 }
 
+// ---- split-K matrix-core tiles ---------------------------------------------
+// The ns tiles of a row block (column ranges ks = 0..ns-1) each publish
+// their products [row][slot] and the slots' sums of squares over their
+// columns into the partial slot (rb, ks), then count themselves on the
+// block's arrival counter.  Once all ns have arrived, tile ks adds up rows
+// [ks*Rs, (ks+1)*Rs) of every matrix (Rs = ceil(rows / ns)) over the ns
+// slots in split order (deterministic) and writes them as the operation's
+// output; every tile reports its completion after its own rows.
+struct KSplit {
+  int ns, ks, rb, kc;
+};
+DEV KSplit ksplit_of(const TD &t) {
+  KSplit k;
+  k.kc = ksplit_kc(t.rpp, t.K);
+  k.ns = (t.K + k.kc - 1) / k.kc;
+  k.ks = t.a3 / k.kc;
+  k.rb = (t.rpp >> 16) & 0x7fff;
+  return k;
+}
+DEV float *kslot(CP &d, const KSplit &k, int ks) {
+  return d.kpart + ((size_t)k.rb * k.ns + ks) * (size_t)kpart_slot(d.B);
+}
+DEV void ksplit_rows(const MGeo &g, const KSplit &k, int &lo, int &nr) {
+  const int R = g.NGs * 16, rs = (R + k.ns - 1) / k.ns;
+  lo = min(R, k.ks * rs);
+  nr = min(R, lo + rs) - lo;
+}
+// sum of squares of slot `lane` over the tile's columns (lane < 16 * B16)
+DEV float mss_sum(Smem &sm, const MGeo &g, int lane) {
+  const f32x4 *src = (const f32x4 *)&sm.red[0][0];
+  const int st = lane >> 4, l16 = lane & 15;
+  float s = 0.f;
+  for (int w = 0; w < kWaves; ++w)
+    for (int m = 0; m < 4; ++m) s += src[w * 64 + m * 16 + l16][st];
+  return s;
+}
+// Control wave: the tile's products (LDS out[row][slot]) and sums of squares
+// to its partial slot, with coherent stores.
+DEV void ksplit_publish(Smem &sm, CP &d, const MGeo &g, const KSplit &k) {
+  const int lane = tidx() & 63, Bp = g.B16 * 16;
+  float *slot = kslot(d, k, k.ks);
+  const __amdgpu_buffer_rsrc_t r = rsrc(slot);
+  const f32x4 *src = (const f32x4 *)sm.xs;
+  const int n4 = g.nseg * g.NGs * 16 * Bp / 4;
+  for (int u = lane; u < n4; u += 64)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, src[u]), r, (uint32_t)u * 16u,
+                                           0, kCpolSc1);
+  if (lane < Bp) sta(slot + (size_t)kMfmaGroups * 16 * Bp + lane, mss_sum(sm, g, lane));
+}
+// Every wave: count this tile (thread 0, after the control wave drained its
+// stores) and wait until the block's ns tiles have arrived.  False when the
+// step is abandoned.
+DEV bool ksplit_arrive(Smem &sm, CP &d, const CallArgs &ca, const TD &t, const KSplit &k) {
+  if (tidx() == 0) {
+    uint32_t *c = d.kcnt + t.a4;
+    const uint32_t want = (ca.epoch + 1u) * (uint32_t)k.ns;
+    uint32_t seen =
+        __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    int ok = 1;
+    if ((int32_t)(seen - want) < 0) {
+      const uint64_t t0 = wall_clock64();
+      for (;;) {
+        __builtin_amdgcn_s_sleep(1);
+        seen = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int32_t)(seen - want) >= 0) break;
+        if (error_set(d)) { ok = 0; break; }
+        if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
+          set_error(d, DEVERR_TIMEOUT, t.gidx, -5, seen, want);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    sm.imisc[0] = ok;
+  }
+  __syncthreads();
+  return sm.imisc[0] != 0;
+}
+// Every wave: rows [lo, lo+nr) of each matrix of the block summed over the
+// ns partial slots into out[(m*nr + r)][slot], the sums of squares into
+// ss[slot]; 16 bytes (4 slots) per thread and slot, loads issued 8 at a time.
+DEV void ksplit_reduce(CP &d, const MGeo &g, const KSplit &k, int lo, int nr, float *out,
+                       float *ss) {
+  const int Bp = g.B16 * 16, c4 = Bp / 4, R = g.NGs * 16;
+  const int nrow = g.nseg * nr * c4;
+  const int nu = nrow + c4;
+  const uint32_t slot_b = (uint32_t)kpart_slot(d.B) * 4u;
+  const __amdgpu_buffer_rsrc_t r = rsrc(kslot(d, k, 0));
+  for (int u = tidx(); u < nu; u += kThreads) {
+    uint32_t off;
+    float *dst;
+    if (u < nrow) {
+      const int m = u / (nr * c4), rem = u - m * nr * c4, rr = rem / c4, c = rem - rr * c4;
+      off = (uint32_t)(((m * R + lo + rr) * Bp + 4 * c) * 4);
+      dst = out + (m * nr + rr) * Bp + 4 * c;
+    } else {
+      const int c = u - nrow;
+      off = (uint32_t)((kMfmaGroups * 16 * Bp + 4 * c) * 4);
+      dst = ss + 4 * c;
+    }
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k.ns; j0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int jj = j0 + j < k.ns ? j0 + j : 0;
+        v[j] = lda4(r, off + (uint32_t)jj * slot_b);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j0 + j < k.ns) a = j0 + j == 0 ? v[j] : a + v[j];
+    }
+    *(f32x4 *)dst = a;
+  }
+}
+
 DEV bool gemv_mfma_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
                        WState &ws) {
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   trace_start(d, t);
   const MGeo g = mgeo_of(d, t);
   float ssl[4] = {0.f, 0.f, 0.f, 0.f};
-  XStage xs;
-  mx_load(d, g, t, 0, xs);
-  mx_store(sm, d, g, 0, 0, xs, ssl);
+  mx_stage(sm, d, g, t, 0, 0, ssl);
   trace_mark(d, t, 0);
   __syncthreads();  // slice 0 staged
   for (int p = 0; p < g.P; ++p) {
-    if (p + 1 < g.P) {
-      mx_load(d, g, t, p + 1, xs);
-      mx_store(sm, d, g, p + 1, (p + 1) & 1, xs, ssl);
-    }
+    if (p + 1 < g.P) mx_stage(sm, d, g, t, p + 1, (p + 1) & 1, ssl);
     __syncthreads();  // pass p done, slice p + 1 staged
   }
   mss_publish(sm, ssl);
   __syncthreads();  // accumulators and sums of squares in LDS
   trace_mark(d, t, 1);
   float *rs = &sm.rows[0][0];
-  if (t.gain) mss_rms(sm, d, g, rs);  // this wave's own LDS writes: no barrier needed
-  mepilogue(d, ca, t, g, sm.xs, rs);
+  const int Bp = g.B16 * 16;
+  const KSplit k = ksplit_of(t);
+  if (k.ns > 1) {
+    ksplit_publish(sm, d, g, k);
+    vm_drain();
+    if (!ksplit_arrive(sm, d, ca, t, k)) return false;  // every tile's partial published
+    int lo, nr;
+    ksplit_rows(g, k, lo, nr);
+    float *red = sm.xs + kMfmaGroups * 16 * 64, *ss = &sm.rows[1][0];
+    ksplit_reduce(d, g, k, lo, nr, red, ss);
+    __syncthreads();  // the slice's sums in LDS
+    if (t.gain && (tidx() & 63) < Bp)
+      rs[tidx() & 63] = 1.0f / sqrtf(ss[tidx() & 63] / (float)g.ld + d.eps);
+    mepilogue(d, ca, t, nr, Bp, lo, red, rs);
+  } else {
+    if (t.gain) mss_rms(sm, d, g, rs);  // this wave's own LDS writes: no barrier needed
+    mepilogue(d, ca, t, g.NGs * 16, Bp, 0, sm.xs, rs);
+  }
   if (persistent) {
     if (t.a5 > 0) vm_drain();
     trace_finish(d, t);
@@ -1514,25 +1663,15 @@ DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float ssl[4] = {0.f, 0.f, 0.f, 0.f};
-  XStage xs;
-  mx_load(d, g, t, 0, xs);
-  mx_store(sm, d, g, 0, 0, xs, ssl);
+  const float ssl[4] = {0.f, 0.f, 0.f, 0.f};  // the control wave stages the activations
   __syncthreads();  // slice 0 staged
   for (int p = 0; p < g.P; ++p) {
     const char *xb = (const char *)sm.xs + (p & 1) * (g.nkb * g.B16 * 2048);
-    const bool more = p + 1 < g.P;
     if (g.nkb >= 16)
       mpass<16>(g, w, acc, xb, cw, p, pre, gn);
     else
       mpass<8>(g, w, acc, xb, cw, p, pre, gn);
-    // the next slice's loads queue behind this pass's refills (the next
-    // pass's weights), so they arrive with them
-    if (more) {
-      mx_load(d, g, t, p + 1, xs);
-      mx_store(sm, d, g, p + 1, (p + 1) & 1, xs, ssl);
-    }
-    __syncthreads();  // pass p done, slice p + 1 staged
+    __syncthreads();  // pass p done, slice p + 1 staged (by the control wave)
   }
   mss_publish(sm, ssl);
   // accumulators to out[row][slot]: row = matrix*NGs*16 + slot*16 + 4(l/16) + e
@@ -1552,6 +1691,14 @@ DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
     }
   }
   __syncthreads();  // accumulators and sums of squares in LDS
+  const KSplit k = ksplit_of(t);
+  if (k.ns > 1) {
+    if (!ksplit_arrive(sm, d, ca, t, k)) return false;
+    int lo, nr;
+    ksplit_rows(g, k, lo, nr);
+    ksplit_reduce(d, g, k, lo, nr, sm.xs + kMfmaGroups * 16 * 64, &sm.rows[1][0]);
+    __syncthreads();  // the slice's sums in LDS
+  }
   __syncthreads();  // outputs written: LDS free for the next task
   ws.x_src = nullptr;
   return true;
@@ -1563,10 +1710,12 @@ DEV bool next_mgeo(CP &d, const uint32_t *slot, MGeo &g) {
   const int op = (int)(int16_t)(uni((int)slot[0]) & 0xffff);
   if (!static_weights(op)) return false;
   const int rows = uni((int)slot[4]);
+  const int k0 = uni((int)slot[5]);
   const uint16_t *w0 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[16]), (uint32_t)uni((int)slot[17]));
   const uint16_t *w1 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[18]), (uint32_t)uni((int)slot[19]));
   const int K = uni((int)slot[28]);
-  g = mgeo(w0, w1, rows, K, d.B);
+  const int kc = ksplit_kc(uni((int)slot[31]), K);
+  g = mgeo(w0, w1, rows, min(kc, K - k0), d.B, K, k0);
   return true;
 }
 

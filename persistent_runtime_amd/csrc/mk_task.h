@@ -36,6 +36,7 @@ constexpr int kMaxPass = 8;
 // matrix-core tiles: 16-row groups, at most kMfmaGroups per task.
 constexpr int kMfmaGroups = 14;
 constexpr int kMfmaMaxBatch = 64;
+constexpr int kMaxKSplit = 16;          // column ranges per split-K matrix-core row block
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
 constexpr int kLdsXBytes = 128 * 1024; // budget for staged activations
 
@@ -130,6 +131,8 @@ struct DevPlan {
   uint32_t *ev;            // event counters, after CTRL_WORDS control words
   uint32_t *att_cnt;       // split-attention arrivals per (layer, slot, KV head),
                            // after the event counters; monotonic like them
+  uint32_t *kcnt;          // split-K arrivals per matrix-core row block, after att_cnt
+  float *kpart;            // split-K partial products, kpart_slot(B) floats per tile
   uint32_t *ctrl;
   const Task *tasks;           // worker-major: each worker's queue is contiguous
   int32_t n_tasks;
@@ -163,5 +166,9 @@ constexpr int32_t kDataEdge = 1 << 30;
 
 // scratch sizes (elements), shared by planner and device code
 inline int64_t part_stride(int hd) { return hd + 4; }  // o[hd], m, l, pad
+// floats per split-K partial slot: the products of one matrix-core tile (at
+// most kMfmaGroups groups of 16 rows) for the padded batch, [row][slot],
+// then the slots' partial sums of squares
+constexpr int64_t kpart_slot(int B) { return (int64_t)(kMfmaGroups * 16 + 1) * ((B + 15) / 16 * 16); }
 
 }  // namespace mk

@@ -151,6 +151,81 @@ struct RowSeg {
   int a3 = 0; // expert gate/up: expert slot
 };
 
+// Matrix-core lowering of a static-weight GEMV for a batch of 16..64 slots.
+// A tile is a block of whole 16-row groups (at most kMfmaGroups; gate/up: at
+// most half of them per matrix) times a range of K.  Every slot's
+// activations are read by every tile that covers their columns, so the
+// operation is cut along K as well (split-K): with NB row blocks, each block
+// is split into ns column ranges, NB * ns <= n_workers, so that a tile's
+// activation slice is not much larger than its weights.  The ns tiles of a
+// block leave their partial products in a shared buffer; each then waits for
+// its siblings (an arrival counter per block) and adds up, in split order,
+// one ns-th of the block's rows, which it writes as the operation's output.
+// Task fields: a1 = first row, a2 = rows (per matrix), a3 = first column k0,
+// rpp = kc | rb << 16 (columns per split, block index within the
+// operation), a4 = the block's arrival counter (LM head: tile index; it is
+// never split).  Tiles are placed one per worker, those of one column range
+// on one XCD where possible (worker w runs on XCD w % 8), so the XCD's L2
+// holds that slice of the activations for all of them.
+static int add_gemv_mfma(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int K,
+                         int nseg, int n_workers, int wait_ev, int64_t extra_bytes,
+                         int *lm_index) {
+  const int Rmax = (nseg == 2 ? kMfmaGroups / 2 : kMfmaGroups) * 16;
+  struct Block { size_t seg; int row0, rows; };
+  std::vector<Block> blocks;
+  for (size_t i = 0; i < segs.size(); ++i) {
+    const int rows = segs[i].rows;
+    if (rows % 16) return -1;
+    const int g = rows / 16, nb = (rows + Rmax - 1) / Rmax;
+    for (int k = 0; k < nb; ++k) {
+      const int g0 = (int)((int64_t)g * k / nb), g1 = (int)((int64_t)g * (k + 1) / nb);
+      blocks.push_back({i, segs[i].row0 + 16 * g0, 16 * (g1 - g0)});
+    }
+  }
+  const int NB = (int)blocks.size();
+  const int64_t row_bytes = (int64_t)nseg * K * 2;
+  int ns = 1;
+  if (op != OP_LMHEAD && NB < n_workers)
+    ns = std::max(1, std::min({n_workers / NB, K / 256, kMaxKSplit}));
+  int kc = (K + ns - 1) / ns;
+  kc = (kc + 31) / 32 * 32;
+  ns = (K + kc - 1) / kc;
+  if (ns > 1) {
+    if (kc > 0xffff || NB > 0x7fff) return -1;
+    b.p.n_kpart = std::max<int64_t>(b.p.n_kpart, (int64_t)NB * ns);
+  }
+  // workers: the tiles of column range ks prefer XCD ks % 8
+  std::vector<std::vector<int>> free_w(8);
+  for (int w = n_workers - 1; w >= 0; --w) free_w[w % 8].push_back(w);
+  auto take_worker = [&](int pref) {
+    int x = pref;
+    if (free_w[x].empty())
+      for (int y = 0; y < 8; ++y)
+        if (free_w[y].size() > free_w[x].size()) x = y;
+    const int w = free_w[x].back();
+    free_w[x].pop_back();
+    return w;
+  };
+  int added = 0;
+  for (int rb = 0; rb < NB; ++rb) {
+    const Block &bl = blocks[rb];
+    const RowSeg &sg = segs[bl.seg];
+    const int cnt = ns > 1 ? b.p.n_kcnt++ : 0;
+    for (int ks = 0; ks < ns; ++ks) {
+      const int k0 = ks * kc, kw = std::min(kc, K - k0);
+      int w = -1;
+      if (ns > 1) w = take_worker(ks % 8);
+      else if (NB <= n_workers) w = rb;  // one tile per worker
+      const int a4 = ns > 1 ? cnt : (lm_index ? (*lm_index)++ : 0);
+      b.add(op, layer, sg.a0, bl.row0, bl.rows, k0, a4, {wait_ev}, {sg.sig},
+            (int64_t)bl.rows * nseg * kw * 2 + extra_bytes, w, ns > 1 ? (kc | rb << 16) : K);
+      ++added;
+    }
+  }
+  (void)row_bytes;
+  return added;
+}
+
 // Lower a static-weight GEMV operation: its rows (all of nseg * K bf16) are
 // cut into one contiguous, near-equal share per worker (the balance is in
 // bytes, as every row has the same length); a share becomes one task per
@@ -167,14 +242,8 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
   while ((row_bytes * unit) % 1024 || unit % min_unit) ++unit;
   int R = (int)((int64_t)kMaxTileUnits16 * 1024 / row_bytes);
   R -= R % unit;
-  if (b.p.mfma && op != OP_EGATEUP && op != OP_EDOWN) {
-    // matrix-core tiles: whole 16-row groups, at most kMfmaGroups per task
-    // (gate/up: at most half of them per matrix); the device streams each
-    // task along K in slices, so a task has one row pass
-    unit = 16;
-    R = (nseg == 2 ? kMfmaGroups / 2 : kMfmaGroups) * 16;
-    pmax = 1;
-  }
+  if (b.p.mfma && op != OP_EGATEUP && op != OP_EDOWN)
+    return add_gemv_mfma(b, op, layer, segs, K, nseg, n_workers, wait_ev, extra_bytes, lm_index);
   if (R < unit) return -1;
   int64_t total = 0;
   for (auto &sg : segs) total += sg.rows;

@@ -37,6 +37,11 @@ struct HostPlan {
   // scratch sizes in elements
   int64_t n_x = 0, n_xmid = 0, n_q = 0, n_k = 0, n_part = 0, n_attn = 0,
           n_h = 0, n_rl = 0, n_tk = 0, n_he = 0, n_amax = 0;
+  // split-K matrix-core tiles: arrival counters (one per row block of every
+  // split operation in the step) and partial-product slots (the most tiles
+  // of one split operation; every operation reuses them)
+  int n_kcnt = 0;
+  int64_t n_kpart = 0;
 };
 
 // Vector width (bytes per lane load) for rows of K bf16 elements, or 0 when

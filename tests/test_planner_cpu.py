@@ -33,7 +33,35 @@ def _cfg(model, B=1, maxp=64, n_pages=None):
     return mk.make_config(model, max_batch=B, max_pages_per_seq=maxp, n_pages=n_pages)
 
 
-def _check_graph(model, tasks, thr, B):
+STATIC = ("QKV", "OPROJ", "GATEUP", "DOWN", "ROUTER", "LMHEAD")
+
+
+def _kdim(model, op):
+    """Row length (input columns) of a static-weight GEMV."""
+    if op == "OPROJ":
+        return model["n_q_heads"] * model["head_dim"]
+    if op == "DOWN":
+        return model["ffn_dim"]
+    return model["hidden"]
+
+
+def _ksplit(model, t):
+    """(k0, kc, ns, ks) of a matrix-core tile (rows_per_pass = kc | rb << 16
+    for split-K tiles, the row length otherwise)."""
+    K = _kdim(model, mk.OPS[t.op])
+    kc = min(t.rows_per_pass & 0xFFFF, K)
+    ns = -(-K // kc)
+    return t.a3, kc, ns, t.a3 // kc
+
+
+def _split_rows(t, ns, ks):
+    """Rows (relative to a1) that split-K tile ks of ns writes."""
+    rs = -(-t.a2 // ns)
+    lo = min(t.a2, ks * rs)
+    return lo, min(t.a2, lo + rs)
+
+
+def _check_graph(model, tasks, thr, B, mfma=False):
     T = len(tasks)
     sig = {}
     for i, t in enumerate(tasks):
@@ -56,8 +84,16 @@ def _check_graph(model, tasks, thr, B):
     L, H = model["n_layers"], model["hidden"]
     nq, nkv, hd = model["n_q_heads"], model["n_kv_heads"], model["head_dim"]
     cover = {}
+    kcover = {}
     for t in tasks:
         op = mk.OPS[t.op]
+        if mfma and op in STATIC:
+            # matrix-core tiles: the column ranges of a row block tile the row
+            k0, kc, ns, ks = _ksplit(model, t)
+            kcover.setdefault((op, t.layer, t.a0, t.a1, t.a2), []).append(
+                (k0, min(k0 + kc, _kdim(model, op))))
+            if k0 != 0:
+                continue
         if op in ("QKV", "OPROJ", "GATEUP", "DOWN", "ROUTER", "LMHEAD", "EGATEUP", "EDOWN"):
             m = (t.a0 if op == "QKV" else (t.a0, t.a3) if op == "EGATEUP"
                  else t.a0 if op == "EDOWN" else 0)
@@ -70,11 +106,32 @@ def _check_graph(model, tasks, thr, B):
         n = (nq * hd if m == 0 else nkv * hd) if op == "QKV" else want[op]
         assert rr[0][0] == 0 and rr[-1][1] == n, (op, l, m)
         assert all(a[1] == b[0] for a, b in zip(rr, rr[1:])), (op, l, m)
+    for key, kk in kcover.items():
+        kk.sort()
+        assert kk[0][0] == 0 and kk[-1][1] == _kdim(model, key[0]), key
+        assert all(a[1] == b[0] for a, b in zip(kk, kk[1:])), key
     return sig
 
 
-def _regions(model, t, B, S):
+def _regions(model, t, B, S, mfma=False):
     """(reads, writes) of one task, as lists of (buffer, layer, slot, sub, lo, hi)."""
+    R, W = _regions_rows(model, t, B, S)
+    op = mk.OPS[t.op]
+    if mfma and op in STATIC and op != "LMHEAD":
+        # a split-K tile writes only its slice of the block's rows (summed
+        # over the block's column ranges after they have all arrived; an
+        # arrival counter, not an event, orders that)
+        k0, kc, ns, ks = _ksplit(model, t)
+        lo, hi = _split_rows(t, ns, ks)
+        W = [(n, l, b, sub, a + lo, a + hi) for (n, l, b, sub, a, _) in W]
+        R = [r for r in R if not (op in ("OPROJ", "DOWN") and r[4] == t.a1 and r[5] == t.a1 + t.a2)]
+        if op in ("OPROJ", "DOWN"):
+            src = "x" if op == "OPROJ" else "xmid"
+            R += [(src, t.layer, b, 0, t.a1 + lo, t.a1 + hi) for b in range(B)]
+    return R, W
+
+
+def _regions_rows(model, t, B, S):
     op = mk.OPS[t.op]
     l, H = t.layer, model["hidden"]
     nq, nkv, hd = model["n_q_heads"], model["n_kv_heads"], model["head_dim"]
@@ -153,7 +210,8 @@ def _overlap(a, b):
 def _bruteforce_deps(model, B, S=None, **optkw):
     opts = mk.default_options(n_cus=optkw.pop("n_cus", 8), **optkw)
     tasks, thr = mk.inspect_plan(_cfg(model, B=B, maxp=8), opts)
-    sig = _check_graph(model, tasks, thr, B)
+    mfma = B >= 16
+    sig = _check_graph(model, tasks, thr, B, mfma)
     # S actually used: count ATTN tasks per (layer 0, slot 0, head 0)
     S = sum(1 for t in tasks if mk.OPS[t.op] == "ATTN" and t.layer == 0 and t.a0 == 0 and t.a1 == 0)
     T = len(tasks)
@@ -164,7 +222,7 @@ def _bruteforce_deps(model, B, S=None, **optkw):
             for p in sig[t.wait_ev[k]]:
                 a |= anc[p] | (1 << p)
         anc[i] = a
-    regs = [_regions(model, t, B, S) for t in tasks]
+    regs = [_regions(model, t, B, S, mfma) for t in tasks]
     written = []
     for i, (_, W) in enumerate(regs):
         for w in W:
@@ -191,6 +249,17 @@ def test_dependencies_match_region_overlap_tiny(B):
 
 def test_dependencies_match_region_overlap_tiny_split_attention():
     T, n = _bruteforce_deps(TINY, 2, attn_splits=3)
+    assert n > 0
+
+
+def test_dependencies_match_region_overlap_batched_split_k():
+    """Matrix-core batch of 16 on 8 workers: the down projection is cut into
+    column ranges (split-K); every tile writes its own slice of rows and the
+    dependency structure still covers every read."""
+    tasks, _ = mk.inspect_plan(_cfg(TINY, B=16, maxp=8), mk.default_options(n_cus=8))
+    splits = [t for t in tasks if mk.OPS[t.op] == "DOWN" and _ksplit(TINY, t)[2] > 1]
+    assert splits
+    T, n = _bruteforce_deps(TINY, 16)
     assert n > 0
 
 
@@ -289,9 +358,23 @@ def test_batched_plans_use_16_row_groups():
     for model in (LLAMA8B, TINY):
         for B in (16, 64):
             tasks, thr = mk.inspect_plan(_cfg(model, B=B, maxp=8), mk.default_options(n_cus=256))
-            _check_graph(model, tasks, thr, B)
+            _check_graph(model, tasks, thr, B, mfma=True)
+            per_op = {}
             for t in tasks:
                 op = mk.OPS[t.op]
                 if op in ("QKV", "OPROJ", "GATEUP", "DOWN", "LMHEAD"):
                     assert t.a1 % 16 == 0 and t.a2 % 16 == 0, (op, t.a1, t.a2)
                     assert t.a2 // 16 <= (7 if op == "GATEUP" else 14), (op, t.a2)
+                    k0, kc, ns, ks = _ksplit(model, t)
+                    assert k0 % 32 == 0 and kc % 32 == 0 and 1 <= ns <= 16, (op, k0, kc, ns)
+                    per_op.setdefault((op, t.layer), []).append((t, ns))
+            for (op, l), tt in per_op.items():
+                if max(ns for _, ns in tt) > 1:
+                    # split operations: every tile on its own worker (the
+                    # tiles of a block wait for each other)
+                    assert len({t.worker for t, _ in tt}) == len(tt) <= 256, (op, l)
+            if model is LLAMA8B:
+                # the large batch splits K wherever the row blocks alone
+                # would leave most workers idle
+                assert any(ns > 1 for (op, l), tt in per_op.items() if op == "DOWN"
+                           for _, ns in tt)
