@@ -123,7 +123,13 @@ typedef struct {
                             batches of 16..64 slots: 0 = auto (on when
                             max_batch >= 16 and every row count is a multiple
                             of 16), -1 = off (vector path)                   */
-  int32_t reserved[5];
+  int32_t attn_pool;     /* persistent executor: attention tasks of a layer are
+                            claimed at run time from a shared counter by the
+                            workers that reach them (balances sequences of
+                            different lengths): 0 = auto (on when a layer has
+                            more attention tasks than workers), 1 = on,
+                            -1 = off (static placement)                       */
+  int32_t reserved[4];
 } mk_plan_options;
 
 typedef struct mk_plan mk_plan;

@@ -366,6 +366,8 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     for (int32_t v : hp.ev_thr) max_thr = std::max(max_thr, v);
     max_thr = std::max(max_thr, hp.S);  // split-attention arrival counters
     max_thr = std::max(max_thr, kMaxKSplit);  // split-K arrival counters
+    for (const Task &t : hp.tasks)              // claimed-attention counters
+      if (t.op == OP_ATTN && hp.attn_pool) max_thr = std::max(max_thr, t.rpp >> 16);
     p->epoch_limit = (uint32_t)(((1u << 31) - 1u) / (uint32_t)max_thr) - 2u;
 
     // device allocations
@@ -374,7 +376,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     int32_t *d_wq;
     if ((rc = p->alloc(&d_wq, hp.worker_off.size() + hp.worker_list.size(), "worker queues")))
       return rc;
-    p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads + hp.n_kcnt;
+    p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads + hp.n_kcnt + c.n_layers;
     p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
     const int64_t n_kpart = hp.n_kpart * kpart_slot(B);
@@ -460,6 +462,8 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.ev = p->ctrl + CTRL_WORDS;
     d.att_cnt = d.ev + E;
     d.kcnt = d.att_cnt + c.n_layers * c.max_batch * c.n_kv_heads;
+    d.pool_cnt = d.kcnt + hp.n_kcnt;
+    d.attn_pool = hp.attn_pool ? 1 : 0;
     d.tasks = d_tasks;
     d.n_tasks = T;
     d.worker_off = d_wq;

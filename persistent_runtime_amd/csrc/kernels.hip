@@ -412,6 +412,7 @@ DEV bool signals_counter(const TD &t) {
 // advances by 512 mod K per chunk.
 typedef u32x4 Buf[kMaxChunks];  // one tile's weights, per lane (16-byte slots)
 
+
 struct Geo {
   const uint16_t *seg0, *seg1;
   uint32_t seg_bytes;  // bytes of the first segment
@@ -431,9 +432,15 @@ DEV Geo make_geo(const uint16_t *s0, const uint16_t *s1, int seg_rows, int nseg,
 }
 DEV int cw_chunks(const Geo &g, int cw) { return min(g.cpw, g.units - cw * g.cpw); }
 
+// Target of the refills that have no next tile: one 1 KiB line every CU
+// reads (it stays in the L2), so a register slot is always written by a load
+// without streaming anything from HBM.
+__device__ __attribute__((aligned(1024))) u32x4 kIdleLine[64];
+DEV uint64_t idle_addr() { return (uint64_t)&kIdleLine[tidx() & 63]; }
+
 // Address of lane's 16 bytes of chunk j of compute wave cw in tile g; slots
-// beyond the wave's chunks read the tile's first chunk instead (always
-// inside the tile), so every slot is written by a load.  Unconditional loads
+// beyond the wave's chunks read the idle line instead, so every slot is
+// written by a load.  Unconditional loads
 // keep each slot in one register across tiles: a slot that a branch might
 // leave unchanged would be copied between registers, which forces a wait for
 // every load in flight.
@@ -442,7 +449,7 @@ DEV uint64_t slot_addr(const Geo &g, int cw, int j) {
   const uint32_t o = (uint32_t)(cw * g.cpw + j) * 1024u + lane16;
   const uint64_t b0 = (uint64_t)g.seg0, b1 = (uint64_t)g.seg1 - g.seg_bytes;
   const uint64_t a = (o < g.seg_bytes ? b0 : b1) + o;
-  return j < cw_chunks(g, cw) ? a : b0 + lane16;
+  return j < cw_chunks(g, cw) ? a : idle_addr();
 }
 
 // Issue the loads of compute wave cw's chunks of a tile into w.
@@ -487,7 +494,7 @@ DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, b
   int col = (int)(((uint32_t)q0 * 512u + (uint32_t)lane * 8u) % (uint32_t)g.K);
   float *pp = part + q0 * 4 + (lane >> 4);
   const bool writer = (lane & 15) == 0;
-  // without a next tile the slots re-read this tile's first chunk
+  // without a next tile the slots load the idle line
   const Geo &gr = pre ? gn : g;
   const int crw = pre ? cw : 0;
 #pragma unroll
@@ -498,7 +505,7 @@ DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, b
       col += g.step;
       col = col >= g.K ? col - g.K : col;
     }
-    w[j] = ldnt((const u32x4 *)(pre ? slot_addr(gr, crw, j) : slot_addr(g, 0, kMaxChunks)));
+    w[j] = ldnt((const u32x4 *)(pre ? slot_addr(gr, crw, j) : idle_addr()));
     __builtin_amdgcn_sched_barrier(0);  // keep each refill right after its use
   }
 }
@@ -1273,7 +1280,7 @@ DEV bool mgroup(const MGeo &g, int cw, int gi, int &seg, int &slot) {
 }
 
 // Address of lane's 16 bytes of register slot j (group j / NKB, k-block
-// j % NKB) of wave cw in pass p; slots without a chunk read the first chunk.
+// j % NKB) of wave cw in pass p; slots without a chunk read the idle line.
 template <int NKB>
 DEV uint64_t maddr(const MGeo &g, int cw, int j, int p) {
   const int lane = tidx() & 63;
@@ -1281,10 +1288,9 @@ DEV uint64_t maddr(const MGeo &g, int cw, int j, int p) {
   int seg = 0, slot = 0;
   const int k = p * g.Ks + kb * 32;
   const bool ok = gi < 2 && mgroup(g, cw, gi, seg, slot) && kb < g.nkb && k < g.K;
-  const uint16_t *base = ok && seg ? g.s1 : g.s0;
-  const int row = (ok ? slot * 16 : 0) + (lane & 15);
-  const int col = (ok ? k : 0) + 8 * (lane >> 4);
-  return (uint64_t)(base + (size_t)row * g.ld + col);
+  const uint16_t *base = seg ? g.s1 : g.s0;
+  const uint64_t a = (uint64_t)(base + (size_t)(slot * 16 + (lane & 15)) * g.ld + k + 8 * (lane >> 4));
+  return ok ? a : idle_addr();
 }
 DEV uint64_t maddr_any(const MGeo &g, int cw, int j, int p) {
   return g.nkb >= 16 ? maddr<16>(g, cw, j, p) : maddr<8>(g, cw, j, p);
@@ -1328,7 +1334,7 @@ DEV void mpass(const MGeo &g, Buf &w, f32x4 (&acc)[2][4], const char *xb, int cw
       }
     }
     const uint64_t na = !last ? maddr<NKB>(g, cw, j, p + 1)
-                              : (pre ? maddr_any(gn, cw, j, 0) : maddr<NKB>(g, cw, kMaxChunks, 0));
+                              : (pre ? maddr_any(gn, cw, j, 0) : idle_addr());
     w[j] = ldnt((const u32x4 *)na);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1664,6 +1670,7 @@ DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float ssl[4] = {0.f, 0.f, 0.f, 0.f};  // the control wave stages the activations
+  const KSplit k = ksplit_of(t);
   __syncthreads();  // slice 0 staged
   for (int p = 0; p < g.P; ++p) {
     const char *xb = (const char *)sm.xs + (p & 1) * (g.nkb * g.B16 * 2048);
@@ -1691,7 +1698,6 @@ DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
     }
   }
   __syncthreads();  // accumulators and sums of squares in LDS
-  const KSplit k = ksplit_of(t);
   if (k.ns > 1) {
     if (!ksplit_arrive(sm, d, ca, t, k)) return false;
     int lo, nr;
@@ -1701,21 +1707,6 @@ DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
   }
   __syncthreads();  // outputs written: LDS free for the next task
   ws.x_src = nullptr;
-  return true;
-}
-
-// Geometry of the next task's first pass (matrix-core mode) from its
-// descriptor words in the ring.
-DEV bool next_mgeo(CP &d, const uint32_t *slot, MGeo &g) {
-  const int op = (int)(int16_t)(uni((int)slot[0]) & 0xffff);
-  if (!static_weights(op)) return false;
-  const int rows = uni((int)slot[4]);
-  const int k0 = uni((int)slot[5]);
-  const uint16_t *w0 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[16]), (uint32_t)uni((int)slot[17]));
-  const uint16_t *w1 = (const uint16_t *)ptr_of((uint32_t)uni((int)slot[18]), (uint32_t)uni((int)slot[19]));
-  const int K = uni((int)slot[28]);
-  const int kc = ksplit_kc(uni((int)slot[31]), K);
-  g = mgeo(w0, w1, rows, min(kc, K - k0), d.B, K, k0);
   return true;
 }
 
@@ -2188,6 +2179,30 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
   return true;
 }
 
+// Claimed attention (persistent, batched plans): the workgroup takes the
+// layer's ATTN tasks one at a time from a shared counter until none is left.
+// The counter grows by every claim, the failed last claim of each worker that
+// holds entries of the layer included, so step e's claims start at
+// e * (claims per step).  Every task still runs exactly once; each reports
+// its own completion as it would in a worker queue.
+DEV bool run_attn_pool(Smem &sm, CP &d, const CallArgs &ca, const TD &t0, WState &ws) {
+  const int first = t0.a4, n = t0.rpp & 0xffff;
+  const uint32_t per_step = (uint32_t)t0.rpp >> 16;
+  uint32_t *cnt = d.pool_cnt + t0.layer;
+  for (;;) {
+    if (tidx() == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.imisc[3] = (int)(old - ca.epoch * per_step);
+    }
+    __syncthreads();
+    const int idx = uni(sm.imisc[3]);
+    __syncthreads();  // every wave has read the claim
+    if (idx < 0 || idx >= n) return true;
+    const TD t = td_from_table(d.tasks, ((const AS4 int *)d.task_pos)[first + idx]);
+    if (!run_small(sm, d, ca, t, true, ws)) return false;
+  }
+}
+
 // Run task t; `w` holds its weights when w_loaded.  When the worker's next
 // task has static weights (pre), their tile geometry is gn and this task
 // leaves them loading into `w`.  Returns whether it did; `alive` turns false
@@ -2274,6 +2289,12 @@ __global__ void __launch_bounds__(kThreads)
   if (wave == 0) {
     for (int k = beg; k < end; ++k) {
       const TD t = td_from_ring(sm.ring[(k - beg) % kRing]);
+      if (t.op == OP_ATTN && d.attn_pool) {
+        if (!run_attn_pool(sm, d, ca, t, ws)) return;
+        k += t.a3 - 1;    // this worker's other entries of the pool
+        __syncthreads();  // the ring reloaded for the next task
+        continue;
+      }
       const bool alive =
           t.op == OP_EDOWN                      ? down_ctl(sm, d, ca, t, true, ws)
           : (MODE == 2 && static_weights(t.op)) ? gemv_mfma_ctl(sm, d, ca, t, true, ws)
@@ -2298,17 +2319,15 @@ __global__ void __launch_bounds__(kThreads)
   while (k < end) {
     TD t = td_from_ring(sm.ring[(k - beg) % kRing]);
     if (MODE == 2 && static_weights(t.op)) {
+      // Matrix-core tiles load their first pass when they start: a phase
+      // ends with its slowest tile (split-K tiles wait for each other), and
+      // weights prefetched by the tiles that finish early would take
+      // bandwidth from it.
       Buf w;
-      mload(mgeo_of(d, t), w, cw);
-      for (;;) {
-        MGeo gn;
-        const bool pre = k + 1 < end && next_mgeo(d, sm.ring[(k + 1 - beg) % kRing], gn);
-        if (!gemv_mfma_cmp(sm, d, ca, t, true, ws, w, true, pre, gn)) return;
-        refill(k);
-        ++k;
-        if (!pre) break;
-        t = td_from_ring(sm.ring[(k - beg) % kRing]);
-      }
+      MGeo gn;
+      if (!gemv_mfma_cmp(sm, d, ca, t, true, ws, w, false, false, gn)) return;
+      refill(k);
+      ++k;
     } else if (static_weights(t.op)) {
       Buf w;
       load_slots(static_geo(t), w, cw);
@@ -2321,6 +2340,15 @@ __global__ void __launch_bounds__(kThreads)
         if (!pre) break;
         t = td_from_ring(sm.ring[(k - beg) % kRing]);
       }
+    } else if (t.op == OP_ATTN && d.attn_pool) {
+      if (!run_attn_pool(sm, d, ca, t, ws)) return;
+      k += t.a3;  // past this worker's entries of the pool: reload the ring there
+      if (wave == 1 && lane < 8) {
+        for (int i = 0; i < 3 && k + i < end; ++i)
+          ((u32x4 *)sm.ring[(k + i - beg) % kRing])[lane] = ldg(tabv + (size_t)(k + i) * 8 + lane);
+        if (k + 3 < end) pend = ldg(tabv + (size_t)(k + 3) * 8 + lane);
+      }
+      __syncthreads();
     } else {
       bool alive;
       if (t.op == OP_EDOWN) {

@@ -49,7 +49,9 @@ enum Op : int16_t {
 // 64-byte task descriptor.  Field use per op:
 //   EMBED   a0=slot
 //   QKV     a0=matrix (0 q, 1 k, 2 v) a1=row0 a2=rows
-//   ATTN    a0=slot a1=kv head a2=split
+//   ATTN    a0=slot a1=kv head a2=split; claimed plans also a3 = this
+//           worker's consecutive entries of the layer (first entry only),
+//           a4 = the layer's first ATTN task, rpp = count | claims per step << 16
 //   MERGE   a0=slot a1=kv head
 //   OPROJ/DOWN/ROUTER  a1=row0 a2=rows
 //   GATEUP  a1=row0 a2=rows per matrix (gate rows then the same up rows)
@@ -132,6 +134,8 @@ struct DevPlan {
   uint32_t *att_cnt;       // split-attention arrivals per (layer, slot, KV head),
                            // after the event counters; monotonic like them
   uint32_t *kcnt;          // split-K arrivals per matrix-core row block, after att_cnt
+  uint32_t *pool_cnt;      // claimed-attention counters per layer, after kcnt
+  int32_t attn_pool;       // persistent workers claim attention tasks at run time
   float *kpart;            // split-K partial products, kpart_slot(B) floats per tile
   uint32_t *ctrl;
   const Task *tasks;           // worker-major: each worker's queue is contiguous

@@ -345,7 +345,19 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   int want = std::max(1, n_cus / (nkv * B));
   int by_len = std::max(1, ctx / 64);
   p.S = std::max(1, std::min(std::min(want, by_len), 64));
+  // Large batches (Cohere "Folyamatos batchkezelés": sequences of different
+  // and changing lengths): the persistent workers claim a layer's attention
+  // tasks at run time from a shared counter; about two tasks per worker, at
+  // least two splits per sequence, keep the last ones to finish short
+  // without multiplying the per-task cost.
+  if (o.attn_pool >= 0 && B >= 16)
+    p.S = std::max(1, std::min({std::max(2, 2 * n_workers / (nkv * B)), std::max(1, ctx / 256), 64}));
   if (o.attn_splits > 0) p.S = std::min(o.attn_splits, 128);  // merge keeps G*S pairs in LDS
+  p.attn_pool = o.attn_pool > 0 || (o.attn_pool == 0 && B > 1 && (int64_t)B * nkv * p.S > n_workers);
+  if (p.attn_pool && (int64_t)B * nkv * p.S > 0x7fff) {
+    err = "too many attention tasks per layer for a claimed pool";
+    return MK_ERR_UNSUPPORTED;
+  }
 
   bool ok = true;
   // batched decode: matrix-core GEMV tiles when every static row count is a
@@ -531,7 +543,7 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   // reports all its completions once, from its last task.
   const bool split_attn = p.S > 1;
   auto same_sig = [&](const Task &a, const Task &b) {
-    if (split_attn && (a.op == OP_ATTN || b.op == OP_ATTN)) return false;
+    if ((split_attn || p.attn_pool) && (a.op == OP_ATTN || b.op == OP_ATTN)) return false;
     if (a.n_sig != b.n_sig || a.n_sig == 0) return false;
     for (int k = 0; k < a.n_sig; ++k)
       if (a.sig_ev[k] != b.sig_ev[k]) return false;
@@ -556,6 +568,39 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     p.worker_list.insert(p.worker_list.end(), lst.begin(), lst.end());
   }
   p.worker_off[n_workers] = (int32_t)p.worker_list.size();
+  if (p.attn_pool) {
+    // Claimed attention: every ATTN task carries its layer's first ATTN task
+    // (a4) and rpp = count | claims per step << 16, where a step's claims are
+    // the count plus one failed claim by each worker holding entries of the
+    // layer; the first of a worker's consecutive entries of a layer carries
+    // their number (a3): that worker claims from the pool there and skips
+    // the rest of them.
+    std::vector<int> first(L, -1), cnt(L, 0), holders(L, 0);
+    for (int i = 0; i < T; ++i)
+      if (p.tasks[i].op == OP_ATTN) {
+        const int l = p.tasks[i].layer;
+        if (first[l] < 0) first[l] = i;
+        cnt[l]++;
+      }
+    for (int w = 0; w < n_workers; ++w) {
+      for (int k = p.worker_off[w]; k < p.worker_off[w + 1];) {
+        Task &t = p.tasks[p.worker_list[k]];
+        if (t.op != OP_ATTN) { ++k; continue; }
+        int j = k + 1;
+        while (j < p.worker_off[w + 1] && p.tasks[p.worker_list[j]].op == OP_ATTN &&
+               p.tasks[p.worker_list[j]].layer == t.layer)
+          ++j;
+        t.a3 = j - k;
+        holders[t.layer]++;
+        k = j;
+      }
+    }
+    for (auto &t : p.tasks)
+      if (t.op == OP_ATTN) {
+        t.a4 = first[t.layer];
+        t.rpp = cnt[t.layer] | (cnt[t.layer] + holders[t.layer]) << 16;
+      }
+  }
   rc = validate_plan(p, err);
   if (rc != MK_OK) return rc;
   // Data edges: the reader checks the tags of the vector it stages instead of

@@ -24,6 +24,7 @@ struct HostPlan {
   int n_lm_tiles = 0;
   int max_pos = 0;
   bool mfma = false;                // static GEMVs as matrix-core tiles (16-row groups)
+  bool attn_pool = false;           // attention tasks claimed at run time (persistent)
   std::vector<Task> tasks;
   std::vector<int32_t> ev_thr;      // per-step threshold of each event
   std::vector<int32_t> task_phase;  // launch index under kernel-per-op

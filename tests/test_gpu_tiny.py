@@ -99,10 +99,12 @@ def test_tiny_free_running_greedy_matches(tiny):
     r.plan.free()
 
 
-def test_tiny_batch_with_empty_slot(tiny):
-    """Three slots: two sequences of different lengths and one empty slot."""
+@pytest.mark.parametrize("pool", [-1, 1], ids=["static_attention", "claimed_attention"])
+def test_tiny_batch_with_empty_slot(tiny, pool):
+    """Three slots: two sequences of different lengths and one empty slot;
+    attention tasks placed statically or claimed at run time."""
     Wd, Wt = tiny
-    r = Runner(TINY, Wd, B=3, maxp=8, attn_splits=2)
+    r = Runner(TINY, Wd, B=3, maxp=8, attn_splits=2, attn_pool=pool)
     pa, pb = _prompt(39), synth.make_prompt(21, 1024, seed=7).tolist()
     ca, cb = O.KVCache(TINY), O.KVCache(TINY)
     for p, t in enumerate(pa):
@@ -127,13 +129,15 @@ def test_tiny_batch_with_empty_slot(tiny):
     r.plan.free()
 
 
-def test_trace_dependencies_and_run_once(tiny):
+@pytest.mark.parametrize("pool", [-1, 1], ids=["static_attention", "claimed_attention"])
+def test_trace_dependencies_and_run_once(tiny, pool):
     """Integer invariants of the persistent scheduler: every task ran exactly
-    once and started only after every producer of its inputs finished."""
+    once and started only after every producer of its inputs finished (also
+    when the attention tasks are claimed from a shared counter)."""
     Wd, _ = tiny
-    r = Runner(TINY, Wd, B=2, maxp=8, debug_trace=1, attn_splits=3)
+    r = Runner(TINY, Wd, B=2, maxp=8, debug_trace=1, attn_splits=3, attn_pool=pool)
     tasks, thr = mk.inspect_plan(r.plan.cfg, mk.default_options(
-        n_cus=r.plan.info()["n_cus"], attn_splits=3))
+        n_cus=r.plan.info()["n_cus"], attn_splits=3, attn_pool=pool))
     sig = {}
     for i, t in enumerate(tasks):
         for k in range(t.n_sig):

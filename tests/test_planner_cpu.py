@@ -378,3 +378,34 @@ def test_batched_plans_use_16_row_groups():
                 # would leave most workers idle
                 assert any(ns > 1 for (op, l), tt in per_op.items() if op == "DOWN"
                            for _, ns in tt)
+
+
+def test_claimed_attention_annotations():
+    """Batches of 16 and more claim attention at run time: every ATTN task names its
+    layer's first ATTN task (a4) and carries count | claims per step << 16
+    (rpp); the first of each worker's consecutive entries of a layer holds
+    their number (a3), and the entries of every layer add up to its count."""
+    for B in (16, 64):
+        tasks, thr = mk.inspect_plan(_cfg(LLAMA8B, B=B, maxp=1024),
+                                     mk.default_options(n_cus=256, planned_ctx=16384))
+        _check_graph(LLAMA8B, tasks, thr, B, mfma=B >= 16)
+        attn = [(i, t) for i, t in enumerate(tasks) if mk.OPS[t.op] == "ATTN"]
+        assert len(attn) > 256, (B, len(attn))  # more tasks than workers: claimed
+        by_layer = {}
+        for i, t in attn:
+            by_layer.setdefault(t.layer, []).append((i, t))
+        for l, tt in by_layer.items():
+            first, n = tt[0][0], len(tt)
+            holders = sum(1 for _, t in tt if t.a3 > 0)
+            assert sum(t.a3 for _, t in tt) == n
+            for _, t in tt:
+                assert t.a4 == first and t.rows_per_pass == n | (n + holders) << 16
+            # a worker's entries of the layer are consecutive in its queue
+            for _, t in tt:
+                if t.a3 > 0:
+                    run = [u for _, u in tt if u.worker == t.worker]
+                    assert len(run) == t.a3
+    for B in (1, 4):  # one task per worker or fewer: static placement
+        tasks, _ = mk.inspect_plan(_cfg(LLAMA8B, B=B, maxp=1024),
+                                   mk.default_options(n_cus=256, planned_ctx=16384))
+        assert all(t.a3 == 0 for t in tasks if mk.OPS[t.op] == "ATTN")
