@@ -293,7 +293,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="llama8b", choices=sorted(WORKLOADS) + ["ragged"])
     ap.add_argument("--batches", default="4,16,64", help="ragged: batch sizes")
-    ap.add_argument("--attn-splits", type=int, default=None, help="ragged: KV splits per sequence")
+    ap.add_argument("--attn-splits", type=int, default=None,
+                    help="KV splits per (sequence, KV head); default: the planner's choice")
     ap.add_argument("--kpo-steps", type=int, default=64, help="kernel-per-op comparison steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kpo", action="store_true")
@@ -346,9 +347,10 @@ def main():
     pos_all = torch.arange(ctx0, ctx0 + W_ + K_ + 1, dtype=torch.int32, device=dev)
 
     def build(executor, graph_replay=0):
+        extra = {} if args.attn_splits is None else {"attn_splits": args.attn_splits}
         return mk.Plan(model, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=1,
                        opts=mk.default_options(executor=executor, planned_ctx=total,
-                                               graph_replay=graph_replay))
+                                               graph_replay=graph_replay, **extra))
 
     def start(plan, ring):
         """Context in place and the first token in ring[0]."""

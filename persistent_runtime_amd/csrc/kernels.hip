@@ -269,6 +269,8 @@ struct WState {
   int x_K, x_nb;
   int sat_ev[2];           // recently satisfied waits (event, wanted count)
   uint32_t sat_want[2];
+  int rt_layer, rt_slot;   // routing held in LDS (sm.imisc/misc[48..]) for this
+                           // (layer, slot) of this step, or -1
 };
 
 DEV void init_ws(WState &ws) {
@@ -278,6 +280,7 @@ DEV void init_ws(WState &ws) {
   ws.x_nb = 0;
   ws.sat_ev[0] = ws.sat_ev[1] = -1;
   ws.sat_want[0] = ws.sat_want[1] = 0;
+  ws.rt_layer = ws.rt_slot = -1;
 }
 
 DEV void set_error(CP &d, uint32_t code, int task, int ev, uint32_t seen, uint32_t want) {
@@ -297,12 +300,17 @@ DEV bool error_set(CP &d) {
 // Waits this worker already saw satisfied in this step are skipped without a
 // poll (tiles of one operation share their input event).  Otherwise thread 0
 // (control wave) polls; a barrier hands the outcome to the workgroup.
-// Returns false when the step is being drained after an error.
-DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws) {
+// Only the task's waits i0 .. i1-1 are considered (a task may wait for its
+// inputs in stages).  Returns false when the step is being drained after an
+// error.
+DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws, int i0 = 0,
+                   int i1 = 3) {
+  i1 = min(i1, t.n_wait);
   bool need = false;
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
-    if (i >= t.n_wait) break;
+    if (i < i0) continue;
+    if (i >= i1) break;
     const int e = t.wait_ev[i];
     if (e & kDataEdge) continue;  // the staged data carries its own readiness
     const uint32_t want = (ca.epoch + 1u) * (uint32_t)t.wait_thr[i];
@@ -315,7 +323,8 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws)
     int ok = 1;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      if (i >= t.n_wait || !ok) break;
+      if (i < i0) continue;
+      if (i >= i1 || !ok) break;
       if (t.wait_ev[i] & kDataEdge) continue;
       uint32_t *c = d.ev + t.wait_ev[i];
       const uint32_t want = (ca.epoch + 1u) * (uint32_t)t.wait_thr[i];
@@ -346,7 +355,8 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws)
   if (ok) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      if (i >= t.n_wait) break;
+      if (i < i0) continue;
+      if (i >= i1) break;
       if (t.wait_ev[i] & kDataEdge) continue;
       ws.sat_ev[1] = ws.sat_ev[0];
       ws.sat_want[1] = ws.sat_want[0];
@@ -948,7 +958,7 @@ struct GemvShape2 {
 
 // B1: compiled for plans with one slot (no slot chunks).
 template <bool B1>
-DEV GemvShape2 gemv_shape(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
+DEV GemvShape2 gemv_shape(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws) {
   GemvShape2 q;
   q.skip = false;
   q.sid = 0;
@@ -962,14 +972,22 @@ DEV GemvShape2 gemv_shape(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
     if (!q.skip) {
       // the control wave routes the slot; the ids reach the other waves
       // through LDS (sm.imisc[48..] ids, sm.misc[48..] weights)
-      if (uni(tidx() >> 6) == 0) {
-        route_wave(d, t.layer, t.a0, q.sid, q.sw);
-        if ((tidx() & 63) < d.topk) {
-          sm.imisc[48 + (tidx() & 63)] = q.sid;
-          sm.misc[48 + (tidx() & 63)] = q.sw;
+      if (ws.rt_layer != t.layer || ws.rt_slot != t.a0) {
+        if (uni(tidx() >> 6) == 0) {
+          route_wave(d, t.layer, t.a0, q.sid, q.sw);
+          if ((tidx() & 63) < d.topk) {
+            sm.imisc[48 + (tidx() & 63)] = q.sid;
+            sm.misc[48 + (tidx() & 63)] = q.sw;
+          }
         }
+        __syncthreads();
+        ws.rt_layer = t.layer;
+        ws.rt_slot = t.a0;
       }
-      __syncthreads();
+      if ((tidx() & 63) < d.topk) {
+        q.sid = sm.imisc[48 + (tidx() & 63)];
+        q.sw = sm.misc[48 + (tidx() & 63)];
+      }
       const int e = sm.imisc[48 + t.a3];
       q.w0 = expert_w_uni(d, 0, t.layer, e, t.w0) + (size_t)t.a1 * t.K;
       q.w1 = expert_w_uni(d, 1, t.layer, e, t.w1) + (size_t)t.a1 * t.K;
@@ -999,7 +1017,7 @@ template <bool B1>
 DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
                   WState &ws) {
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
-  const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t);
+  const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t, ws);
   if (q.skip) {
     if (persistent) {
       trace_start(d, t);
@@ -1057,7 +1075,7 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
                   WState &ws, Buf &w, bool w_loaded, bool pre, const Geo &gn) {
   const int cw = uni(tidx() >> 6) - 1;
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
-  const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t);
+  const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t, ws);
   if (q.skip) return true;
   if (!w_loaded) load_slots(q.g, w, cw);
   if (!gemv_fits(d, t, q)) return false;
@@ -1115,33 +1133,51 @@ DEV DownShape down_shape(CP &d, const CallArgs &ca, const TD &t) {
   s.cpw = (s.units + kCW - 1) / kCW;
   return s;
 }
-// lane j < k: the slot's j-th routed expert and its weight (written by the
-// slot's first gate/up task, which the down tasks wait for)
-DEV void routed(CP &d, const TD &t, int &id, float &w) {
+// A down task waits in two stages: for the router logits (its first
+// waits), from which it routes the slot itself -- the same top-k as the
+// slot's gate/up tasks -- and issues its experts' weight loads; then for the
+// experts' activations (its last wait), which the weights no longer have to
+// wait behind.  The control wave routes; lane j < k of every wave gets the
+// j-th expert id and weight through LDS.
+DEV bool down_route(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
+                    WState &ws, int &id, float &w) {
+  if (persistent && !wait_deps(sm, d, ca, t, ws, 0, t.n_wait - 1)) return false;
   const int lane = tidx() & 63;
-  id = 0;
-  w = 0.f;
-  if (lane < d.topk) {
-    const size_t o = ((size_t)t.layer * d.B + t.a0) * d.topk + lane;
-    id = ldai(d.tk_ids + o);
-    w = lda(d.tk_w + o);
-    if (id < 0 || id >= d.E) id = 0;
+  if (ws.rt_layer != t.layer || ws.rt_slot != t.a0) {  // not routed by this worker yet
+    if (uni(tidx() >> 6) == 0) {
+      int sid;
+      float sw;
+      route_wave(d, t.layer, t.a0, sid, sw);
+      if (lane < d.topk) {
+        sm.imisc[48 + lane] = sid;
+        sm.misc[48 + lane] = sw;
+      }
+    }
+    __syncthreads();
+    ws.rt_layer = t.layer;
+    ws.rt_slot = t.a0;
   }
+  id = lane < d.topk ? sm.imisc[48 + lane] : 0;
+  w = lane < d.topk ? sm.misc[48 + lane] : 0.f;
+  return true;
 }
 
 DEV bool down_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
                   WState &ws) {
-  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
-  trace_start(d, t);
   const DownShape s = down_shape(d, ca, t);
   const int lane = tidx() & 63;
   if (s.skip) {
+    if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+    trace_start(d, t);
     if (persistent) trace_finish(d, t);
     for (int i = lane; i < t.a2; i += 64) stt(t.dst, i, 0.f, ca.tag);
   } else {
     int id;
     float w;
-    routed(d, t, id, w);
+    if (!down_route(sm, d, ca, t, persistent, ws, id, w)) return false;
+    // (the compute waves issue the experts' weight loads here)
+    if (persistent && !wait_deps(sm, d, ca, t, ws, t.n_wait - 1, t.n_wait)) return false;
+    trace_start(d, t);
     stage_x(sm, ws, t.src, t.K, d.topk, nullptr, d.eps);
     trace_mark(d, t, 0);
     const float aux0 = lane < t.a2 ? ldv(t.aux, lane) : 0.f;
@@ -1166,12 +1202,11 @@ DEV bool down_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
 DEV bool down_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
                   WState &ws) {
   const int cw = uni(tidx() >> 6) - 1, lane = tidx() & 63;
-  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   const DownShape s = down_shape(d, ca, t);
-  if (s.skip) return true;
+  if (s.skip) return !persistent || wait_deps(sm, d, ca, t, ws);
   int id;
   float wt;
-  routed(d, t, id, wt);
+  if (!down_route(sm, d, ca, t, persistent, ws, id, wt)) return false;
   // lane j: the first row of segment j
   const uint64_t base = (uint64_t)(expert_w_lane(d, 2, t.layer, id, t.w0) + (size_t)t.a1 * t.K);
   const int blo = (int)(uint32_t)base, bhi = (int)(uint32_t)(base >> 32);
@@ -1188,6 +1223,7 @@ DEV bool down_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     w[j] = ldnt((const u32x4 *)(b + (uint64_t)rj * 1024u + lane16));
     if (j < cnt && ++rr == s.cps) { rr = 0; ++sg; }
   }
+  if (persistent && !wait_deps(sm, d, ca, t, ws, t.n_wait - 1, t.n_wait)) return false;
   stage_x(sm, ws, t.src, t.K, d.topk, nullptr, d.eps);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   const int Fe = t.K, step = 512 % Fe;

@@ -121,7 +121,7 @@ struct Builder {
     if (phase >= 0) p.phases.back().second = (int)p.tasks.size();
   }
   void add(int op, int layer, int a0, int a1, int a2, int a3, int a4,
-           std::initializer_list<int> waits, std::initializer_list<int> sigs,
+           const std::vector<int> &waits, std::initializer_list<int> sigs,
            int64_t bytes, int worker = -1, int rpp = 0) {
     Task t{};
     t.rpp = rpp;
@@ -236,7 +236,7 @@ static int add_gemv_mfma(Builder &b, int op, int layer, const std::vector<RowSeg
 // register tile.
 int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int K, int nseg,
              int n_workers, int pmax, int wait_ev, int64_t extra_bytes, int *lm_index,
-             int min_unit = 1) {
+             int min_unit = 1, int early_ev = -1) {
   const int64_t row_bytes = (int64_t)nseg * K * 2;
   int unit = 1;
   while ((row_bytes * unit) % 1024 || unit % min_unit) ++unit;
@@ -244,6 +244,10 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
   R -= R % unit;
   if (b.p.mfma && op != OP_EGATEUP && op != OP_EDOWN)
     return add_gemv_mfma(b, op, layer, segs, K, nseg, n_workers, wait_ev, extra_bytes, lm_index);
+  // the waits of every task: an earlier-stage event first when given (the
+  // expert down projection routes from the router logits before its inputs)
+  const std::vector<int> waits =
+      early_ev >= 0 ? std::vector<int>{early_ev, wait_ev} : std::vector<int>{wait_ev};
   if (R < unit) return -1;
   int64_t total = 0;
   for (auto &sg : segs) total += sg.rows;
@@ -287,7 +291,7 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
           const int P = (int)((n + R - 1) / R);
           int rpp = (int)((n + P - 1) / P);
           rpp += (unit - rpp % unit) % unit;
-          b.add(op, layer, sg.a0, (int)(sg.row0 + lo), (int)n, sg.a3, 0, {wait_ev}, {sg.sig},
+          b.add(op, layer, sg.a0, (int)(sg.row0 + lo), (int)n, sg.a3, 0, waits, {sg.sig},
                 n * row_bytes + extra_bytes, w, rpp);
           ++added;
           lo += n;
@@ -314,7 +318,7 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
       rpp += (unit - rpp % unit) % unit;
       const int row0 = (int)(sg.row0 + (lo - seg_base));
       const int a4 = lm_index ? (*lm_index)++ : 0;
-      b.add(op, layer, sg.a0, row0, (int)n, sg.a3, a4, {wait_ev}, {sg.sig},
+      b.add(op, layer, sg.a0, row0, (int)n, sg.a3, a4, waits, {sg.sig},
             n * row_bytes + extra_bytes, w, rpp);
       ++added;
       lo += n;
@@ -477,7 +481,7 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
         while (((int64_t)unit * Fe * 2) % 1024) ++unit;
         std::vector<RowSeg> segs;
         for (int s = 0; s < B; ++s) segs.push_back({s, 0, H, x_ev[l + 1]});
-        if (add_gemv(b, OP_EDOWN, l, segs, Fe, K, n_workers, 1, eh, 0, nullptr, unit) < 0)
+        if (add_gemv(b, OP_EDOWN, l, segs, Fe, K, n_workers, 1, eh, 0, nullptr, unit, rlev) < 0)
           ok = false;
       }
     }

@@ -188,9 +188,10 @@ def _regions_rows(model, t, B, S):
         if t.a1 == 0 and j == 0:
             W.append(("tk", l, b, 0, 0, K))
     elif op == "EDOWN":
-        # rows a1..a1+a2 of every routed expert, weighted sum + residual
+        # routes the slot itself from the router logits, then rows a1..a1+a2
+        # of every routed expert, weighted sum + residual
         b = t.a0
-        R += [("tk", l, b, 0, 0, K), ("xmid", l, b, 0, t.a1, t.a1 + t.a2)]
+        R += [("rl", l, b, 0, 0, E), ("xmid", l, b, 0, t.a1, t.a1 + t.a2)]
         R += [("he", l, b, j, 0, Fe) for j in range(K)]
         W.append(("x", l + 1, b, 0, t.a1, t.a1 + t.a2))
     elif op == "LMHEAD":
