@@ -129,7 +129,12 @@ typedef struct {
                             different lengths): 0 = auto (on when a layer has
                             more attention tasks than workers), 1 = on,
                             -1 = off (static placement)                       */
-  int32_t reserved[4];
+  int32_t weight_lds;    /* single-slot plans: stream part of every weight pass
+                            through LDS (more weights in flight across each
+                            dependency wait), possible when the staged
+                            activations fit 72 KiB: 0 = auto (dense models),
+                            1 = on, -1 = off                                 */
+  int32_t reserved[3];
 } mk_plan_options;
 
 typedef struct mk_plan mk_plan;

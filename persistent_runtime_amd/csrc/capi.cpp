@@ -427,6 +427,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.Fe = c.expert_ffn_dim; d.B = B; d.maxp = c.max_pages_per_seq; d.npages = c.n_pages;
     d.S = hp.S; d.G = hp.G; d.max_pos = hp.max_pos; d.n_lm_tiles = hp.n_lm_tiles;
     d.mfma = hp.mfma ? 1 : 0;
+    d.lds_slots = hp.lds_slots;
     d.eps = c.rms_eps;
     d.embed = (const uint16_t *)w->embed;
     d.lm_head = (const uint16_t *)w->lm_head;

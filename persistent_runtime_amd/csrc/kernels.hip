@@ -187,8 +187,8 @@ DEV void vm_drain() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-constexpr int kPartSlot = kMaxTileUnits16 * 4;   // GEMV partials per slot of a tile
-constexpr int kRowSlot = kMaxTileUnits16 * 2;    // rows per tile (rows hold >= 256 elements)
+constexpr int kPartSlot = kMaxTileUnits * 4;   // GEMV partials per slot of a tile
+constexpr int kRowSlot = kMaxTileUnits * 2;    // rows per tile (rows hold >= 256 elements)
 #ifndef MK_REFILL_PER_SLOT
 #define MK_REFILL_PER_SLOT 0
 #endif
@@ -462,10 +462,51 @@ DEV uint64_t slot_addr(const Geo &g, int cw, int j) {
   return j < cw_chunks(g, cw) ? a : idle_addr();
 }
 
-// Issue the loads of compute wave cw's chunks of a tile into w.
-DEV void load_slots(const Geo &g, Buf &w, int cw) {
+// LDS slots (single-slot plans): compute wave cw's chunks kMaxChunks ..
+// kMaxChunks+kLdsSlots-1 of every pass live in LDS at kLdsWbufOff of the
+// activation stage, one 1 KiB slot each, and are filled by LDS-DMA (64 lanes
+// x 16 bytes to consecutive addresses from the M0 base; the compiler does
+// not track these loads, nothing else in this kernel uses M0).  Every pass
+// issues the register refills first, then the slots' DMAs, always all of
+// them (slots without a chunk load the idle line), so when the slots are
+// consumed exactly kMaxChunks vector-memory operations were issued after the
+// last DMA: waiting for that count completes them all.  The compiler's own
+// waits for the register slots do not count the DMAs and wait for a few
+// loads more than needed, which is safe.
+DEV uint32_t wslot(const float *xs, int cw, int s) {
+  return (uint32_t)(uintptr_t)xs + (uint32_t)kLdsWbufOff + (uint32_t)(cw * kLdsSlots + s) * 1024u;
+}
+DEV void dma16(uint64_t src, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
+}
+// All kLdsSlots slots of a pass at once: the last slot's DMA (and so every
+// earlier one) is complete once only the kMaxChunks register refills issued
+// after it remain; then four reads at a time, each group waited for in its
+// own statement.
+DEV void take_slots(uint32_t a, u32x4 (&v)[kLdsSlots]) {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kMaxChunks) : "memory");
+#pragma unroll
+  for (int s = 0; s < kLdsSlots; s += 4)
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(v[s]), "=v"(v[s + 1]), "=v"(v[s + 2]), "=v"(v[s + 3])
+        : "v"(a + (uint32_t)s * 1024u)
+        : "memory");
+}
+
+// Issue the loads of compute wave cw's chunks of a tile into w (and its LDS
+// slots when lds).
+DEV void load_slots(const Geo &g, Buf &w, int cw, const float *xs, bool lds) {
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) w[j] = ldnt((const u32x4 *)slot_addr(g, cw, j));
+  if (lds) {
+#pragma unroll
+    for (int s = 0; s < kLdsSlots; ++s) dma16(slot_addr(g, cw, kMaxChunks + s), wslot(xs, cw, s));
+  }
 }
 
 DEV float dot8(u32x4 w, const float *x) {
@@ -497,7 +538,7 @@ DEV float row16_sum(float v) {
 // code (uniform branches only), which lets the compiler wait for each slot
 // with "all but the newest loads done" instead of draining the queue.
 DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, bool pre,
-                   const Geo &gn) {
+                   const Geo &gn, bool lds) {
   const int lane = tidx() & 63;
   const int cnt = cw_chunks(g, cw);
   const int q0 = cw * g.cpw;
@@ -517,6 +558,23 @@ DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, b
     }
     w[j] = ldnt((const u32x4 *)(pre ? slot_addr(gr, crw, j) : idle_addr()));
     __builtin_amdgcn_sched_barrier(0);  // keep each refill right after its use
+  }
+  if (lds) {
+    u32x4 v[kLdsSlots];
+    take_slots(wslot(xs, cw, 0) + (uint32_t)(tidx() & 63) * 16u, v);
+#pragma unroll
+    for (int s = 0; s < kLdsSlots; ++s) {
+      const int j = kMaxChunks + s;
+      if (j < cnt) {
+        const float r = row16_sum(dot8(v[s], xs + col));
+        if (writer) pp[j * 4] = r;
+        col += g.step;
+        col = col >= g.K ? col - g.K : col;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kLdsSlots; ++s)
+      dma16(pre ? slot_addr(gr, crw, kMaxChunks + s) : idle_addr(), wslot(xs, cw, s));
   }
 }
 
@@ -1077,7 +1135,8 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t, ws);
   if (q.skip) return true;
-  if (!w_loaded) load_slots(q.g, w, cw);
+  const bool lds = d.lds_slots != 0;  // (single-slot plans only)
+  if (!w_loaded) load_slots(q.g, w, cw, sm.xs, lds);
   if (!gemv_fits(d, t, q)) return false;
   const int K = q.g.K;
   auto geo_of = [&](int p) { return p == 0 ? q.g : pass_geo(q.w0, q.w1, t.a2, t.rpp, K, p); };
@@ -1097,10 +1156,10 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
       const Geo gq = lastp ? gn : geo_of(p + 1);
       const bool pre_p = lastp ? (pre && last) : true;
       if (B1 || n == 1) {
-        gemv_dot1(gp, w, sm.xs, red + p * kPartSlot, cw, pre_p, gq);
+        gemv_dot1(gp, w, sm.xs, red + p * kPartSlot, cw, pre_p, gq, lds);
       } else {
         gemv_dotn(gp, w, sm.xs, n, red + p * n * kPartSlot, cw);
-        if (pre_p) load_slots(gq, w, cw);
+        if (pre_p) load_slots(gq, w, cw, sm.xs, false);
       }
     }
     __syncthreads();  // partials complete
@@ -1781,6 +1840,9 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   float *wl = wm + kWaves * kMaxGroup;       // [kWaves][kMaxGroup]
   float *wo = wl + kWaves * kMaxGroup;       // [kWaves][kMaxGroup][HD]
   float *scur = wo + kWaves * kMaxGroup * HD;
+  // below the LDS weight slots, which may hold loads in flight
+  static_assert((kMaxGroup * QROW + 2 * HD + 2 * kWaves * kMaxGroup + kWaves * kMaxGroup * HD +
+                 kMaxGroup) * 4 <= kLdsWbufOff, "attention LDS overlaps the weight slots");
 
   const int pos = uni(ldg(ca.positions + b));
   const size_t head0 = ((size_t)l * B + b) * nq + (size_t)g * G;  // first head row
@@ -2361,23 +2423,23 @@ __global__ void __launch_bounds__(kThreads)
       // bandwidth from it.
       Buf w;
       MGeo gn;
-      if (!gemv_mfma_cmp(sm, d, ca, t, true, ws, w, false, false, gn)) return;
+      if (!gemv_mfma_cmp(sm, d, ca, t, true, ws, w, false, false, gn)) goto done;
       refill(k);
       ++k;
     } else if (static_weights(t.op)) {
       Buf w;
-      load_slots(static_geo(t), w, cw);
+      load_slots(static_geo(t), w, cw, sm.xs, d.lds_slots != 0);
       for (;;) {
         Geo gn;
         const bool pre = k + 1 < end && next_geo(sm.ring[(k + 1 - beg) % kRing], gn);
-        if (!gemv_cmp<B1>(sm, d, ca, t, true, ws, w, true, pre, gn)) return;
+        if (!gemv_cmp<B1>(sm, d, ca, t, true, ws, w, true, pre, gn)) goto done;
         refill(k);
         ++k;
         if (!pre) break;
         t = td_from_ring(sm.ring[(k - beg) % kRing]);
       }
     } else if (t.op == OP_ATTN && d.attn_pool) {
-      if (!run_attn_pool(sm, d, ca, t, ws)) return;
+      if (!run_attn_pool(sm, d, ca, t, ws)) goto done;
       k += t.a3;  // past this worker's entries of the pool: reload the ring there
       if (wave == 1 && lane < 8) {
         for (int i = 0; i < 3 && k + i < end; ++i)
@@ -2396,11 +2458,13 @@ __global__ void __launch_bounds__(kThreads)
       } else {
         alive = run_small(sm, d, ca, t, true, ws);
       }
-      if (!alive) return;
+      if (!alive) goto done;
       refill(k);
       ++k;
     }
   }
+done:
+  vm_drain();  // LDS-DMA loads the compiler does not track complete before the wave ends
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -2415,6 +2479,7 @@ __global__ void __launch_bounds__(kThreads)
   WState ws;
   init_ws(ws);
   run_task_once(sm, d, ca, t, ws);
+  vm_drain();  // LDS-DMA loads the compiler does not track complete before the wave ends
 }
 
 __global__ void mk_stage_kernel(int32_t *tok, int32_t *pos, int B, int slot,

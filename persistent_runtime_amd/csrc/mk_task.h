@@ -26,12 +26,19 @@ constexpr int kCW = kWaves - 1;        // compute waves
 // wave holds up to kMaxChunks 16-byte loads per lane.
 constexpr int kMaxChunks = 16;
 constexpr int kMaxTileUnits16 = kCW * kMaxChunks;           // 1 KiB units/tile
+// Single-slot plans whose staged activations fit kLdsWbufOff bytes extend
+// every pass by kLdsSlots chunks per compute wave held in LDS (filled by
+// LDS-DMA at [kLdsWbufOff, kLdsXBytes) of the activation stage): a pass is
+// then kMaxTileUnits 1 KiB units, and more weights stream ahead of each
+// dependency wait.
+constexpr int kLdsSlots = 8;
+constexpr int kMaxTileUnits = kCW * (kMaxChunks + kLdsSlots);
 constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 8;           // query heads per KV head
 constexpr int kMaxBatchGemv = 4;       // slots a GEMV tile handles at once
-// A GEMV task streams its rows in passes of at most one register tile each;
-// passes x slots per task are bounded by the LDS partial-sum buffers.
-constexpr int kMaxPass = 8;
+// A GEMV task streams its rows in passes of at most one tile each; passes x
+// slots per task are bounded by the LDS partial-sum buffers.
+constexpr int kMaxPass = 6;
 // Batched decode (16..64 slots) runs the static-weight GEMVs as bf16
 // matrix-core tiles: 16-row groups, at most kMfmaGroups per task.
 constexpr int kMfmaGroups = 14;
@@ -39,6 +46,7 @@ constexpr int kMfmaMaxBatch = 64;
 constexpr int kMaxKSplit = 16;          // column ranges per split-K matrix-core row block
 constexpr int kLdsBytes = 160 * 1024;  // LDS per CU on gfx950
 constexpr int kLdsXBytes = 128 * 1024; // budget for staged activations
+constexpr int kLdsWbufOff = kLdsXBytes - kCW * kLdsSlots * 1024;  // 72 KiB
 
 enum Op : int16_t {
   OP_EMBED = 1, OP_QKV = 2, OP_ATTN = 3, OP_MERGE = 4, OP_OPROJ = 5,
@@ -109,6 +117,7 @@ struct DevPlan {
   int32_t L, H, nq, nkv, hd, F, V, E, topk, Fe, B, maxp, npages, S, G;
   int32_t max_pos, n_lm_tiles;
   int32_t mfma;            // static GEMVs as matrix-core tiles (batch 16..64)
+  int32_t lds_slots;       // kLdsSlots when passes extend into LDS, else 0
   float eps;
   // weights (bf16 as uint16)
   const uint16_t *embed, *lm_head, *final_norm;

@@ -240,7 +240,9 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
   const int64_t row_bytes = (int64_t)nseg * K * 2;
   int unit = 1;
   while ((row_bytes * unit) % 1024 || unit % min_unit) ++unit;
-  int R = (int)((int64_t)kMaxTileUnits16 * 1024 / row_bytes);
+  // the expert down projection keeps register-only passes
+  const int units = op == OP_EDOWN ? kMaxTileUnits16 : b.p.tile_units;
+  int R = (int)((int64_t)units * 1024 / row_bytes);
   R -= R % unit;
   if (b.p.mfma && op != OP_EGATEUP && op != OP_EDOWN)
     return add_gemv_mfma(b, op, layer, segs, K, nseg, n_workers, wait_ev, extra_bytes, lm_index);
@@ -370,6 +372,17 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     const bool rows16 = H % 16 == 0 && (nq * hd) % 16 == 0 && hd % 16 == 0 &&
                         c.vocab % 16 == 0 && (moe ? c.n_experts % 16 == 0 : c.ffn_dim % 16 == 0);
     p.mfma = o.batched_mfma >= 0 && B >= 16 && B <= kMfmaMaxBatch && rows16;
+  }
+  // single slot: GEMV passes extend into the LDS above the staged
+  // activations when the longest staged row leaves that space free.  Auto
+  // for dense models only: a MoE layer is a chain of short tasks, where the
+  // slots' extra waits cost more than the deeper prefetch saves (measured).
+  {
+    const int64_t kx = std::max<int64_t>(std::max<int64_t>(H, (int64_t)nq * hd),
+                                         moe ? (int64_t)c.top_k * c.expert_ffn_dim : c.ffn_dim);
+    const bool want = o.weight_lds > 0 || (o.weight_lds == 0 && !moe);
+    p.lds_slots = (B == 1 && want && kx * 4 <= kLdsWbufOff) ? kLdsSlots : 0;
+    p.tile_units = kCW * (kMaxChunks + p.lds_slots);
   }
   // passes per task: slots x passes share the LDS partial buffers; when the
   // slots of a step do not fit one activation stage the weights of a pass

@@ -70,7 +70,8 @@ class mk_plan_options(C.Structure):
                 ("debug_trace", C.c_int32), ("device", C.c_int32),
                 ("spin_budget", C.c_int64), ("n_cus", C.c_int32),
                 ("graph_replay", C.c_int32), ("batched_mfma", C.c_int32),
-                ("attn_pool", C.c_int32), ("reserved", C.c_int32 * 4)]
+                ("attn_pool", C.c_int32), ("weight_lds", C.c_int32),
+                ("reserved", C.c_int32 * 3)]
 
 
 class mk_task_info(C.Structure):
