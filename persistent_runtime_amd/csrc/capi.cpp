@@ -225,7 +225,7 @@ static void resolve_tasks(HostPlan &hp, const std::vector<const void *> &tab, co
         t.src = TG(d.xmid, (size_t)l * B * H);
         t.gain = W(1, l);
         t.K = H;
-        t.dst = d.rl + (size_t)l * B * E + t.a1;
+        t.dst = TG(d.rl, (size_t)l * B * E + t.a1);
         t.ostride = E;
         break;
       case OP_LMHEAD:
@@ -380,8 +380,8 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
     const int64_t n_kpart = hp.n_kpart * kpart_slot(B);
-    const int64_t nf = 2 * (hp.n_x + hp.n_xmid + hp.n_attn + hp.n_h + hp.n_q + 2 * hp.n_k) + hp.n_part +
-                       hp.n_rl + hp.n_tk + hp.n_he + hp.n_amax + n_kpart;
+    const int64_t nf = 2 * (hp.n_x + hp.n_xmid + hp.n_attn + hp.n_h + hp.n_q + 2 * hp.n_k + hp.n_rl) +
+                       hp.n_part + hp.n_tk + hp.n_he + hp.n_amax + n_kpart;
     float *fs;
     if ((rc = p->alloc(&fs, (size_t)nf, "activation scratch"))) return rc;
     int32_t *is;
@@ -449,7 +449,7 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.k = take(2 * hp.n_k); d.v = take(2 * hp.n_k); d.part = take(hp.n_part);
     d.attn = take(2 * hp.n_attn);
     d.h = take(2 * hp.n_h);
-    d.rl = take(hp.n_rl); d.tk_w = take(hp.n_tk); d.he = take(hp.n_he);
+    d.rl = take(2 * hp.n_rl); d.tk_w = take(hp.n_tk); d.he = take(hp.n_he);
     d.amax_v = take(hp.n_amax);
     d.kpart = take(n_kpart);
     d.tk_ids = hp.n_tk ? is : nullptr;

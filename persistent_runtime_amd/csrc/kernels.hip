@@ -876,16 +876,17 @@ template <bool MAX> DEV uint32_t wave_ext_u32(uint32_t v) {
 // with the j-th one's id and its weight, the softmax over the k chosen
 // logits.  Each lane keeps the best of its own untaken logits; a round takes
 // the wave's best key, then the lowest id holding it, and only the lane that
-// owned it rescans.
-DEV void route_wave(CP &d, int l, int b, int &sid, float &sw) {
+// owned it rescans.  The logits are a tagged vector: the loads wait for
+// this step's tag (a failure leaves sm.imisc[2] = tag for the caller).
+DEV void route_wave(Smem &sm, CP &d, const CallArgs &ca, const TD &t, int &sid, float &sw) {
   const int lane = tidx() & 63, E = d.E, K = d.topk;
-  const float *r = d.rl + ((size_t)l * d.B + b) * E;
+  const size_t r0 = ((size_t)t.layer * d.B + t.a0) * E;
   constexpr int kPer = 8;  // logits per lane: E <= 512
   uint32_t key[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     key[i] = 0u;
-    if (i * 64 < E && i * 64 + lane < E) key[i] = fkey(lda(r + i * 64 + lane));
+    if (i * 64 < E && i * 64 + lane < E) key[i] = fkey(ldt_wait(sm, d, ca, t, d.rl, r0 + i * 64 + lane));
   }
   uint32_t taken = 0;
   auto scan = [&](uint32_t &bk, uint32_t &bi) {  // best untaken (key, id) of this lane
@@ -992,8 +993,8 @@ DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const float *rsum
       case OP_QKV:  // tagged
         stt(t.dst, e, y, ca.tag);
         break;
-      default:  // ROUTER
-        sta(t.dst + e, y);
+      default:  // ROUTER; tagged
+        stt(t.dst, e, y, ca.tag);
         break;
     }
   }
@@ -1012,6 +1013,7 @@ struct GemvShape2 {
   int sid;      // expert tasks: lane j < k holds the j-th routed expert id
   float sw;     //   and its weight
   bool skip;    // expert task of an empty slot: no work
+  bool fail;    // the routing's logits never arrived (step abandoned)
 };
 
 // B1: compiled for plans with one slot (no slot chunks).
@@ -1019,6 +1021,7 @@ template <bool B1>
 DEV GemvShape2 gemv_shape(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws) {
   GemvShape2 q;
   q.skip = false;
+  q.fail = false;
   q.sid = 0;
   q.sw = 0.f;
   q.w0 = t.w0;
@@ -1032,13 +1035,14 @@ DEV GemvShape2 gemv_shape(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WSta
       // through LDS (sm.imisc[48..] ids, sm.misc[48..] weights)
       if (ws.rt_layer != t.layer || ws.rt_slot != t.a0) {
         if (uni(tidx() >> 6) == 0) {
-          route_wave(d, t.layer, t.a0, q.sid, q.sw);
+          route_wave(sm, d, ca, t, q.sid, q.sw);
           if ((tidx() & 63) < d.topk) {
             sm.imisc[48 + (tidx() & 63)] = q.sid;
             sm.misc[48 + (tidx() & 63)] = q.sw;
           }
         }
         __syncthreads();
+        q.fail = sm.imisc[2] == (int)ca.tag;
         ws.rt_layer = t.layer;
         ws.rt_slot = t.a0;
       }
@@ -1076,6 +1080,7 @@ DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
                   WState &ws) {
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t, ws);
+  if (q.fail) return false;
   if (q.skip) {
     if (persistent) {
       trace_start(d, t);
@@ -1134,6 +1139,7 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   const int cw = uni(tidx() >> 6) - 1;
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t, ws);
+  if (q.fail) return false;
   if (q.skip) return true;
   const bool lds = d.lds_slots != 0;  // (single-slot plans only)
   if (!w_loaded) load_slots(q.g, w, cw, sm.xs, lds);
@@ -1206,13 +1212,14 @@ DEV bool down_route(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persi
     if (uni(tidx() >> 6) == 0) {
       int sid;
       float sw;
-      route_wave(d, t.layer, t.a0, sid, sw);
+      route_wave(sm, d, ca, t, sid, sw);
       if (lane < d.topk) {
         sm.imisc[48 + lane] = sid;
         sm.misc[48 + lane] = sw;
       }
     }
     __syncthreads();
+    if (sm.imisc[2] == (int)ca.tag) return false;  // the logits never arrived
     ws.rt_layer = t.layer;
     ws.rt_slot = t.a0;
   }
@@ -1587,7 +1594,7 @@ DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, int R, int Bp, int r0
       else if (op == OP_OPROJ || op == OP_DOWN || op == OP_QKV)
         stt(t.dst, e, a[u] + y, ca.tag);  // QKV adds zero
       else
-        sta(t.dst + e, y);  // ROUTER
+        stt(t.dst, e, y, ca.tag);  // ROUTER
     }
   }
 }

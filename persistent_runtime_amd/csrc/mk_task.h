@@ -135,7 +135,8 @@ struct DevPlan {
   const int32_t *page_table;
   // scratch (fp32 unless noted); layouts in planner.cpp
   float *x, *xmid, *q, *k, *v, *part, *attn, *h;   // all but part: tagged pairs
-  float *rl, *tk_w, *he, *amax_v;
+  float *rl;                                        // router logits: tagged pairs
+  float *tk_w, *he, *amax_v;
   int32_t *tk_ids, *amax_i;
   const float *rope_cos, *rope_sin;                     // [max_pos][hd/2]
   // control

@@ -473,6 +473,7 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
       // residual (no separate combine task).
       const int E = c.n_experts, K = c.top_k, Fe = c.expert_ffn_dim;
       int rlev = b.ev();
+      data_ev.push_back(rlev);  // the router logits are tagged
       b.begin_phase();
       if (add_gemv(b, OP_ROUTER, l, {{0, 0, E, rlev}}, H, 1, n_workers, pmax_for(H), xo, 0,
                    nullptr) < 0)
