@@ -94,8 +94,11 @@ typedef struct {
   const void *const *router, *const *e_gate, *const *e_up, *const *e_down;
 } mk_weights;
 
-/* Paged KV cache (caller-owned).  k_pool, v_pool: bf16
- * [n_layers][n_pages][n_kv_heads][page_size][head_dim].  page_table: device
+/* Paged KV cache (caller-owned), bf16.  k_pool:
+ * [n_layers][n_pages][n_kv_heads][page_size][head_dim]; v_pool:
+ * [n_layers][n_pages][n_kv_heads][head_dim][page_size] (values transposed
+ * within a page: the 16 positions of one dimension are contiguous, the
+ * operand layout of the matrix-core attention products).  page_table: device
  * int32 [max_batch][max_pages_per_seq]; entry [b][j] is the pool page holding
  * positions 16j..16j+15 of slot b.  The caller may edit page_table and the
  * pools between steps (sequences joining / retiring). */

@@ -104,23 +104,6 @@ DEV float wave_max(float v) {
   v = fmaxf(v, dpp<DPP_MIRROR>(v));
   return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
 }
-// sum over the 4 lanes of each quad (result in all 4)
-DEV float quad_sum(float v) {
-  v += dpp<DPP_XOR1>(v);
-  v += dpp<DPP_XOR2>(v);
-  return v;
-}
-// values replicated within quads: max / sum over the 16 quads, uniform
-DEV float quads_max(float v) {
-  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
-  v = fmaxf(v, dpp<DPP_MIRROR>(v));
-  return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
-}
-DEV float quads_sum(float v) {
-  v += dpp<DPP_HALF_MIRROR>(v);
-  v += dpp<DPP_MIRROR>(v);
-  return (lanef(v, 0) + lanef(v, 16)) + (lanef(v, 32) + lanef(v, 48));
-}
 DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
 // (value, index) maximum; NaN never wins, equal values keep the lower index
 DEV bool better(float v, int i, float bv, int bi) {
@@ -1826,9 +1809,7 @@ DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
 // first two pages are loaded before the task waits for the query/key/value
 // tiles of its group.
 // Returns false when the step is drained after an error.
-// GM >= G: the heads of a group are processed GM at a time as independent
-// dependency chains (heads G..GM-1, when present, compute unused values).
-template <int HD, int GM>
+template <int HD>
 DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
                   WState &ws) {
   const int tix = t.gidx;
@@ -1853,11 +1834,9 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
 
   const int pos = uni(ldg(ca.positions + b));
   const size_t head0 = ((size_t)l * B + b) * nq + (size_t)g * G;  // first head row
-  constexpr int DQ = HD / 4;                  // key dims per lane
-  constexpr int KV4 = DQ / 8;                 // 16-byte loads per lane
-  constexpr int VPOS = HD == 128 ? 16 : 8;    // value rows per lane
-  const int tq = lane >> 2, qd = lane & 3;
-  const int vdim = HD == 128 ? 2 * lane : 2 * (lane & 31);
+  constexpr int KB = HD / 32;  // 32-dim blocks of a key row: score products per page
+  constexpr int NB = HD / 16;  // 16-dim blocks of a value row: output products per pair
+  const int r16 = lane & 15, grp = lane >> 4;
   const bool pos_ok = pos >= 0 && pos < d.max_pos;
   const int n = pos + 1;
   const int lo = pos_ok ? (int)((int64_t)sp * n / S) : 0;
@@ -1871,30 +1850,40 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     const int i = c0 + lane;
     return i < npw ? ldg(ptab + (size_t)i * kWaves) : -1;
   };
-  u32x4 kA[KV4], kB[KV4];
-  uint32_t vA[VPOS], vB[VPOS];
-  // keys (lane: position tq, dims qd*DQ ..) and values (lane: dims vdim,
-  // vdim+1 of its VPOS positions) of page i of the current id chunk
-  auto load_page = [&](int pid, int i, u32x4 *kr, uint32_t *vr) {
+  // The wave's pages are taken in pairs.  Keys of a page are the A operand
+  // of the score products (lane: position r16, dims kb*32 + 8*grp .. +8, one
+  // 16-byte load per k-block); the values of a pair are the B operand of the
+  // output products (lane: dim nn*16 + r16 of the pair's first page for
+  // lanes 0-31, of its second for 32-63, positions 8*(grp&1) .. +8: the
+  // value pool is transposed within a page, so that is one 16-byte load).
+  u32x4 kq[2][KB], vq[NB];
+  auto page_base = [&](int pid, int i) -> size_t {
     int pg = __builtin_amdgcn_readlane(pid, i);
     pg = pg >= 0 && pg < d.npages ? pg : 0;  // a bad id is reported before use
-    const size_t pbase = (((size_t)l * d.npages + pg) * nkv + g) * kPageSize * HD;
+    return (((size_t)l * d.npages + pg) * nkv + g) * kPageSize * HD;
+  };
+  auto load_keys = [&](int pid, int i, u32x4 (&kr)[KB]) {
+    const size_t pb = page_base(pid, i);
 #pragma unroll
-    for (int k = 0; k < KV4; ++k)
-      kr[k] = ldg((const u32x4 *)(d.k_pool + pbase + tq * HD + qd * DQ + k * 8));
+    for (int kb = 0; kb < KB; ++kb)
+      kr[kb] = ldg((const u32x4 *)(d.k_pool + pb + r16 * HD + kb * 32 + 8 * grp));
+  };
+  auto load_values = [&](int pid, int i0, int i1) {
+    const size_t pa = page_base(pid, i0), pz = page_base(pid, i1);
+    const size_t pb = lane < 32 ? pa : pz;
 #pragma unroll
-    for (int k = 0; k < VPOS; ++k) {
-      const int tt = HD == 128 ? k : 2 * k + (lane >> 5);
-      vr[k] = ldg((const uint32_t *)(d.v_pool + pbase + tt * HD + vdim));
-    }
+    for (int nn = 0; nn < NB; ++nn)
+      vq[nn] = ldg((const u32x4 *)(d.v_pool + pb + (size_t)(nn * 16 + r16) * kPageSize +
+                                   8 * (grp & 1)));
   };
   // (Everything loaded here has arrived before the page loop: the task's
   // own input loads after the wait are waited for in order.)
   int pid = -1;
   if (npw > 0) {
     pid = page_ids(0);
-    load_page(pid, 0, kA, vA);
-    if (npw > 1) load_page(pid, 1, kB, vB);
+    load_keys(pid, 0, kq[0]);
+    load_keys(pid, min(1, npw - 1), kq[1]);
+    load_values(pid, 0, min(1, npw - 1));
   }
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   if (!pos_ok) {
@@ -1943,10 +1932,10 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
       kc[i] = bf1(kb);
       vc[i] = bf1(vb);
       if (pg_ok) {
-        const size_t off =
-            ((((size_t)l * d.npages + pg) * nkv + g) * kPageSize + (pos & (kPageSize - 1))) * HD + i;
-        stg(d.k_pool + off, kb);
-        stg(d.v_pool + off, vb);
+        const size_t page = ((size_t)l * d.npages + pg) * nkv + g;
+        const int ps = pos & (kPageSize - 1);
+        stg(d.k_pool + (page * kPageSize + ps) * HD + i, kb);
+        stg(d.v_pool + (page * HD + i) * kPageSize + ps, vb);  // [dim][position]
       }
     }
   }
@@ -1955,94 +1944,38 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   trace_start(d, t);  // inputs complete
   trace_mark(d, t, 0);
 
-  // --- page loop
-  float m[GM], ls[GM], o0[GM], o1[GM];
+  // --- page loop (matrix cores)
+  // Queries as the B operand of the score products: lane = head r16 (zero
+  // past G), dims kb*32 + 8*grp .. +8, as a bf16 value and a bf16 remainder
+  // (two products keep about 16 bits of the fp32 query).
+  bf16x8 qh[KB], ql[KB];
+  {
+    const int hq = r16 < G ? r16 : 0;
 #pragma unroll
-  for (int h = 0; h < GM; ++h) { m[h] = -INFINITY; ls[h] = 0.f; o0[h] = 0.f; o1[h] = 0.f; }
-  // online softmax over the 16 positions of page i of this wave; every step
-  // runs for all GM heads before the next (independent chains, no branches)
-  auto consume = [&](int i, const u32x4 *kr, const uint32_t *vr) {
-    const int p = (blk0 + wave + i * kWaves) * kPageSize + tq;
-    const bool valid = p >= lo && p < chi;
-    float sc[GM];
+    for (int kb = 0; kb < KB; ++kb) {
+      const int d0 = kb * 32 + 8 * grp;
+      const float *qp = qs + hq * QROW + (d0 / (HD / 4)) * QQ + (d0 & (HD / 4 - 1));
+      f32x8 x;
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      const float *qh = qs + h * QROW + qd * QQ;
-      float pk[KV4];  // one short chain per 16-byte key load
-#pragma unroll
-      for (int k = 0; k < KV4; ++k) {
-        const f32x4 x0 = *(const f32x4 *)(qh + k * 8), x1 = *(const f32x4 *)(qh + k * 8 + 4);
-        float c = bf_lo(kr[k].x) * x0.x;
-        c = fmaf(bf_hi(kr[k].x), x0.y, c);
-        c = fmaf(bf_lo(kr[k].y), x0.z, c);
-        c = fmaf(bf_hi(kr[k].y), x0.w, c);
-        c = fmaf(bf_lo(kr[k].z), x1.x, c);
-        c = fmaf(bf_hi(kr[k].z), x1.y, c);
-        c = fmaf(bf_lo(kr[k].w), x1.z, c);
-        c = fmaf(bf_hi(kr[k].w), x1.w, c);
-        pk[k] = c;
-      }
-      float a = pk[0];
-#pragma unroll
-      for (int k = 1; k < KV4; ++k) a += pk[k];
-      sc[h] = a;
-      // two heads at a time: their query slices (2 x DQ floats) stay in
-      // registers, not all GM heads' at once
-      if (h & 1) __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < 8; ++e) x[e] = r16 < G ? qp[e] : 0.f;
+      qh[kb] = __builtin_convertvector(x, bf16x8);
+      ql[kb] = __builtin_convertvector(x - __builtin_convertvector(qh[kb], f32x8), bf16x8);
     }
+  }
+  // Online softmax in base 2 per head: lane r16's head; its running max and
+  // sum are kept in the four lanes of the head (one per 16-lane group).  The
+  // outputs o[nn] hold heads 4*grp + j, dims nn*16 + r16.
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[NB];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      const float a = quad_sum(sc[h]);
-      sc[h] = valid ? a : -INFINITY;
-    }
-    float pe[GM];
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      const float mn = fmaxf(m[h], quads_max(sc[h]));
-      const bool live = mn != -INFINITY;
-      const float alpha = live ? exp2f(m[h] - mn) : 1.f;
-      pe[h] = live ? exp2f(sc[h] - mn) : 0.f;
-      m[h] = live ? mn : m[h];
-      ls[h] *= alpha;
-      o0[h] *= alpha;
-      o1[h] *= alpha;
-    }
-#pragma unroll
-    for (int h = 0; h < GM; ++h) ls[h] += quads_sum(pe[h]);
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      // two chains per output (even / odd positions)
-      float a0 = o0[h], a1 = o1[h], b0 = 0.f, b1 = 0.f;
-#pragma unroll
-      for (int k = 0; k < VPOS; ++k) {
-        float pt;
-        if (HD == 128) {
-          pt = lanef(pe[h], k * 4);
-        } else {  // lanes 0-31 take even positions, 32-63 odd ones
-          const float pe_even = lanef(pe[h], 8 * k), pe_odd = lanef(pe[h], 8 * k + 4);
-          pt = (lane >> 5) ? pe_odd : pe_even;
-        }
-        if (k & 1) {
-          b0 = fmaf(pt, bf_lo(vr[k]), b0);
-          b1 = fmaf(pt, bf_hi(vr[k]), b1);
-        } else {
-          a0 = fmaf(pt, bf_lo(vr[k]), a0);
-          a1 = fmaf(pt, bf_hi(vr[k]), a1);
-        }
-      }
-      o0[h] = a0 + b0;
-      o1[h] = a1 + b1;
-    }
-  };
-  // Inside the loop no load is skipped by a branch (a page past the end
-  // re-reads the last one): a load that a branch may skip makes the compiler
-  // wait for every load in flight instead of one buffer's.
+  for (int nn = 0; nn < NB; ++nn) o[nn] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < npw; c0 += 64) {
     const int nc = min(64, npw - c0);
     if (c0 > 0) {
       pid = page_ids(c0);
-      load_page(pid, 0, kA, vA);
-      load_page(pid, min(1, nc - 1), kB, vB);
+      load_keys(pid, 0, kq[0]);
+      load_keys(pid, min(1, nc - 1), kq[1]);
+      load_values(pid, 0, min(1, nc - 1));
     }
     const uint64_t bad = __ballot(lane < nc && (pid < 0 || pid >= d.npages));
     if (bad) {
@@ -2050,26 +1983,92 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
         set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pid, (uint32_t)d.npages);
       break;
     }
-    int i = 0;
-    for (; i + 2 < nc; i += 2) {
-      consume(c0 + i, kA, vA);
-      load_page(pid, i + 2, kA, vA);
-      consume(c0 + i + 1, kB, vB);
-      load_page(pid, min(i + 3, nc - 1), kB, vB);
-    }
-    consume(c0 + i, kA, vA);
-    if (i + 1 < nc) consume(c0 + i + 1, kB, vB);
-  }
-  // per-wave state to LDS
+    for (int i = 0; i < nc; i += 2) {
+      // scores of pages i, i+1: lane = head r16, positions 4*grp + j
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    if (h >= G) break;
-    float a0 = o0[h], a1 = o1[h];
-    if (HD == 64) { a0 += __shfl_xor(a0, 32, 64); a1 += __shfl_xor(a1, 32, 64); }
-    if (lane == 0) { wm[wave * kMaxGroup + h] = m[h]; wl[wave * kMaxGroup + h] = ls[h]; }
-    if (HD == 128 || lane < 32) {
-      wo[(wave * kMaxGroup + h) * HD + vdim] = a0;
-      wo[(wave * kMaxGroup + h) * HD + vdim + 1] = a1;
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, kq[0][kb]);
+        const bf16x8 kz = __builtin_bit_cast(bf16x8, kq[1][kb]);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[kb], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kz, qh[kb], sb, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[kb], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kz, ql[kb], sb, 0, 0, 0);
+      }
+      // the next pair's keys (no load is skipped by a branch: past the end
+      // the last page is read again)
+      const int n0 = min(i + 2, nc - 1), n1 = min(i + 3, nc - 1);
+      load_keys(pid, n0, kq[0]);
+      load_keys(pid, n1, kq[1]);
+      const int pa = (blk0 + wave + (c0 + i) * kWaves) * kPageSize + 4 * grp;
+      const int pz = pa + kWaves * kPageSize;
+      const bool has_z = i + 1 < nc;
+      float sc[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sc[j] = pa + j >= lo && pa + j < chi ? sa[j] : -INFINITY;
+        sc[4 + j] = has_z && pz + j >= lo && pz + j < chi ? sb[j] : -INFINITY;
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m_run, mx);
+      const bool live = mn != -INFINITY;
+      const float alpha = live ? exp2f(m_run - mn) : 1.f;
+      float pe[8], rs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pe[e] = live ? exp2f(sc[e] - mn) : 0.f;
+        rs += pe[e];
+      }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      l_run = l_run * alpha + rs;
+      m_run = live ? mn : m_run;
+      // rescale the outputs of heads 4*grp + j (their factors sit in lanes
+      // 4*grp + j)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float aj = __shfl(alpha, 4 * grp + j, 64);
+#pragma unroll
+        for (int nn = 0; nn < NB; ++nn) o[nn][j] *= aj;
+      }
+      // the weights as the A operand of the output products: lane = head
+      // r16, positions 8*grp .. +8 of the pair (grp 0-1: first page, 2-3:
+      // second), gathered from the lanes holding them
+      const int src0 = r16 + 32 * (grp & 1), src1 = src0 + 16;
+      f32x8 pv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a0 = __shfl(pe[j], src0, 64), z0 = __shfl(pe[4 + j], src0, 64);
+        const float a1 = __shfl(pe[j], src1, 64), z1 = __shfl(pe[4 + j], src1, 64);
+        pv[j] = grp < 2 ? a0 : z0;
+        pv[4 + j] = grp < 2 ? a1 : z1;
+      }
+      const bf16x8 ph = __builtin_convertvector(pv, bf16x8);
+      const bf16x8 pl = __builtin_convertvector(pv - __builtin_convertvector(ph, f32x8), bf16x8);
+#pragma unroll
+      for (int nn = 0; nn < NB; ++nn) {
+        const bf16x8 vv = __builtin_bit_cast(bf16x8, vq[nn]);
+        o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vv, o[nn], 0, 0, 0);
+        o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vv, o[nn], 0, 0, 0);
+      }
+      load_values(pid, n0, n1);  // the next pair's values
+    }
+  }
+  // per-wave state to LDS: lane h < G holds head h's max and sum
+  if (lane < G) {
+    wm[wave * kMaxGroup + lane] = m_run;
+    wl[wave * kMaxGroup + lane] = l_run;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = 4 * grp + j;
+    if (h < G) {
+#pragma unroll
+      for (int nn = 0; nn < NB; ++nn) wo[(wave * kMaxGroup + h) * HD + nn * 16 + r16] = o[nn][j];
     }
   }
   if (has_cur && wave < G) {  // score of the current key for head `wave`
@@ -2233,9 +2232,8 @@ DEV void run_argmax(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
 // stores, then thread 0 reports).
 DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent, WState &ws) {
   if (t.op == OP_ATTN) {  // waits for its inputs itself, after a prefetch
-    const bool ok = d.hd == 128 ? (d.G <= 4 ? run_attn<128, 4>(sm, d, ca, t, persistent, ws)
-                                            : run_attn<128, 8>(sm, d, ca, t, persistent, ws))
-                                : run_attn<64, 8>(sm, d, ca, t, persistent, ws);
+    const bool ok = d.hd == 128 ? run_attn<128>(sm, d, ca, t, persistent, ws)
+                                : run_attn<64>(sm, d, ca, t, persistent, ws);
     if (!ok) return false;
   } else {
     if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;

@@ -1,8 +1,9 @@
 """Paged KV-cache buffers for the megakernel (device memory via torch).
 
-Pool layout (bf16): [n_layers][n_pages][n_kv_heads][16][head_dim]; the page
-table (int32 [max_batch][max_pages_per_seq]) maps (slot, position // 16) to a
-pool page.  Pages are handed out from a seeded random permutation of the pool
+Pool layouts (bf16): keys [n_layers][n_pages][n_kv_heads][16][head_dim],
+values [n_layers][n_pages][n_kv_heads][head_dim][16] (transposed within a
+page); the page table (int32 [max_batch][max_pages_per_seq]) maps (slot,
+position // 16) to a pool page.  Pages are handed out from a seeded random permutation of the pool
 ("shuffled page tables").
 """
 from __future__ import annotations
@@ -19,9 +20,10 @@ class PagedKV:
         L, nkv, hd = model["n_layers"], model["n_kv_heads"], model["head_dim"]
         self.model, self.B, self.maxp = model, max_batch, max_pages_per_seq
         self.n_pages = n_pages if n_pages is not None else max_batch * max_pages_per_seq
-        shape = (L, self.n_pages, nkv, PAGE, hd)
-        self.k_pool = torch.zeros(shape, dtype=torch.bfloat16, device=device)
-        self.v_pool = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        self.k_pool = torch.zeros((L, self.n_pages, nkv, PAGE, hd), dtype=torch.bfloat16,
+                                  device=device)
+        self.v_pool = torch.zeros((L, self.n_pages, nkv, hd, PAGE), dtype=torch.bfloat16,
+                                  device=device)
         g = torch.Generator()
         g.manual_seed(int(seed))
         order = (torch.randperm(self.n_pages, generator=g) if shuffle
@@ -73,7 +75,7 @@ class PagedKV:
         slots = (pos % PAGE).to(self.k_pool.device)
         # advanced indices (pages, slots) put the token axis first
         self.k_pool[:, pages, :, slots, :] = K.to(self.k_pool.device).permute(1, 0, 2, 3)
-        self.v_pool[:, pages, :, slots, :] = V.to(self.v_pool.device).permute(1, 0, 2, 3)
+        self.v_pool[:, pages, :, :, slots] = V.to(self.v_pool.device).permute(1, 0, 2, 3)
 
     def read_tokens(self, slot: int, n: int):
         """Keys/values of positions 0..n-1 of a slot: bf16 [L, n, nkv, hd]."""
@@ -81,5 +83,5 @@ class PagedKV:
         pages = self.table_host[slot, pos // PAGE].long().to(self.k_pool.device)
         slots = (pos % PAGE).to(self.k_pool.device)
         k = self.k_pool[:, pages, :, slots, :].permute(1, 0, 2, 3)
-        v = self.v_pool[:, pages, :, slots, :].permute(1, 0, 2, 3)
+        v = self.v_pool[:, pages, :, :, slots].permute(1, 0, 2, 3)
         return k, v
