@@ -346,11 +346,12 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   p.max_pos = c.max_pages_per_seq * kPageSize;
 
   // attention splits: enough (slot, KV head, split) tasks to cover the CUs,
-  // but at least about 64 keys per split
+  // but at least 128 keys per split (a page for each of a task's waves) and
+  // at most 256 partials (G heads x S splits) for the merging split to read
   int ctx = o.planned_ctx > 0 ? std::min(o.planned_ctx, p.max_pos) : p.max_pos;
   int want = std::max(1, n_cus / (nkv * B));
-  int by_len = std::max(1, ctx / 64);
-  p.S = std::max(1, std::min(std::min(want, by_len), 64));
+  int by_len = std::max(1, ctx / 128);
+  p.S = std::max(1, std::min({want, by_len, std::max(1, 256 / (nq / nkv)), 64}));
   // Large batches (Cohere "Folyamatos batchkezelés": sequences of different
   // and changing lengths): the persistent workers claim a layer's attention
   // tasks at run time from a shared counter; about two tasks per worker, at
