@@ -465,7 +465,7 @@ DEV void dma16(uint64_t src, uint32_t lds_base) {
                : "memory", "m0");
 }
 // All kLdsSlots slots of a pass at once: the last slot's DMA (and so every
-// earlier one) is complete once only the kMaxChunks register refills issued
+// earlier one) is complete once only the kMaxChunks register reloads issued
 // after it remain; then four reads at a time, each group waited for in its
 // own statement.
 DEV void take_slots(uint32_t a, u32x4 (&v)[kLdsSlots]) {
@@ -515,22 +515,20 @@ DEV float row16_sum(float v) {
 }
 
 // Compute wave cw: the partials of its chunks with the staged activations xs
-// of one slot into part[4*chunk + DPP row].  When `pre`, each slot is
-// refilled with the next tile `gn` as soon as it has been used, so the next
-// tile streams in while this one is consumed.  The body is straight-line
-// code (uniform branches only), which lets the compiler wait for each slot
-// with "all but the newest loads done" instead of draining the queue.
-DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, bool pre,
-                   const Geo &gn, bool lds) {
+// of one slot into part[4*chunk + DPP row].  Each slot is reloaded with the
+// same slot of `gn` as soon as it has been used (the idle line where gn has
+// no such chunk), so the next pass streams in while this one is consumed.
+// The body is straight-line code (uniform branches only), which lets the
+// compiler wait for each slot with "all but the newest loads done" instead
+// of draining the queue.
+DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, const Geo &gn,
+                   bool lds) {
   const int lane = tidx() & 63;
   const int cnt = cw_chunks(g, cw);
   const int q0 = cw * g.cpw;
   int col = (int)(((uint32_t)q0 * 512u + (uint32_t)lane * 8u) % (uint32_t)g.K);
   float *pp = part + q0 * 4 + (lane >> 4);
   const bool writer = (lane & 15) == 0;
-  // without a next tile the slots load the idle line
-  const Geo &gr = pre ? gn : g;
-  const int crw = pre ? cw : 0;
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
     if (j < cnt) {
@@ -539,12 +537,12 @@ DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, b
       col += g.step;
       col = col >= g.K ? col - g.K : col;
     }
-    w[j] = ldnt((const u32x4 *)(pre ? slot_addr(gr, crw, j) : idle_addr()));
-    __builtin_amdgcn_sched_barrier(0);  // keep each refill right after its use
+    w[j] = ldnt((const u32x4 *)slot_addr(gn, cw, j));
+    __builtin_amdgcn_sched_barrier(0);  // keep each reload right after its use
   }
   if (lds) {
     u32x4 v[kLdsSlots];
-    take_slots(wslot(xs, cw, 0) + (uint32_t)(tidx() & 63) * 16u, v);
+    take_slots(wslot(xs, cw, 0) + (uint32_t)lane * 16u, v);
 #pragma unroll
     for (int s = 0; s < kLdsSlots; ++s) {
       const int j = kMaxChunks + s;
@@ -556,8 +554,7 @@ DEV void gemv_dot1(const Geo &g, Buf &w, const float *xs, float *part, int cw, b
       }
     }
 #pragma unroll
-    for (int s = 0; s < kLdsSlots; ++s)
-      dma16(pre ? slot_addr(gr, crw, kMaxChunks + s) : idle_addr(), wslot(xs, cw, s));
+    for (int s = 0; s < kLdsSlots; ++s) dma16(slot_addr(gn, cw, kMaxChunks + s), wslot(xs, cw, s));
   }
 }
 
@@ -1113,12 +1110,16 @@ DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
 }
 
 // Compute waves: stream the task's passes through `w` (holding the first
-// pass when w_loaded), refilling each slot right after its use with the next
-// pass, and after the last pass with the first pass of the next task `gn`
-// when `pre`; then the row sums.
+// pass when w_loaded), reloading each slot right after its use with the next
+// pass; then the row sums.  When `pre`, the first pass of the next task `gn`
+// follows: interleaved with the last pass when `inter` (the next task waits
+// only for this task's operation), else, in single-slot plans, issued once
+// the row sums are written, so that this task's outputs, and the chain of
+// operations behind them that the next task waits for, are not held behind
+// its loads.
 template <bool B1>
 DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
-                  WState &ws, Buf &w, bool w_loaded, bool pre, const Geo &gn) {
+                  WState &ws, Buf &w, bool w_loaded, bool pre, const Geo &gn, bool inter) {
   const int cw = uni(tidx() >> 6) - 1;
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t, ws);
@@ -1139,21 +1140,28 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     // The first pass was loaded before the task; waiting for all of it here
     // lets the pass loop wait per slot for the loads it issues itself.
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    // every pass reloads its slots with the next pass; the last one with the
+    // next task only when interleaved, else with the idle line (a slot chunk
+    // before the last keeps its single pass for the next chunk)
+    const bool defer = B1 && !inter;  // (multi-slot tiles measured better without)
+    const bool tail = pre && last && !defer;
+    Geo idle = gn;
+    idle.units = 0;
+    idle.cpw = 0;
     for (int p = 0; p < q.P; ++p) {
-      const Geo gp = geo_of(p);
       const bool lastp = p + 1 == q.P;
-      const Geo gq = lastp ? gn : geo_of(p + 1);
-      const bool pre_p = lastp ? (pre && last) : true;
+      const Geo gq = !lastp ? geo_of(p + 1) : tail ? gn : idle;
       if (B1 || n == 1) {
-        gemv_dot1(gp, w, sm.xs, red + p * kPartSlot, cw, pre_p, gq, lds);
+        gemv_dot1(geo_of(p), w, sm.xs, red + p * kPartSlot, cw, gq, lds);
       } else {
-        gemv_dotn(gp, w, sm.xs, n, red + p * n * kPartSlot, cw);
-        if (pre_p) load_slots(gq, w, cw, sm.xs, false);
+        gemv_dotn(geo_of(p), w, sm.xs, n, red + p * n * kPartSlot, cw);
+        if (!lastp || tail) load_slots(gq, w, cw, sm.xs, false);
       }
     }
     __syncthreads();  // partials complete
     gemv_rows(K, q.P, [&](int p) { return geo_of(p).units * 512 / K; }, red, rsum, n, cw);
     __syncthreads();  // row sums complete
+    if (pre && last && defer) load_slots(gn, w, cw, sm.xs, lds);  // (outputs being written)
     if (n < q.nb) {
       ws.x_src = nullptr;
       __syncthreads();
@@ -2332,8 +2340,28 @@ DEV void run_task_once(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState 
   } else {
     Buf w;
     Geo gn;
-    gemv_cmp<false>(sm, d, ca, t, false, ws, w, false, false, gn);
+    gemv_cmp<false>(sm, d, ca, t, false, ws, w, false, false, gn, false);
   }
+}
+
+// Whether the task with descriptor words `nx` waits for nothing but what the
+// task `cur` reports (another tile of the same operation, or a direct
+// consumer): its first pass is then loaded while `cur` finishes.  A task
+// that waits for a later operation (the output projection behind attention)
+// gets its loads after `cur`'s outputs, which its wait leaves time for.
+// Words: 0 op | layer << 16, 1 n_wait | n_sig << 16, 8-10 waited events,
+// 14-15 signalled events.
+DEV bool waits_on(const uint32_t *nx, const uint32_t *cur) {
+  const int w0 = uni((int)nx[0]), c0 = uni((int)cur[0]);
+  if (w0 == c0) return true;
+  const int nw = uni((int)(nx[1] & 0xffffu)), ns = uni((int)(cur[1] >> 16));
+  for (int i = 0; i < nw && i < 3; ++i) {
+    const int e = uni((int)nx[8 + i]);
+    bool found = false;
+    for (int j = 0; j < ns && j < 2; ++j) found = found || e == uni((int)cur[14 + j]);
+    if (!found) return false;
+  }
+  return nw > 0;
 }
 
 // Geometry of the next task's first pass from its descriptor words in the
@@ -2436,8 +2464,10 @@ __global__ void __launch_bounds__(kThreads)
       load_slots(static_geo(t), w, cw, sm.xs, d.lds_slots != 0);
       for (;;) {
         Geo gn;
-        const bool pre = k + 1 < end && next_geo(sm.ring[(k + 1 - beg) % kRing], gn);
-        if (!gemv_cmp<B1>(sm, d, ca, t, true, ws, w, true, pre, gn)) goto done;
+        const uint32_t *nx = sm.ring[(k + 1 - beg) % kRing];
+        const bool pre = k + 1 < end && next_geo(nx, gn);
+        const bool inter = pre && waits_on(nx, sm.ring[(k - beg) % kRing]);
+        if (!gemv_cmp<B1>(sm, d, ca, t, true, ws, w, true, pre, gn, inter)) goto done;
         refill(k);
         ++k;
         if (!pre) break;
@@ -2459,7 +2489,7 @@ __global__ void __launch_bounds__(kThreads)
       } else if (is_gemv(t.op)) {
         Buf w;
         Geo gn;
-        alive = gemv_cmp<B1>(sm, d, ca, t, true, ws, w, false, false, gn);
+        alive = gemv_cmp<B1>(sm, d, ca, t, true, ws, w, false, false, gn, false);
       } else {
         alive = run_small(sm, d, ca, t, true, ws);
       }
