@@ -236,7 +236,7 @@ static int add_gemv_mfma(Builder &b, int op, int layer, const std::vector<RowSeg
 // register tile.
 int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int K, int nseg,
              int n_workers, int pmax, int wait_ev, int64_t extra_bytes, int *lm_index,
-             int min_unit = 1, int early_ev = -1) {
+             int min_unit = 1, int early_ev = -1, const std::vector<int> *only = nullptr) {
   const int64_t row_bytes = (int64_t)nseg * K * 2;
   int unit = 1;
   while ((row_bytes * unit) % 1024 || unit % min_unit) ++unit;
@@ -302,12 +302,15 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
     }
     return added;
   }
+  // (a single matrix: the workers in `only` when given, else all of them)
+  const int nw = only ? (int)only->size() : n_workers;
   size_t si = 0;
   int64_t seg_base = 0;  // rows before segs[si]
-  for (int w = 0; w < n_workers; ++w) {
-    int64_t lo = total * w / n_workers, hi = total * (w + 1) / n_workers;
+  for (int i = 0; i < nw; ++i) {
+    const int w = only ? (*only)[i] : i;
+    int64_t lo = total * i / nw, hi = total * (i + 1) / nw;
     lo -= lo % unit;
-    hi = (w + 1 == n_workers) ? total : hi - hi % unit;
+    hi = (i + 1 == nw) ? total : hi - hi % unit;
     while (lo < hi) {
       while (lo >= seg_base + segs[si].rows) seg_base += segs[si++].rows;
       const RowSeg &sg = segs[si];
@@ -420,6 +423,21 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     b.add(OP_EMBED, 0, s, 0, 0, 0, 0, {}, {x_ev[0]}, (int64_t)H * 2);
 
   const int G = p.G;
+  // When a layer's attention tasks fill at most a quarter of the workers and
+  // a worker's share of the output projection is one pass, attention runs
+  // on workers of their own (the highest indices, which spread over the
+  // XCDs) and the projection's rows go to the others: a worker that runs
+  // attention cannot load its projection rows ahead, so its share would
+  // finish last and hold back the next operation.  (Longer shares stream
+  // mostly after the wait anyway; there the attention workers would idle.)
+  const int n_attn = B * nkv * p.S;
+  const int64_t oproj_share = (int64_t)H * nq * hd * 2 / n_workers;
+  std::vector<int> attn_w, oproj_w;
+  if (!p.mfma && !p.attn_pool && n_attn * 4 <= n_workers &&
+      oproj_share * n_workers / (n_workers - n_attn) <= (int64_t)p.tile_units * 1024) {
+    for (int i = 0; i < n_attn; ++i) attn_w.push_back(n_workers - 1 - i);
+    for (int w = 0; w < n_workers - n_attn; ++w) oproj_w.push_back(w);
+  }
   for (int l = 0; l < L; ++l) {
     // QKV, group by group so a KV head's attention can start early
     std::vector<int> grp(nkv);
@@ -446,7 +464,8 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     for (int s = 0; s < B; ++s)
       for (int g = 0; g < nkv; ++g)
         for (int sp = 0; sp < p.S; ++sp)
-          b.add(OP_ATTN, l, s, g, sp, 0, 0, {grp[g]}, {mrg}, 0);
+          b.add(OP_ATTN, l, s, g, sp, 0, 0, {grp[g]}, {mrg}, 0,
+                attn_w.empty() ? -1 : attn_w[(s * nkv + g) * p.S + sp]);
     if (p.S > 1) p.ev_thr[mrg] = B * nkv;  // one merged group per (slot, KV head)
     // O projection + residual
     int xo = b.ev();
@@ -454,7 +473,7 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     data_ev.push_back(xo);
     b.begin_phase();
     if (add_gemv(b, OP_OPROJ, l, {{0, 0, H, xo}}, nq * hd, 1, n_workers, pmax_for(nq * hd), mrg,
-                 0, nullptr) < 0)
+                 0, nullptr, 1, -1, oproj_w.empty() ? nullptr : &oproj_w) < 0)
       ok = false;
     if (!moe) {
       int hev = b.ev();
