@@ -296,8 +296,9 @@ def main():
     ap.add_argument("--attn-splits", type=int, default=None,
                     help="KV splits per (sequence, KV head); default: the planner's choice")
     ap.add_argument("--kpo-steps", type=int, default=64, help="kernel-per-op comparison steps")
-    ap.add_argument("--no-weight-lds", action="store_true",
-                    help="keep GEMV passes in registers only (no LDS weight slots)")
+    ap.add_argument("--weight-lds", choices=("auto", "on", "off"), default="auto",
+                    help="LDS weight slots of single-slot GEMV passes (auto: the planner's choice)")
+    ap.add_argument("--no-weight-lds", action="store_true", help="the same as --weight-lds off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kpo", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -350,8 +351,10 @@ def main():
 
     def build(executor, graph_replay=0):
         extra = {} if args.attn_splits is None else {"attn_splits": args.attn_splits}
-        if args.no_weight_lds:
+        if args.no_weight_lds or args.weight_lds == "off":
             extra["weight_lds"] = -1
+        elif args.weight_lds == "on":
+            extra["weight_lds"] = 1
         return mk.Plan(model, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=1,
                        opts=mk.default_options(executor=executor, planned_ctx=total,
                                                graph_replay=graph_replay, **extra))
