@@ -1754,9 +1754,9 @@ DEV bool gemv_mfma_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
 DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
                        WState &ws, Buf &w, bool w_loaded, bool pre, const MGeo &gn) {
   const int cw = uni(tidx() >> 6) - 1, lane = tidx() & 63;
-  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   const MGeo g = mgeo_of(d, t);
-  if (!w_loaded) mload(g, w, cw);
+  if (!w_loaded) mload(g, w, cw);  // weights do not wait for the inputs
+  if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   f32x4 acc[2][4];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -2450,10 +2450,11 @@ __global__ void __launch_bounds__(kThreads)
   while (k < end) {
     TD t = td_from_ring(sm.ring[(k - beg) % kRing]);
     if (MODE == 2 && static_weights(t.op)) {
-      // Matrix-core tiles load their first pass when they start: a phase
-      // ends with its slowest tile (split-K tiles wait for each other), and
-      // weights prefetched by the tiles that finish early would take
-      // bandwidth from it.
+      // Matrix-core tiles: each tile's last pass refills the idle line; the
+      // next tile issues its first pass before it waits for its inputs, so
+      // those weights stream during the wait.  (Refilling with the next
+      // tile during the last pass would hold this tile's end behind the
+      // issue of those loads.)
       Buf w;
       MGeo gn;
       if (!gemv_mfma_cmp(sm, d, ca, t, true, ws, w, false, false, gn)) goto done;
