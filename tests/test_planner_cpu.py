@@ -336,7 +336,7 @@ def test_gemv_shares_balanced_and_passes_fit():
             assert max(per_worker.values()) <= 1.1 * mean, op
             continue
         if op == "OPROJ":
-            # attention (40 tasks here: a sixth of the workers) runs on
+            # attention (one task per KV head at this short context) runs on
             # workers of its own, the projection's rows on all the others
             attn = {t.worker for t in tasks if mk.OPS[t.op] == "ATTN" and t.layer == layer}
             assert 0 < len(attn) <= 64 and not attn & set(per_worker), op
@@ -441,3 +441,17 @@ def test_lds_weight_slots_only_where_the_stage_leaves_room():
     assert max_pass(LLAMA8B, 4) <= 7 * 16 * 1024
     # MoE: off unless asked for
     assert max_pass(MOE30B, 1) <= 7 * 16 * 1024 < max_pass(MOE30B, 1, weight_lds=1)
+
+
+def test_single_split_for_short_single_sequence_contexts():
+    """One sequence whose context is at most 768 keys keeps one split per KV
+    head (no merge hop); longer contexts, and batches, keep the split count
+    that covers the CUs."""
+    def splits(ctx, B=1):
+        tasks, _ = mk.inspect_plan(_cfg(LLAMA8B, B=B, maxp=(ctx + 15) // 16),
+                                   mk.default_options(n_cus=256, planned_ctx=ctx))
+        return sum(1 for t in tasks if mk.OPS[t.op] == "ATTN" and t.layer == 0 and t.a0 == 0
+                   and t.a1 == 0)
+    assert splits(551) == 1 and splits(768) == 1
+    assert splits(769) == 6 and splits(1047) == 8
+    assert splits(768, B=4) > 1
