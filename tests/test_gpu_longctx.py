@@ -5,7 +5,10 @@ keys and values, the same values given to the oracle's cache).
 With one attention split per KV head, every wave of an attention task walks
 more than 64 pages, so the page-id chunks after the first are taken; the
 automatic split count is checked at the same contexts.  The full 131072-token
-context of the long-context workload is one of the cases.
+context of the long-context workload is one of the cases; one case keeps the
+GEMV passes in registers only (no LDS weight slots), where a task whose next
+task waits behind attention loads that task's first pass after its own
+outputs.
 """
 import numpy as np
 import pytest
@@ -33,14 +36,16 @@ def _weights():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("ctx,splits", [(20000, 1), (20000, 0), (131064, 1), (131064, 0)])
-def test_long_context_attention_chunks(ctx, splits):
+@pytest.mark.parametrize("ctx,splits,lds", [(20000, 1, 0), (20000, 0, 0), (131064, 1, 0),
+                                            (131064, 0, 0), (20000, 0, -1)])
+def test_long_context_attention_chunks(ctx, splits, lds):
+    """lds = -1: GEMV passes in registers only (no LDS weight slots)."""
     Wd, Wt = _weights()
-    print(f"longctx: ctx {ctx} splits {splits or 'auto'}", flush=True)
+    print(f"longctx: ctx {ctx} splits {splits or 'auto'} weight_lds {lds}", flush=True)
     K, V = synth.make_kv_values(CFG, ctx, device="cuda")
     steps = 3
     r = Runner(CFG, Wd, B=1, maxp=(ctx + steps + 15) // 16, planned_ctx=ctx + steps,
-               attn_splits=splits)
+               attn_splits=splits, weight_lds=lds)
     r.kv.write_tokens(0, K, V)
     Kh = synth.bf16_to_f32_np(synth.to_numpy_bf16(K))
     Vh = synth.bf16_to_f32_np(synth.to_numpy_bf16(V))
