@@ -305,8 +305,9 @@ def main():
                     help="run a plain 1 GiB device copy (traffic-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
-                                   "(see the sharding notes in the design document)"}))
+        print(json.dumps({"error": "the decode-step kernel runs on one GPU; --gpus above 1 is "
+                                   "not supported (the path would shard by tensor parallelism "
+                                   "across GPUs, which is not built)"}))
         sys.exit(2)
 
     import torch
