@@ -417,3 +417,139 @@ def test_argmax_ties_and_margin():
     assert O.greedy_argmax(lg) == 1
     assert O.top2_margin(lg) == 0.0
     assert abs(O.top2_margin(np.array([3.0, 1.0, 2.5])) - 0.5) < 1e-15
+
+
+# ------------------------------------------------- forced MoE routing -------
+# The forced branch of the oracle's MoE block re-runs a step with the expert
+# ids the device chose where the device took a legitimate near-tie decision
+# (the router's k-th and (k+1)-th logits nearly equal).  It is pinned here on
+# its own, since ordinary runs never take it.
+def _torch_moe_block(Wt, layer, b, ids):
+    """Independent torch composition of one MoE block with a given expert
+    set: router logits by torch, softmax over the chosen logits by torch,
+    expert SwiGLU MLPs by torch, summed in ascending expert id (float64)."""
+    bt = torch.from_numpy(np.asarray(b, dtype=np.float64))
+    r = torch.from_numpy(Wt.get("router", layer)) @ bt
+    ids = sorted(int(e) for e in ids)
+    w = torch.softmax(r[torch.tensor(ids)], 0)
+    y = torch.zeros_like(bt)
+    for we, e in zip(w, ids):
+        Wg = torch.from_numpy(Wt.get("e_gate", layer, e))
+        Wu = torch.from_numpy(Wt.get("e_up", layer, e))
+        Wd = torch.from_numpy(Wt.get("e_down", layer, e))
+        y = y + we * (Wd @ (F.silu(Wg @ bt) * (Wu @ bt)))
+    return y.numpy(), w.numpy()
+
+
+def test_moe_forced_own_routing_reproduces_unforced_exactly():
+    """Forcing the oracle's own expert ids, given in any order, must leave
+    every logit bit-identical (the forced ids are sorted and weighted from
+    the same router logits)."""
+    cfg = dict(_tiny_moe_cfg(E=8, k=3), n_layers=2)
+    W, Wt = _tiny_weights(cfg, np.float32)
+    toks = synth.make_prompt(6, cfg["vocab"]).tolist()
+    c0, c1 = O.KVCache(cfg), O.KVCache(cfg)
+    g = np.random.default_rng(5)
+    for p, t in enumerate(toks):
+        info = []
+        a = O.decode_step(Wt, cfg, c0, t, p, info=info)
+        forced = {d["layer"]: g.permutation(d["ids"]).tolist() for d in info}
+        info2 = []
+        b = O.decode_step(Wt, cfg, c1, t, p, forced_experts=forced, info=info2)
+        assert np.array_equal(a, b), p
+        for d1, d2 in zip(info, info2):
+            assert np.array_equal(d1["ids"], d2["ids"])
+            assert np.array_equal(d1["w"], d2["w"])
+
+
+def test_moe_forced_swap_matches_torch_composition():
+    """One routed expert swapped for an unrouted one: the block output and
+    the routing weights (softmax over the forced set's own router logits)
+    equal an independent torch composition; and the result differs from the
+    unforced block, so the override is not ignored."""
+    cfg = _tiny_moe_cfg(E=8, k=3)
+    W, Wt = _tiny_weights(cfg, np.float64)
+    b = RNG.standard_normal(64)
+    info = []
+    y0 = O.model._ffn(Wt, cfg, 0, b, np.float64, info=info)
+    own = info[0]["ids"].tolist()
+    out = [e for e in range(8) if e not in own]
+    for drop in range(3):
+        forced = [e for i, e in enumerate(own) if i != drop] + [out[drop]]
+        info = []
+        y = O.model._ffn(Wt, cfg, 0, b, np.float64, forced=forced[::-1], info=info)
+        ref, w_ref = _torch_moe_block(Wt, 0, b, forced)
+        assert info[0]["ids"].tolist() == sorted(forced)
+        assert np.allclose(info[0]["w"], w_ref, rtol=0, atol=1e-14)
+        assert np.max(np.abs(y - ref)) < 1e-12
+        assert np.max(np.abs(y - y0)) > 1e-6
+
+
+def test_moe_forced_layer_only_changes_that_layer():
+    """Forcing one layer's routing leaves the steps' earlier layers alone: a
+    forced swap in the last layer changes the logits, one in a layer whose
+    own ids are forced back unchanged does not."""
+    cfg = dict(_tiny_moe_cfg(E=8, k=2), n_layers=2)
+    W, Wt = _tiny_weights(cfg, np.float64)
+    info = []
+    base = O.decode_step(Wt, cfg, O.KVCache(cfg, np.float64), 3, 0, info=info)
+    own1 = info[1]["ids"].tolist()
+    swap = [own1[0], next(e for e in range(8) if e not in own1)]
+    info2 = []
+    got = O.decode_step(Wt, cfg, O.KVCache(cfg, np.float64), 3, 0,
+                        forced_experts={1: swap}, info=info2)
+    assert np.array_equal(info2[0]["ids"], info[0]["ids"])
+    assert info2[1]["ids"].tolist() == sorted(swap)
+    assert np.max(np.abs(got - base)) > 1e-6
+    same = O.decode_step(Wt, cfg, O.KVCache(cfg, np.float64), 3, 0,
+                         forced_experts={0: info[0]["ids"].tolist()})
+    assert np.array_equal(same, base)
+
+
+# ------------------------------------ 8B-shaped spot checks (2 layers) ------
+@pytest.fixture(scope="module")
+def llama8b_l2():
+    """The Llama-3-8B shape truncated to 2 layers (real per-layer shapes and
+    the full 128256-row LM head), generated on the CPU."""
+    cfg = synth.truncated(synth.MODELS["llama8b"], 2)
+    W = {k: synth.to_numpy_bf16(v) for k, v in synth.make_weights(cfg).items()}
+    return cfg, W
+
+
+@pytest.mark.slow
+def test_incremental_equals_full_recompute_llama8b_2layer(llama8b_l2):
+    """Incremental decode equals the full causal recompute on the 8B shape
+    (two layers), at every position of a 6-token sequence.  In fp32 with an
+    unrounded cache the two summation orders agree within 1e-4.  With the
+    bf16 cache a key computed in a different order can round to the other
+    bf16 neighbour (one such flip moves a logit by ~2e-4), so the bf16-cache
+    check runs in float64, where both orders give the same rounding."""
+    cfg, W = llama8b_l2
+    toks = synth.make_prompt(6, cfg["vocab"]).tolist()
+    for dtype, kv_bf16, tol in ((np.float32, False, 1e-4), (np.float64, True, 1e-9)):
+        Wt = O.OracleWeights(W, cfg, dtype)
+        full = O.forward_full(Wt, cfg, toks, kv_bf16=kv_bf16)
+        cache = O.KVCache(cfg, dtype, kv_bf16=kv_bf16)
+        for p, t in enumerate(toks):
+            lg = O.decode_step(Wt, cfg, cache, t, p)
+            assert np.max(np.abs(lg - full[p])) <= tol, (dtype, p)
+        del Wt
+
+
+@pytest.mark.slow
+def test_fp32_oracle_error_bound_llama8b_2layer(llama8b_l2):
+    """The fp32 oracle against its float64 shadow on the 8B shape (two
+    layers), cache unrounded: the working type's own error stays below 1e-4
+    in every logit, far under the 3e-2 parity bound."""
+    cfg, W = llama8b_l2
+    Wt32 = O.OracleWeights(W, cfg, np.float32)
+    Wt64 = O.OracleWeights(W, cfg, np.float64)
+    toks = synth.make_prompt(4, cfg["vocab"]).tolist()
+    c32 = O.KVCache(cfg, np.float32, kv_bf16=False)
+    c64 = O.KVCache(cfg, np.float64, kv_bf16=False)
+    worst = 0.0
+    for p, t in enumerate(toks):
+        a = O.decode_step(Wt32, cfg, c32, t, p)
+        b = O.decode_step(Wt64, cfg, c64, t, p)
+        worst = max(worst, float(np.max(np.abs(a.astype(np.float64) - b))))
+    assert worst < 1e-4, worst
