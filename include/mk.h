@@ -137,7 +137,13 @@ typedef struct {
                             dependency wait), possible when the staged
                             activations fit 72 KiB: 0 = auto (dense models),
                             1 = on, -1 = off                                 */
-  int32_t reserved[3];
+  int32_t debug_withhold; /* test hook: list index + 1 of one task whose counter
+                            signals the persistent executor withholds, so the
+                            waits on them end in MK_ERR_TIMEOUT after
+                            spin_budget (every workgroup still exits); cleared
+                            by the mk_plan_status call that reports the error.
+                            0 = none                                         */
+  int32_t reserved[2];
 } mk_plan_options;
 
 typedef struct mk_plan mk_plan;
@@ -182,6 +188,10 @@ void mk_free(mk_plan *plan);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char *mk_last_error(void);
+
+/* Hash of the sources the library was built from (16 hex digits), so a
+ * caller can refuse a library built from other sources. */
+const char *mk_build_id(void);
 
 /* ---- introspection (host only; no GPU needed) ----------------------------
  * mk_inspect_plan runs the planner for `cfg` with opts->n_cus CUs and

@@ -93,6 +93,11 @@ extern "C" {
 
 const char *mk_last_error(void) { return g_err.c_str(); }
 
+#ifndef MK_SOURCE_HASH
+#define MK_SOURCE_HASH "unknown"
+#endif
+const char *mk_build_id(void) { return MK_SOURCE_HASH; }
+
 void mk_plan_options_default(mk_plan_options *o) {
   if (!o) return;
   std::memset(o, 0, sizeof(*o));
@@ -473,6 +478,9 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
     d.spin_budget = o.spin_budget > 0 ? o.spin_budget : 100000000LL;  // 1 s at 100 MHz
     d.trace = trace;
     d.trace_mode = o.debug_trace;
+    if (o.debug_withhold < 0 || o.debug_withhold > T)
+      return fail(MK_ERR_INVALID_ARG, "debug_withhold names no task of the plan");
+    d.withhold = o.debug_withhold - 1;
     resolve_tasks(hp, tab, *w, d);
     {
       // device table in worker-major order, plus list index -> position
@@ -608,8 +616,18 @@ int mk_plan_status(mk_plan *plan, void *stream) {
              w[CTRL_ERR_TASK], (int)w[CTRL_ERR_EV], (int)w[CTRL_ERR_SEEN], w[CTRL_ERR_WANT]);
     code = MK_ERR_INVALID_ARG;
   }
-  HIP_TRY(hipMemset(plan->ctrl, 0, (size_t)plan->n_ctrl_words * 4), "reset counters");
+  // Reset the error and the counters, keeping the data tag of graph-replayed
+  // steps: the failed step's partial outputs carry that tag, so the next
+  // step must count on from it, not restart where stale values would pass.
+  HIP_TRY(hipMemset(plan->ctrl, 0, (size_t)CTRL_TAG * 4), "reset control words");
+  HIP_TRY(hipMemset(plan->ctrl + CTRL_WORDS, 0, (size_t)(plan->n_ctrl_words - CTRL_WORDS) * 4),
+          "reset counters");
   plan->epoch = 0;
+  if (plan->d.withhold >= 0) {  // the test hook applies until its error is reported
+    plan->d.withhold = -1;
+    HIP_TRY(hipMemcpy(plan->d_dev, &plan->d, sizeof plan->d, hipMemcpyHostToDevice),
+            "upload plan");
+  }
   return fail(code, buf);
 }
 

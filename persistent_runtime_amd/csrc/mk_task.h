@@ -156,6 +156,8 @@ struct DevPlan {
   int64_t spin_budget;     // in s_memrealtime ticks (100 MHz)
   uint32_t *trace;         // 6 u32 per task, or null
   int32_t trace_mode;      // 1: dependency tickets + times, 2: times only
+  int32_t withhold;        // test hook: list index of a task whose counter
+                           // signals are withheld, or -1
 };
 
 // Per-step arguments, passed by value next to a device copy of DevPlan.

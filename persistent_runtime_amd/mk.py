@@ -33,7 +33,8 @@ OP_ID = {v: k for k, v in OPS.items()}
 # every function include/mk.h declares
 EXPORTS = ["mk_plan_options_default", "mk_build_plan", "mk_decode_step",
            "mk_prefill", "mk_plan_status", "mk_free", "mk_last_error",
-           "mk_inspect_plan", "mk_read_trace", "mk_plan_info", "mk_read_routing"]
+           "mk_build_id", "mk_inspect_plan", "mk_read_trace", "mk_plan_info",
+           "mk_read_routing"]
 
 
 class mk_config(C.Structure):
@@ -71,7 +72,7 @@ class mk_plan_options(C.Structure):
                 ("spin_budget", C.c_int64), ("n_cus", C.c_int32),
                 ("graph_replay", C.c_int32), ("batched_mfma", C.c_int32),
                 ("attn_pool", C.c_int32), ("weight_lds", C.c_int32),
-                ("reserved", C.c_int32 * 3)]
+                ("debug_withhold", C.c_int32), ("reserved", C.c_int32 * 2)]
 
 
 class mk_task_info(C.Structure):
@@ -90,6 +91,13 @@ def _load():
             f"libmk.so not found at {LIB_PATH}; build it with "
             "`python -m persistent_runtime_amd.build` (there is no fallback)")
     lib = C.CDLL(LIB_PATH)
+    lib.mk_build_id.restype = C.c_char_p
+    from .build import source_hash
+    built, want = lib.mk_build_id().decode(), source_hash()
+    if built != want and not os.environ.get("MK_LIB"):
+        raise ImportError(
+            f"{LIB_PATH} was built from other sources (build id {built}, sources {want}); "
+            "rebuild it with `python -m persistent_runtime_amd.build`")
     vp, i32, pi32 = C.c_void_p, C.c_int32, C.POINTER(C.c_int32)
     lib.mk_plan_options_default.argtypes = [C.POINTER(mk_plan_options)]
     lib.mk_plan_options_default.restype = None

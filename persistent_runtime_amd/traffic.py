@@ -26,7 +26,7 @@ COPY = "copyBuffer"
 def kernel_source_hash() -> str:
     """Hash of the sources that decide the kernel's memory traffic."""
     h = hashlib.sha256()
-    for f in ("kernels.hip", "mk_task.h", "planner.cpp"):
+    for f in ("kernels.h", "kernels_m1.hip", "mk_task.h", "planner.cpp"):
         with open(os.path.join(HERE, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -1,6 +1,8 @@
-"""Continuous batching on the Llama-3-8B shape at full size: 16 slots with
-seeded synthetic cached contexts uniform in [128, 16384] over shuffled
-16-token pages, in the launch configuration the ragged benchmark times.
+"""Continuous batching on the Llama-3-8B shape at full size: 4, 16 and 64
+slots (the vector multi-slot tiles, and the matrix-core tiles with split-K
+at 16 and 64) with seeded synthetic cached contexts uniform in [128, 16384]
+over shuffled 16-token pages, in the launch configuration the ragged
+benchmark times.
 
 Three decode steps.  Before the second, one sequence retires and a new one
 (fresh context and KV) joins its slot; during the third, one slot is empty
@@ -26,7 +28,11 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-B = 16
+
+@pytest.fixture(scope="module")
+def llama8b():
+    Wd = synth.make_weights(LLAMA8B, device="cuda")
+    return Wd, oracle_weights(Wd, LLAMA8B)
 
 
 def _host_kv(cfg, ctx, sid):
@@ -36,16 +42,17 @@ def _host_kv(cfg, ctx, sid):
 
 
 @pytest.mark.timeout(1200)
-def test_llama8b_ragged_batch_join_retire():
+@pytest.mark.parametrize("B", [4, 16, 64])
+def test_llama8b_ragged_batch_join_retire(llama8b, B):
     cfg = LLAMA8B
+    Wd, Wt = llama8b
     sched = synth.ragged_schedule(B, 3)
     ctx = list(sched["ctx0"])
     sid = list(sched["sid0"])
-    join_slot, empty_slot = 5, 9
+    join_slot, empty_slot = (1, 2) if B < 8 else (5, 9)
     join_ctx, join_sid = 3001, 10_000
     sample = sorted({join_slot, int(np.argmax(ctx)), int(np.argmin(ctx)), 0} - {empty_slot})
-    print(f"ragged: contexts {ctx}; oracle sample {sample}", flush=True)
-    Wd = synth.make_weights(cfg, device="cuda")
+    print(f"ragged B={B}: contexts {ctx}; oracle sample {sample}", flush=True)
     maxp = (16384 + 8 + 15) // 16
     n_pages = sum((c + 8 + 15) // 16 for c in ctx) + (join_ctx + 8 + 15) // 16
     kv = PagedKV(cfg, max_batch=B, max_pages_per_seq=maxp, n_pages=n_pages, device="cuda")
@@ -58,7 +65,6 @@ def test_llama8b_ragged_batch_join_retire():
         del K, V
     plan = mk.Plan(cfg, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=B,
                    opts=mk.default_options(planned_ctx=16384))
-    Wt = oracle_weights(Wd, cfg)
     tok_d = torch.zeros(B, dtype=torch.int32, device="cuda")
     pos_d = torch.zeros(B, dtype=torch.int32, device="cuda")
     nxt_d = torch.zeros(B, dtype=torch.int32, device="cuda")
@@ -97,7 +103,7 @@ def test_llama8b_ragged_batch_join_retire():
             d = float(np.max(np.abs(g_lg[b] - ref)))
             worst = max(worst, d)
             m = O.top2_margin(ref)
-            print(f"ragged: step {step} slot {b} ctx {pos[b]} max|dlogit| {d:.3e} margin {m:.3f}",
+            print(f"ragged B={B}: step {step} slot {b} ctx {pos[b]} max|dlogit| {d:.3e} margin {m:.3f}",
                   flush=True)
             if m > MARGIN:
                 assert int(g_ids[b]) == O.greedy_argmax(ref), (step, b)
@@ -109,3 +115,5 @@ def test_llama8b_ragged_batch_join_retire():
                 ctx[b] += 1
     assert worst <= LOGIT_TOL, worst
     plan.free()
+    del kv, caches
+    torch.cuda.empty_cache()

@@ -155,19 +155,129 @@ def test_trace_dependencies_and_run_once(tiny, pool):
     r.plan.free()
 
 
+def _lm_head_withhold(r):
+    """The plan's argmax task, the LM-head event it waits on, and one LM-head
+    task that reports completions to that event."""
+    tasks, _ = mk.inspect_plan(r.plan.cfg, mk.default_options(n_cus=r.plan.info()["n_cus"]))
+    arg = next(i for i, t in enumerate(tasks) if t.op == mk.OP_ID["ARGMAX"])
+    ev = tasks[arg].wait_ev[0]
+    lm = next(i for i, t in enumerate(tasks)
+              if t.op == mk.OP_ID["LMHEAD"] and t.sig_count > 0 and ev in list(t.sig_ev)[:t.n_sig])
+    return arg, ev, lm
+
+
 def test_timeout_is_reported_not_hung(tiny):
-    """A one-tick dependency-wait budget makes waits fail; the kernel drains
-    and mk_plan_status reports MK_ERR_TIMEOUT."""
+    """One LM-head task's completion signal is withheld (a test hook of the
+    plan), so the argmax task's wait can never be met: the wait gives up
+    after its 20 ms budget, every workgroup exits, and mk_plan_status
+    reports MK_ERR_TIMEOUT naming the argmax task and the LM-head event.
+    The hook ends with that report; the next step runs normally and gives
+    the same logits as a plan without the hook."""
     Wd, _ = tiny
-    r = Runner(TINY, Wd, B=1, maxp=8, spin_budget=1)
+    probe = Runner(TINY, Wd, B=1, maxp=8)
+    arg, ev, lm = _lm_head_withhold(probe)
+    probe.step([3], [0])
+    ref = probe.logits.cpu().numpy().copy()
+    probe.plan.free()
+    r = Runner(TINY, Wd, B=1, maxp=8, spin_budget=2_000_000, debug_withhold=lm + 1)
     r.tok.fill_(3)
     r.pos.fill_(0)
-    for _ in range(3):
-        r.plan.decode_step(r.tok, r.pos, r.nxt, r.logits)
+    r.plan.decode_step(r.tok, r.pos, r.nxt, r.logits)
     rc = r.plan.status()
-    # a step can also finish without ever waiting; both outcomes are legal
-    assert rc in (mk.MK_OK, mk.MK_ERR_TIMEOUT), rc
+    assert rc == mk.MK_ERR_TIMEOUT, rc
+    msg = mk.last_error()
+    assert f"task {arg} waited on event {ev}" in msg, msg
+    ids, lg = r.step([3], [0])  # raises on an error
+    assert np.array_equal(lg, ref)
     r.plan.free()
+
+
+def test_nonfinite_values_in_unwritten_pool_slots(tiny):
+    """Pools filled with NaN / infinity bit patterns before use: positions a
+    step has not written yet (after the current one on its page, the split
+    edges, pages of other sequences) must not reach the outputs, although
+    the matrix-core value products load whole pages.  Split counts 1 and 3
+    and a two-slot batch."""
+    Wd, Wt = tiny
+    for splits, B in ((1, 1), (3, 1), (2, 2)):
+        print(f"nonfinite pools: splits={splits} B={B}", flush=True)
+        r = Runner(TINY, Wd, B=B, maxp=8, attn_splits=splits)
+        r.kv.k_pool.view(torch.int16).fill_(0x7FC0)   # quiet NaN
+        r.kv.v_pool.view(torch.int16).fill_(0x7F80)   # +infinity
+        r.kv.v_pool.view(torch.int16)[..., ::3].fill_(0x7FC0)
+        worst, ids, cache = teacher_forced_run(r, Wt, _prompt(23), 5)
+        assert np.isfinite(worst) and worst <= LOGIT_TOL, worst
+        assert_ids(ids)
+        r.plan.free()
+
+
+def test_graph_replay_recovers_after_error(tiny):
+    """A replayable plan whose first step fails (a bad token) leaves outputs
+    tagged with that step's data tag; after mk_plan_status reports the error,
+    the next step must not accept them as its own.  Its logits equal those of
+    a fresh plan."""
+    Wd, _ = tiny
+    ref_r = Runner(TINY, Wd, B=1, maxp=8, attn_splits=2)
+    ref_r.step([7], [0])
+    ref = ref_r.logits.cpu().numpy().copy()
+    ref_r.plan.free()
+    r = Runner(TINY, Wd, B=1, maxp=8, attn_splits=2, graph_replay=1)
+    r.tok.fill_(5000)  # vocab is 1024
+    r.pos.fill_(0)
+    r.plan.decode_step(r.tok, r.pos, r.nxt, r.logits)
+    assert r.plan.status() == mk.MK_ERR_INVALID_ARG
+    ids, lg = r.step([7], [0])
+    assert np.array_equal(lg, ref)
+    r.plan.free()
+
+
+def test_abi_page_layout_written_by_caller(tiny):
+    """The pools in the layout include/mk.h documents, written here directly
+    (not through the repository's KV helper): keys [L][page][kv][16][hd],
+    values [L][page][kv][hd][16], a shuffled page table.  A synthetic
+    37-token context is placed that way; one decode step at position 37 must
+    match the oracle decoding against the same keys and values, and the key
+    and value the step stored for position 37 must sit where the layout puts
+    them (layer 0 within one bf16 ulp of the oracle's)."""
+    Wd, Wt = tiny
+    cfg = TINY
+    L, nkv, hd, n = cfg["n_layers"], cfg["n_kv_heads"], cfg["head_dim"], 37
+    n_pages, maxp = 11, 4
+    K, V = synth.make_kv_values(cfg, n, stream_id=3)          # [L, n, nkv, hd] bf16
+    k_pool = torch.zeros((L, n_pages, nkv, 16, hd), dtype=torch.bfloat16)
+    v_pool = torch.zeros((L, n_pages, nkv, hd, 16), dtype=torch.bfloat16)
+    pages = [9, 2, 6]                                          # positions 0-15, 16-31, 32-47
+    for t in range(n):
+        pg, sl = pages[t // 16], t % 16
+        for l in range(L):
+            for g in range(nkv):
+                k_pool[l, pg, g, sl, :] = K[l, t, g, :]
+                v_pool[l, pg, g, :, sl] = V[l, t, g, :]
+    table = torch.full((1, maxp), -1, dtype=torch.int32)
+    table[0, :3] = torch.tensor(pages, dtype=torch.int32)
+    k_d, v_d, t_d = k_pool.to(DEV), v_pool.to(DEV), table.to(DEV)
+    plan = mk.Plan(cfg, Wd, k_d, v_d, t_d, max_batch=1)
+    tok = torch.tensor([11], dtype=torch.int32, device=DEV)
+    pos = torch.tensor([n], dtype=torch.int32, device=DEV)
+    nxt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    lg = torch.zeros(1, cfg["vocab"], dtype=torch.float32, device=DEV)
+    plan.decode_step(tok, pos, nxt, lg)
+    plan.check()
+    Kh = synth.bf16_to_f32_np(synth.to_numpy_bf16(K))
+    Vh = synth.bf16_to_f32_np(synth.to_numpy_bf16(V))
+    cache = O.KVCache(cfg, K=list(Kh), V=list(Vh))
+    ref = O.decode_step(Wt, cfg, cache, 11, n)
+    assert float(np.max(np.abs(lg[0].cpu().numpy() - ref))) <= LOGIT_TOL
+    pg, sl = pages[n // 16], n % 16
+    k_new = k_d[0, pg, :, sl, :].float().cpu().numpy()         # [nkv, hd]
+    v_new = v_d[0, pg, :, :, sl].float().cpu().numpy()
+    assert np.all(np.abs(k_new - cache.K[0][n]) <= bf16_ulp(cache.K[0][n]) + 1e-6)
+    assert np.all(np.abs(v_new - cache.V[0][n]) <= bf16_ulp(cache.V[0][n]) + 1e-6)
+    # nothing else of the pools changed
+    k_d[:, pg, :, sl, :] = 0
+    v_d[:, pg, :, :, sl] = 0
+    assert torch.equal(k_d.cpu(), k_pool) and torch.equal(v_d.cpu(), v_pool)
+    plan.free()
 
 
 def test_bad_inputs_are_errors(tiny):
