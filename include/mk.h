@@ -158,6 +158,21 @@ void mk_plan_options_default(mk_plan_options *opts);
 int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
                   const mk_plan_options *opts, mk_plan **out);
 
+/* For callers that cannot allocate device memory (steps under HIP graph
+ * capture, serving loops that forbid allocation): mk_build_plan without any
+ * device allocation.  The plan's device state (task table, counters,
+ * activation scratch, RoPE table) is placed in the library's static scratch
+ * array of 32 MiB, which every device the library runs on holds until the
+ * process ends; a plan that needs more is refused with MK_ERR_UNSUPPORTED.
+ * Calls no hipMalloc / hipFree (host-side planning uses the C++ heap) and
+ * synchronises the device first.  There is one such array per device, so
+ * building another plan this way replaces the state of the previous one on
+ * that device: steps of the older plan then fail with MK_ERR_INVALID_ARG, and
+ * steps of two such plans that overlap on one device would race.
+ * mk_free releases only the host side. */
+int mk_build_plan_noalloc(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
+                          const mk_plan_options *opts, mk_plan **out);
+
 /* One decode step for all max_batch slots.
  *  tokens_dev[b]     input token of slot b (int32, device)
  *  positions_dev[b]  0-based position of that token (= number of tokens

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <memory>
 #include <cstdio>
@@ -72,6 +73,11 @@ struct mk_plan {
                              // the split-attention and split-K arrival counters
   int n_att_cnt = 0;         // arrival counters (both kinds)
   int n_ctrl_words = 0;
+  // Plans built by mk_build_plan_noalloc carve their device state out of the
+  // device's static scratch array instead of allocating it.
+  char *arena = nullptr;
+  size_t arena_off = 0, arena_cap = 0;
+  uint32_t arena_gen = 0;    // which of the device's static plans this is
 
   ~mk_plan() {
     for (void *p : allocs) hipFree(p);
@@ -80,6 +86,18 @@ struct mk_plan {
   int alloc(T **p, size_t count, const char *what) {
     *p = nullptr;
     if (count == 0) return MK_OK;
+    if (arena) {
+      const size_t off = (arena_off + 255) & ~(size_t)255;
+      if (off + count * sizeof(T) > arena_cap)
+        return fail(MK_ERR_UNSUPPORTED,
+                    std::string("the plan's device state (") + what + " and what precedes it, " +
+                        std::to_string(off + count * sizeof(T)) +
+                        " bytes) exceeds the static scratch of " + std::to_string(arena_cap) +
+                        " bytes; use mk_build_plan");
+      *p = (T *)(arena + off);
+      arena_off = off + count * sizeof(T);
+      return MK_OK;
+    }
     void *v = nullptr;
     hipError_t e = hipMalloc(&v, count * sizeof(T));
     if (e != hipSuccess) return hip_fail(e, what);
@@ -88,6 +106,13 @@ struct mk_plan {
     return MK_OK;
   }
 };
+
+namespace {
+// Generation of the newest static plan per device: building one replaces the
+// device state of the one before, whose handle then refuses to run.
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t> g_static_gen[kMaxDevices];
+}  // namespace
 
 extern "C" {
 
@@ -319,8 +344,8 @@ static int check_weights(const mk_config &c, const mk_weights &w, std::vector<co
   return MK_OK;
 }
 
-int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
-                  const mk_plan_options *opts, mk_plan **out) {
+static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
+                      const mk_plan_options *opts, mk_plan **out, bool noalloc) {
   try {
     if (!out) return fail(MK_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
@@ -350,6 +375,17 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
       return fail(MK_ERR_UNSUPPORTED, "device has less LDS per workgroup than the kernels need");
 
     std::unique_ptr<mk_plan> p(new mk_plan());
+    if (noalloc) {
+      if (dev >= kMaxDevices) return fail(MK_ERR_UNSUPPORTED, "device ordinal too large");
+      // every earlier static plan's work has finished before its state is
+      // overwritten
+      HIP_TRY(hipDeviceSynchronize(), "hipDeviceSynchronize");
+      void *base = nullptr;
+      HIP_TRY(static_scratch(dev, &base), "static scratch address");
+      p->arena = (char *)base;
+      p->arena_cap = kStaticScratchBytes;
+      p->arena_gen = ++g_static_gen[dev];
+    }
     p->device = dev;
     p->executor = o.executor;
     p->graph_replay = o.graph_replay != 0;
@@ -507,6 +543,21 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
   }
 }
 
+int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
+                  const mk_plan_options *opts, mk_plan **out) {
+  return build_plan(cfg, w, kv, opts, out, false);
+}
+
+int mk_build_plan_noalloc(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
+                          const mk_plan_options *opts, mk_plan **out) {
+  return build_plan(cfg, w, kv, opts, out, true);
+}
+
+// A static plan whose device state a newer static plan has replaced.
+static bool stale_static(const mk_plan *plan) {
+  return plan->arena && plan->arena_gen != g_static_gen[plan->device].load();
+}
+
 static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positions,
                      hipStream_t s, int32_t *next, float *logits) {
   const DevPlan &d = plan->d;
@@ -556,6 +607,8 @@ int mk_decode_step(mk_plan *plan, const int32_t *tokens_dev, const int32_t *posi
     if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
     if (!tokens_dev || !positions_dev || !next_tokens_dev)
       return fail(MK_ERR_INVALID_ARG, "tokens, positions and next_tokens are required");
+    if (stale_static(plan))
+      return fail(MK_ERR_INVALID_ARG, "a newer mk_build_plan_noalloc plan replaced this plan's state");
     DeviceGuard guard(plan->device);
     return step_impl(plan, tokens_dev, positions_dev, (hipStream_t)stream, next_tokens_dev,
                      logits_dev);
@@ -573,6 +626,8 @@ int mk_prefill(mk_plan *plan, int32_t slot, const int32_t *tokens_dev, int32_t n
     if (!tokens_dev || n < 1) return fail(MK_ERR_INVALID_ARG, "need n >= 1 prompt tokens");
     if (start_pos < 0 || (int64_t)start_pos + n > plan->hp.max_pos)
       return fail(MK_ERR_INVALID_ARG, "prompt positions exceed the page-table capacity");
+    if (stale_static(plan))
+      return fail(MK_ERR_INVALID_ARG, "a newer mk_build_plan_noalloc plan replaced this plan's state");
     DeviceGuard guard(plan->device);
     hipStream_t s = (hipStream_t)stream;
     for (int i = 0; i < n; ++i) {
@@ -598,6 +653,8 @@ int mk_prefill(mk_plan *plan, int32_t slot, const int32_t *tokens_dev, int32_t n
 
 int mk_plan_status(mk_plan *plan, void *stream) {
   if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
+  if (stale_static(plan))
+    return fail(MK_ERR_INVALID_ARG, "a newer mk_build_plan_noalloc plan replaced this plan's state");
   DeviceGuard guard(plan->device);
   HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
   uint32_t w[CTRL_WORDS];

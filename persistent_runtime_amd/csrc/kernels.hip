@@ -1,6 +1,8 @@
 // kernels.hip -- the kernel-per-op executor, the small helper kernels and the
 // launch functions; the persistent kernel's variants are in kernels_m*.hip,
 // the device code they share in kernels.h.
+#include <mutex>
+
 #include "kernels.h"
 
 namespace mk {
@@ -77,6 +79,31 @@ hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t s) {
 }
 
 int persistent_lds_bytes() { return (int)sizeof(Smem); }
+
+// Device state of plans built without allocating (mk_build_plan_noalloc).
+// Each device holds its own copy from module load until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: host
+// code uses only the address hipGetSymbolAddress reports for the device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];
+}  // namespace
+
+hipError_t static_scratch(int device, void **ptr) {
+  *ptr = nullptr;
+  if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 }  // namespace mk
 

@@ -32,4 +32,10 @@ hipError_t launch_zero_u32(uint32_t *p, int n, hipStream_t s);
 // Resource use of the persistent kernel (for reports).
 int persistent_lds_bytes();
 
+// The device's copy of the library's static scratch array (kStaticScratchBytes,
+// 256-byte aligned), for plans that allocate no device memory.  `device` must
+// be the current device; its address is looked up once per device.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(int device, void **ptr);
+
 }  // namespace mk

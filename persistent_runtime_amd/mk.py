@@ -34,7 +34,7 @@ OP_ID = {v: k for k, v in OPS.items()}
 EXPORTS = ["mk_plan_options_default", "mk_build_plan", "mk_decode_step",
            "mk_prefill", "mk_plan_status", "mk_free", "mk_last_error",
            "mk_build_id", "mk_inspect_plan", "mk_read_trace", "mk_plan_info",
-           "mk_read_routing"]
+           "mk_read_routing", "mk_build_plan_noalloc"]
 
 
 class mk_config(C.Structure):
@@ -104,6 +104,7 @@ def _load():
     lib.mk_build_plan.argtypes = [C.POINTER(mk_config), C.POINTER(mk_weights),
                                   C.POINTER(mk_kv), C.POINTER(mk_plan_options),
                                   C.POINTER(vp)]
+    lib.mk_build_plan_noalloc.argtypes = lib.mk_build_plan.argtypes
     lib.mk_decode_step.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.mk_prefill.argtypes = [vp, i32, vp, i32, i32, vp, vp, vp]
     lib.mk_plan_status.argtypes = [vp, vp]
@@ -115,7 +116,8 @@ def _load():
     lib.mk_read_trace.argtypes = [vp, vp, C.POINTER(C.c_uint32), i32]
     lib.mk_plan_info.argtypes = [vp, pi32, pi32, pi32, pi32]
     lib.mk_read_routing.argtypes = [vp, vp, pi32, C.POINTER(C.c_float), i32]
-    for f in ("mk_build_plan", "mk_decode_step", "mk_prefill", "mk_plan_status",
+    for f in ("mk_build_plan", "mk_build_plan_noalloc", "mk_decode_step", "mk_prefill",
+              "mk_plan_status",
               "mk_inspect_plan", "mk_read_trace", "mk_plan_info", "mk_read_routing"):
         getattr(lib, f).restype = C.c_int
     return lib
@@ -193,7 +195,7 @@ class Plan:
     """
 
     def __init__(self, model: dict, W: dict, k_pool, v_pool, page_table,
-                 max_batch=1, opts: mk_plan_options | None = None):
+                 max_batch=1, opts: mk_plan_options | None = None, noalloc=False):
         L = model["n_layers"]
         self.model, self.W = model, W
         self.k_pool, self.v_pool, self.page_table = k_pool, v_pool, page_table
@@ -227,8 +229,9 @@ class Plan:
         kv = mk_kv(k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr())
         self.opts = opts if opts is not None else default_options()
         h = C.c_void_p()
-        _check(lib.mk_build_plan(C.byref(self.cfg), C.byref(w), C.byref(kv),
-                                 C.byref(self.opts), C.byref(h)))
+        build = lib.mk_build_plan_noalloc if noalloc else lib.mk_build_plan
+        _check(build(C.byref(self.cfg), C.byref(w), C.byref(kv), C.byref(self.opts),
+                     C.byref(h)))
         self.handle = h
 
     @staticmethod
