@@ -24,10 +24,10 @@ Parity pins: every function here is pinned by tests/test_oracle_pins.py
 the pages and are pinned only through those invariants, chiefly "incremental
 decode with a KV cache equals full causal recompute".
 """
-from .model import (rmsnorm, rope_cos_sin, rope, softmax, attention, silu,
+from .model import (rmsnorm, rope_cos_sin, rope, softmax, attention, causal_attention, silu,
                     swiglu, route_topk, KVCache, OracleWeights, decode_step,
                     forward_full, greedy_argmax, top2_margin, round_bf16)
 
-__all__ = ["rmsnorm", "rope_cos_sin", "rope", "softmax", "attention", "silu",
+__all__ = ["rmsnorm", "rope_cos_sin", "rope", "softmax", "attention", "causal_attention", "silu",
            "swiglu", "route_topk", "KVCache", "OracleWeights", "decode_step",
            "forward_full", "greedy_argmax", "top2_margin", "round_bf16"]

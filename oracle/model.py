@@ -271,15 +271,71 @@ def decode_step(Wt: OracleWeights, cfg: dict, cache: KVCache, token: int,
     return (logits, x) if return_hidden else logits
 
 
-def forward_full(Wt: OracleWeights, cfg: dict, tokens, return_cache=False, kv_bf16=True):
+def causal_attention(Q, K, V, n_kv_heads):
+    """Causal attention of T query positions over the same T positions (GQA).
+
+    Q: [T, nq, hd] (rotated); K, V: [T, nkv, hd].  For every head the T x T
+    score matrix (Q_h K_g^T) / sqrt(hd) is masked above the diagonal (position
+    t sees keys 0..t), softmax is taken along each row and the rows weight V_g:
+    the textbook masked-attention definition, in matrix form.  Returns
+    [T, nq, hd].
+    """
+    T, nq, hd = Q.shape
+    group = nq // n_kv_heads
+    out = np.empty_like(Q)
+    scale = Q.dtype.type(1.0 / np.sqrt(hd))
+    future = np.triu(np.ones((T, T), dtype=bool), k=1)
+    for h in range(nq):
+        g = h // group
+        s = (Q[:, h, :] @ K[:, g, :].T) * scale       # [T, T]
+        s[future] = -np.inf
+        out[:, h, :] = softmax(s, axis=-1) @ V[:, g, :]
+    return out
+
+
+def _ffn_tokens(Wt, cfg, layer, B, dtype):
+    """The feed-forward block for every row of B [T, H] at once.
+
+    Dense: the SwiGLU MLP as matrix products.  MoE: each token is routed by
+    route_topk exactly as in the single-token block; then, expert by expert
+    in ascending id, the tokens routed to that expert pass through its MLP
+    together and their weighted outputs are added to their rows (so every
+    row still sums its experts in ascending id)."""
+    if cfg["n_experts"] == 0:
+        G = B @ Wt.get("w_gate", layer).T
+        U = B @ Wt.get("w_up", layer).T
+        return swiglu(G, U) @ Wt.get("w_down", layer).T
+    R = B @ Wt.get("router", layer).T                  # [T, E]
+    T, E = R.shape
+    W = np.zeros((T, E), dtype=dtype)
+    chosen = np.zeros((T, E), dtype=bool)
+    for t in range(T):
+        ids, w, _ = route_topk(R[t], cfg["top_k"])
+        W[t, ids] = w
+        chosen[t, ids] = True
+    Y = np.zeros_like(B)
+    for e in range(E):
+        rows = np.nonzero(chosen[:, e])[0]
+        if rows.size == 0:
+            continue
+        Wg = _up(Wt.W["e_gate"][layer][e], dtype)
+        Wu = _up(Wt.W["e_up"][layer][e], dtype)
+        Wd = _up(Wt.W["e_down"][layer][e], dtype)
+        Be = B[rows]
+        Y[rows] += W[rows, e][:, None] * (swiglu(Be @ Wg.T, Be @ Wu.T) @ Wd.T)
+    return Y
+
+
+def forward_full(Wt: OracleWeights, cfg: dict, tokens, return_cache=False, kv_bf16=True,
+                 last_only=False):
     """Full causal forward over a whole token sequence (no cache reuse).
 
     Position t attends to positions 0..t, reading keys and values in the
     cache's storage format (kv_bf16 as in KVCache).  Returns logits
-    [T, vocab].  This is the recompute that incremental decoding must
-    reproduce.  With return_cache=True it also returns the rotated keys and
-    values it computed, as a KVCache ready for incremental decoding from
-    position T.
+    [T, vocab] ([1, vocab] of the last position with last_only).  This is
+    the recompute that incremental decoding must reproduce.  With
+    return_cache=True it also returns the rotated keys and values it
+    computed, as a KVCache ready for incremental decoding from position T.
     """
     cache = KVCache(cfg, Wt.dtype, kv_bf16=kv_bf16) if return_cache else None
     dtype = Wt.dtype
@@ -300,17 +356,10 @@ def forward_full(Wt: OracleWeights, cfg: dict, tokens, return_cache=False, kv_bf
             Kx, Vx = round_bf16(Kx), round_bf16(Vx)
         if cache is not None:
             cache.K[l], cache.V[l] = Kx.copy(), Vx.copy()
-        O = np.empty_like(Q)
-        for t in range(T):
-            O[t] = attention(Q[t], Kx[: t + 1], Vx[: t + 1], nkv)
+        O = causal_attention(Q, Kx, Vx, nkv)
         X = X + O.reshape(T, nq * hd) @ Wt.get("wo", l).T
         B = rmsnorm(X, Wt.get("ffn_norm", l), eps, dtype)
-        if cfg["n_experts"] == 0:
-            G = B @ Wt.get("w_gate", l).T
-            U = B @ Wt.get("w_up", l).T
-            X = X + swiglu(G, U) @ Wt.get("w_down", l).T
-        else:
-            X = X + np.stack([_ffn(Wt, cfg, l, B[t], dtype) for t in range(T)])
-    Hn = rmsnorm(X, Wt.get("final_norm"), eps, dtype)
+        X = X + _ffn_tokens(Wt, cfg, l, B, dtype)
+    Hn = rmsnorm(X[-1:] if last_only else X, Wt.get("final_norm"), eps, dtype)
     logits = Hn @ Wt.get("lm_head").T
     return (logits, cache) if return_cache else logits
