@@ -61,7 +61,7 @@ enum {
   MK_OP_EMBED = 1, MK_OP_QKV = 2, MK_OP_ATTN = 3, MK_OP_MERGE = 4,
   MK_OP_OPROJ = 5, MK_OP_GATEUP = 6, MK_OP_DOWN = 7, MK_OP_ROUTER = 8,
   MK_OP_TOPK = 9, MK_OP_EGATEUP = 10, MK_OP_EDOWN = 11, MK_OP_COMBINE = 12,
-  MK_OP_LMHEAD = 13, MK_OP_ARGMAX = 14
+  MK_OP_LMHEAD = 13, MK_OP_ARGMAX = 14, MK_OP_KVAPP = 15
 };
 
 /* Model shape and capacity.  n_experts == 0 selects the dense SwiGLU MLP
@@ -143,7 +143,18 @@ typedef struct {
                             spin_budget (every workgroup still exits); cleared
                             by the mk_plan_status call that reports the error.
                             0 = none                                         */
-  int32_t reserved[2];
+  int32_t shared_seqs;   /* 1: several slots of one step may hold one sequence
+                            (a prompt chunk at consecutive positions, mixed
+                            with other sequences' decode tokens: see
+                            mk_batch_step); every slot's key and value are
+                            stored before the layer's attention reads the
+                            cache.  0: each slot holds its own sequence      */
+  int32_t prefill_chunk; /* mk_prefill: prompt tokens per launch, run as the
+                            slots of an internal shared-sequence plan of that
+                            many slots (matrix-core tiles at 16..64): 0 = auto
+                            (64 when the model's row counts allow matrix-core
+                            tiles, else token by token), -1 = one token per
+                            decode step, 16..64 = that many                  */
 } mk_plan_options;
 
 typedef struct mk_plan mk_plan;
@@ -185,10 +196,29 @@ int mk_decode_step(mk_plan *plan, const int32_t *tokens_dev,
                    const int32_t *positions_dev, void *stream,
                    int32_t *next_tokens_dev, float *logits_dev);
 
+/* One step of a mixed batch (MPK summary, "भविष्य की दिशा", and Cohere,
+ * "Folyamatos batchkezelés": chunked prefill beside decode in one launch):
+ * slot b feeds tokens_dev[b] at position positions_dev[b] (< 0: empty) of the
+ * sequence whose pages are page_table row seq_rows_dev[b] (device int32
+ * [max_batch], each in [0, max_batch)).  Several slots may name one row --
+ * the consecutive positions of a prompt chunk of that sequence, each attending
+ * causally to everything before it including the chunk's earlier tokens --
+ * only in plans built with shared_seqs = 1; otherwise the rows must be
+ * distinct.  Outputs as mk_decode_step (per slot). */
+int mk_batch_step(mk_plan *plan, const int32_t *tokens_dev, const int32_t *positions_dev,
+                  const int32_t *seq_rows_dev, void *stream, int32_t *next_tokens_dev,
+                  float *logits_dev);
+
 /* Feed n prompt tokens tokens_dev[0..n) of one slot at positions
  * start_pos..start_pos+n-1, filling its KV pages (other slots are left
- * untouched).  next_token_dev (optional) receives the greedy token after the
- * last prompt token, logits_dev (optional) its fp32 logits [vocab]. */
+ * untouched): the full causal forward over the prompt (MPK summary, "MPK का
+ * मुख्य मूल्य": the prompt before greedy decoding).  With prefill_chunk
+ * enabled the prompt runs in chunks of up to that many tokens, each chunk one
+ * launch of an internal shared-sequence plan whose projections are
+ * matrix-core tiles with the chunk's tokens as the M dimension; otherwise one
+ * decode step per token.  next_token_dev (optional) receives the greedy token
+ * after the last prompt token, logits_dev (optional) its fp32 logits [vocab].
+ * Device-side errors of the chunks are reported by mk_plan_status. */
 int mk_prefill(mk_plan *plan, int32_t slot, const int32_t *tokens_dev,
                int32_t n, int32_t start_pos, void *stream,
                int32_t *next_token_dev, float *logits_dev);

@@ -68,6 +68,9 @@ struct mk_plan {
   uint32_t tag = 0;          // data tag of the last step (never 0 once used)
   bool graph_replay = false;
   int32_t *stage_tok = nullptr, *stage_pos = nullptr, *stage_next = nullptr;
+  int32_t *stage_rows = nullptr;
+  mk_plan *prefill = nullptr;  // internal shared-sequence plan that runs mk_prefill
+                               // in chunks, or null (token by token)
   float *stage_logits = nullptr;
   uint32_t *ctrl = nullptr;  // CTRL_WORDS control words, the event counters, then
                              // the split-attention and split-K arrival counters
@@ -80,6 +83,7 @@ struct mk_plan {
   uint32_t arena_gen = 0;    // which of the device's static plans this is
 
   ~mk_plan() {
+    delete prefill;
     for (void *p : allocs) hipFree(p);
   }
   template <class T>
@@ -345,7 +349,8 @@ static int check_weights(const mk_config &c, const mk_weights &w, std::vector<co
 }
 
 static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
-                      const mk_plan_options *opts, mk_plan **out, bool noalloc) {
+                      const mk_plan_options *opts, mk_plan **out, bool noalloc,
+                      int pt_rows = 0) {
   try {
     if (!out) return fail(MK_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
@@ -355,6 +360,8 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     if (opts) o = *opts;
     if (o.executor != MK_EXEC_PERSISTENT && o.executor != MK_EXEC_KERNEL_PER_OP)
       return fail(MK_ERR_INVALID_ARG, "unknown executor");
+    if (o.prefill_chunk > 0 && (o.prefill_chunk < 16 || o.prefill_chunk > kMfmaMaxBatch))
+      return fail(MK_ERR_INVALID_ARG, "prefill_chunk must be 0, -1 or 16..64");
     std::string err;
     int rc = check_config(*cfg, err);
     if (rc != MK_OK) return fail(rc, err);
@@ -426,7 +433,7 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     float *fs;
     if ((rc = p->alloc(&fs, (size_t)nf, "activation scratch"))) return rc;
     int32_t *is;
-    if ((rc = p->alloc(&is, (size_t)(hp.n_tk + hp.n_amax + 3 * B), "index scratch"))) return rc;
+    if ((rc = p->alloc(&is, (size_t)(hp.n_tk + hp.n_amax + 4 * B), "index scratch"))) return rc;
     const void **d_tab;
     if ((rc = p->alloc(&d_tab, tab.size(), "weight tables"))) return rc;
     const int half = c.head_dim / 2;
@@ -459,7 +466,7 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     }
     HIP_TRY(hipMemset(p->ctrl, 0, (size_t)p->n_ctrl_words * 4), "zero counters");
     HIP_TRY(hipMemset(fs, 0, (size_t)nf * 4), "zero scratch");
-    HIP_TRY(hipMemset(is, 0, (size_t)(hp.n_tk + hp.n_amax + 3 * B) * 4), "zero scratch");
+    HIP_TRY(hipMemset(is, 0, (size_t)(hp.n_tk + hp.n_amax + 4 * B) * 4), "zero scratch");
     if (trace) HIP_TRY(hipMemset(trace, 0, (size_t)T * 24), "zero trace");
 
     DevPlan &d = p->d;
@@ -468,6 +475,8 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     d.Fe = c.expert_ffn_dim; d.B = B; d.maxp = c.max_pages_per_seq; d.npages = c.n_pages;
     d.S = hp.S; d.G = hp.G; d.max_pos = hp.max_pos; d.n_lm_tiles = hp.n_lm_tiles;
     d.mfma = hp.mfma ? 1 : 0;
+    d.kv_first = hp.kv_first ? 1 : 0;
+    d.pt_rows = pt_rows > 0 ? pt_rows : B;
     d.lds_slots = hp.lds_slots;
     d.eps = c.rms_eps;
     d.embed = (const uint16_t *)w->embed;
@@ -498,6 +507,7 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     p->stage_tok = is + hp.n_tk + hp.n_amax;
     p->stage_pos = p->stage_tok + B;
     p->stage_next = p->stage_pos + B;
+    p->stage_rows = p->stage_next + B;
     d.rope_cos = rope;
     d.rope_sin = rope + (size_t)hp.max_pos * half;
     d.ctrl = p->ctrl;
@@ -536,6 +546,31 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     }
     if ((rc = p->alloc(&p->d_dev, 1, "plan copy"))) return rc;
     HIP_TRY(hipMemcpy(p->d_dev, &d, sizeof d, hipMemcpyHostToDevice), "upload plan");
+    // Chunked prefill: a second plan over the same weights, pools and page
+    // table whose slots are the tokens of one prompt chunk (one sequence at
+    // consecutive positions), run on matrix-core tiles where the row counts
+    // allow; token by token otherwise, and for plans that may not allocate.
+    if (!noalloc && pt_rows == 0 && o.prefill_chunk >= 0 && o.debug_trace == 0) {
+      const mk_config &cc = *cfg;
+      const bool rows16 = cc.hidden % 16 == 0 && (cc.n_q_heads * cc.head_dim) % 16 == 0 &&
+                          cc.vocab % 16 == 0 &&
+                          (cc.n_experts ? cc.n_experts % 16 == 0 : cc.ffn_dim % 16 == 0);
+      const int chunk = o.prefill_chunk > 0 ? o.prefill_chunk : (rows16 ? kMfmaMaxBatch : 0);
+      if (chunk > 0) {
+        mk_config pc = cc;
+        pc.max_batch = chunk;
+        mk_plan_options po = o;
+        po.shared_seqs = 1;
+        po.prefill_chunk = -1;
+        po.graph_replay = 0;
+        po.debug_withhold = 0;
+        po.attn_splits = 0;
+        po.attn_pool = 0;
+        po.device = dev;
+        rc = build_plan(&pc, w, kv, &po, &p->prefill, false, cc.max_batch);
+        if (rc != MK_OK) return rc;
+      }
+    }
     *out = p.release();
     return MK_OK;
   } catch (const std::exception &ex) {
@@ -559,11 +594,12 @@ static bool stale_static(const mk_plan *plan) {
 }
 
 static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positions,
-                     hipStream_t s, int32_t *next, float *logits) {
+                     const int32_t *rows, hipStream_t s, int32_t *next, float *logits) {
   const DevPlan &d = plan->d;
   CallArgs ca;
   ca.tokens = tokens;
   ca.positions = positions;
+  ca.rows = rows;
   ca.next_tokens = next;
   ca.logits = logits;
   if (plan->graph_replay) {
@@ -610,8 +646,25 @@ int mk_decode_step(mk_plan *plan, const int32_t *tokens_dev, const int32_t *posi
     if (stale_static(plan))
       return fail(MK_ERR_INVALID_ARG, "a newer mk_build_plan_noalloc plan replaced this plan's state");
     DeviceGuard guard(plan->device);
-    return step_impl(plan, tokens_dev, positions_dev, (hipStream_t)stream, next_tokens_dev,
-                     logits_dev);
+    return step_impl(plan, tokens_dev, positions_dev, nullptr, (hipStream_t)stream,
+                     next_tokens_dev, logits_dev);
+  } catch (const std::exception &ex) {
+    return fail(MK_ERR_PLAN, ex.what());
+  }
+}
+
+int mk_batch_step(mk_plan *plan, const int32_t *tokens_dev, const int32_t *positions_dev,
+                  const int32_t *seq_rows_dev, void *stream, int32_t *next_tokens_dev,
+                  float *logits_dev) {
+  try {
+    if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
+    if (!tokens_dev || !positions_dev || !seq_rows_dev || !next_tokens_dev)
+      return fail(MK_ERR_INVALID_ARG, "tokens, positions, seq_rows and next_tokens are required");
+    if (stale_static(plan))
+      return fail(MK_ERR_INVALID_ARG, "a newer mk_build_plan_noalloc plan replaced this plan's state");
+    DeviceGuard guard(plan->device);
+    return step_impl(plan, tokens_dev, positions_dev, seq_rows_dev, (hipStream_t)stream,
+                     next_tokens_dev, logits_dev);
   } catch (const std::exception &ex) {
     return fail(MK_ERR_PLAN, ex.what());
   }
@@ -630,11 +683,38 @@ int mk_prefill(mk_plan *plan, int32_t slot, const int32_t *tokens_dev, int32_t n
       return fail(MK_ERR_INVALID_ARG, "a newer mk_build_plan_noalloc plan replaced this plan's state");
     DeviceGuard guard(plan->device);
     hipStream_t s = (hipStream_t)stream;
+    if (mk_plan *q = plan->prefill) {
+      // chunks of up to C tokens, each one step of the prefill plan; the
+      // last token's slot gives the next token and the logits
+      const int C = q->hp.cfg.max_batch;
+      for (int i0 = 0; i0 < n; i0 += C) {
+        const int cnt = std::min(C, n - i0);
+        const bool last = i0 + cnt == n;
+        HIP_TRY(launch_stage_chunk(q->stage_tok, q->stage_pos, q->stage_rows, C, tokens_dev + i0,
+                                   cnt, start_pos + i0, slot, s),
+                "prefill staging");
+        int rc = step_impl(q, q->stage_tok, q->stage_pos, q->stage_rows, s, q->stage_next,
+                           (last && logits_dev) ? q->stage_logits : nullptr);
+        if (rc != MK_OK) return rc;
+        if (last) {
+          const int j = cnt - 1;
+          if (next_token_dev)
+            HIP_TRY(hipMemcpyAsync(next_token_dev, q->stage_next + j, 4, hipMemcpyDeviceToDevice,
+                                   s),
+                    "prefill token copy");
+          if (logits_dev)
+            HIP_TRY(hipMemcpyAsync(logits_dev, q->stage_logits + (size_t)j * c.vocab,
+                                   (size_t)c.vocab * 4, hipMemcpyDeviceToDevice, s),
+                    "prefill logits copy");
+        }
+      }
+      return MK_OK;
+    }
     for (int i = 0; i < n; ++i) {
       HIP_TRY(launch_stage(plan->stage_tok, plan->stage_pos, c.max_batch, slot, tokens_dev, i,
                            start_pos, s),
               "prefill staging");
-      int rc = step_impl(plan, plan->stage_tok, plan->stage_pos, s, plan->stage_next,
+      int rc = step_impl(plan, plan->stage_tok, plan->stage_pos, nullptr, s, plan->stage_next,
                          (i == n - 1 && logits_dev) ? plan->stage_logits : nullptr);
       if (rc != MK_OK) return rc;
     }
@@ -655,6 +735,13 @@ int mk_plan_status(mk_plan *plan, void *stream) {
   if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
   if (stale_static(plan))
     return fail(MK_ERR_INVALID_ARG, "a newer mk_build_plan_noalloc plan replaced this plan's state");
+  if (plan->prefill) {  // errors of the prompt chunks land in the prefill plan
+    const int rc = mk_plan_status(plan->prefill, stream);
+    if (rc != MK_OK) {
+      g_err = "prefill: " + g_err;
+      return rc;
+    }
+  }
   DeviceGuard guard(plan->device);
   HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
   uint32_t w[CTRL_WORDS];

@@ -143,6 +143,9 @@ DEV float lda(const float *p) {
 DEV void sta(float *p, float v) {
   __hip_atomic_store((AS1 float *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+DEV void sta16(uint16_t *p, uint16_t v) {
+  __hip_atomic_store((AS1 uint16_t *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 DEV int ldai(const int32_t *p) {
   return __hip_atomic_load((const AS1 int32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -266,6 +269,17 @@ DEV void init_ws(WState &ws) {
   ws.sat_ev[0] = ws.sat_ev[1] = -1;
   ws.sat_want[0] = ws.sat_want[1] = 0;
   ws.rt_layer = ws.rt_slot = -1;
+}
+
+DEV void set_error(CP &d, uint32_t code, int task, int ev, uint32_t seen, uint32_t want);
+
+// The page-table row of slot b's sequence (a prompt chunk's slots share one);
+// a row outside the table is reported (task tix) and row 0 read instead.
+DEV const int32_t *page_row(CP &d, const CallArgs &ca, int b, int tix) {
+  const int r = ca.rows ? uni(ldg(ca.rows + b)) : b;
+  const bool ok = r >= 0 && r < d.pt_rows;
+  if (!ok && tidx() == 0) set_error(d, DEVERR_BAD_INPUT, tix, -5, (uint32_t)r, (uint32_t)d.pt_rows);
+  return d.page_table + (size_t)(ok ? r : 0) * d.maxp;
 }
 
 DEV void set_error(CP &d, uint32_t code, int task, int ev, uint32_t seen, uint32_t want) {
@@ -1851,11 +1865,15 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   const int n = pos + 1;
   const int lo = pos_ok ? (int)((int64_t)sp * n / S) : 0;
   const int hi = pos_ok ? (int)((int64_t)(sp + 1) * n / S) : 0;
-  const int chi = hi < pos ? hi : pos;  // cached keys [lo, chi)
+  // cached keys [lo, chi); in shared-sequence plans the current one is
+  // cached too (stored by the layer's KVAPP tasks before this task runs)
+  const bool kvf = d.kv_first != 0;
+  const int chi = kvf || hi < pos ? hi : pos;
   const int blk0 = lo / kPageSize, blk1 = chi > lo ? (chi - 1) / kPageSize : -1;
   // this wave's pages: blk0 + wave + i * kWaves for i < npw
   const int npw = blk1 >= blk0 + wave ? (blk1 - blk0 - wave) / kWaves + 1 : 0;
-  const int32_t *ptab = d.page_table + (size_t)b * d.maxp + blk0 + wave;
+  const int32_t *prow = pos_ok ? page_row(d, ca, b, tix) : d.page_table;
+  const int32_t *ptab = prow + blk0 + wave;
   auto page_ids = [&](int c0) {  // lane i: the id of page c0 + i (or -1)
     const int i = c0 + lane;
     return i < npw ? ldg(ptab + (size_t)i * kWaves) : -1;
@@ -1889,13 +1907,19 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   // (Everything loaded here has arrived before the page loop: the task's
   // own input loads after the wait are waited for in order.)
   int pid = -1;
-  if (npw > 0) {
-    pid = page_ids(0);
-    load_keys(pid, 0, kq[0]);
-    load_keys(pid, min(1, npw - 1), kq[1]);
-    load_values(pid, 0, min(1, npw - 1));
-  }
+  auto first_pair = [&]() {
+    if (npw > 0) {
+      pid = page_ids(0);
+      load_keys(pid, 0, kq[0]);
+      load_keys(pid, min(1, npw - 1), kq[1]);
+      load_values(pid, 0, min(1, npw - 1));
+    }
+  };
+  // (shared-sequence plans: this step writes into the pages, so they are
+  // read only after the wait)
+  if (!kvf) first_pair();
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  if (kvf) first_pair();
   if (!pos_ok) {
     trace_start(d, t);
     if (pos >= d.max_pos && tid == 0)
@@ -1913,7 +1937,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     }
     return true;
   }
-  const bool has_cur = (hi == n);
+  const bool has_cur = !kvf && hi == n;
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
   const float *cs = d.rope_cos + (size_t)pos * (HD / 2);
   const float *sn = d.rope_sin + (size_t)pos * (HD / 2);
@@ -1929,7 +1953,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   }
   if (has_cur) {
     const size_t kvo = (((size_t)l * B + b) * nkv + g) * HD;
-    const int pg = uni(ldg(d.page_table + (size_t)b * d.maxp + pos / kPageSize));
+    const int pg = uni(ldg(prow + pos / kPageSize));
     const bool pg_ok = pg >= 0 && pg < d.npages;
     if (!pg_ok && tid == 0) set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pg, (uint32_t)d.npages);
     for (int i = tid; i < HD; i += kThreads) {
@@ -2150,6 +2174,42 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   return true;
 }
 
+// Shared-sequence plans: store slot b's rotated key and its value, every KV
+// head, into the page of its position (the same rotation and bf16 rounding
+// as the attention task's own store in the other plans).  The layer's
+// attention tasks wait for all of these, so each slot of a prompt chunk sees
+// the keys of the chunk's earlier positions.
+DEV void run_kvapp(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
+  const int l = t.layer, b = t.a0, HD = d.hd, half = HD / 2, nkv = d.nkv;
+  const int pos = uni(ldg(ca.positions + b));
+  if (pos < 0) return;
+  if (pos >= d.max_pos) {
+    if (tidx() == 0) set_error(d, DEVERR_BAD_INPUT, t.gidx, -1, (uint32_t)pos, (uint32_t)d.max_pos);
+    return;
+  }
+  const int pg = uni(ldg(page_row(d, ca, b, t.gidx) + pos / kPageSize));
+  if (pg < 0 || pg >= d.npages) {
+    if (tidx() == 0) set_error(d, DEVERR_BAD_INPUT, t.gidx, -2, (uint32_t)pg, (uint32_t)d.npages);
+    return;
+  }
+  const float *cs = d.rope_cos + (size_t)pos * half;
+  const float *sn = d.rope_sin + (size_t)pos * half;
+  const size_t kv0 = ((size_t)l * d.B + b) * nkv * HD;
+  const int ps = pos & (kPageSize - 1);
+  for (int idx = tidx(); idx < nkv * HD; idx += kThreads) {
+    const int g = idx / HD, i = idx - g * HD, i0 = i & (half - 1);
+    const float a = ldt_wait(sm, d, ca, t, d.k, kv0 + g * HD + i0);
+    const float c2 = ldt_wait(sm, d, ca, t, d.k, kv0 + g * HD + i0 + half);
+    const float cv = ldg(cs + i0), sv = ldg(sn + i0);
+    const float kr = (i < half) ? a * cv - c2 * sv : a * sv + c2 * cv;
+    const size_t page = ((size_t)l * d.npages + pg) * nkv + g;
+    // agent-coherent stores: other CUs read these pages later in this step
+    sta16(d.k_pool + (page * kPageSize + ps) * HD + i, f2bf(kr));
+    sta16(d.v_pool + (page * HD + i) * kPageSize + ps,
+          f2bf(ldt_wait(sm, d, ca, t, d.v, kv0 + g * HD + i)));
+  }
+}
+
 // Log-sum-exp merge of the S split partials (o[HD], m, l) of one (slot, KV
 // head): the group's G query heads.  Every thread takes one 16-byte output
 // vector and a subset of the splits (split sp goes to subset sp mod nsub);
@@ -2282,6 +2342,7 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
       run_embed(d, ca, t);
       break;
     case OP_ARGMAX: run_argmax(sm, d, ca, t); break;
+    case OP_KVAPP: run_kvapp(sm, d, ca, t); break;
     default: break;
   }
   ws.x_src = nullptr;  // LDS reused: the activation cache is gone

@@ -30,6 +30,15 @@ __global__ void mk_stage_kernel(int32_t *tok, int32_t *pos, int B, int slot,
   pos[b] = b == slot ? start + i : -1;
 }
 
+__global__ void mk_stage_chunk_kernel(int32_t *tok, int32_t *pos, int32_t *rows, int B,
+                                      const int32_t *tokens, int cnt, int start, int row) {
+  const int b = threadIdx.x + blockIdx.x * blockDim.x;
+  if (b >= B) return;
+  tok[b] = b < cnt ? tokens[b] : 0;
+  pos[b] = b < cnt ? start + b : -1;
+  rows[b] = row;
+}
+
 __global__ void mk_bump_kernel(uint32_t *p) {
   if (threadIdx.x == 0) {
     const uint32_t v = p[0] + 1u;
@@ -64,6 +73,13 @@ hipError_t launch_stage(int32_t *stage_tok, int32_t *stage_pos, int B, int slot,
                         const int32_t *tokens, int i, int start, hipStream_t s) {
   hipLaunchKernelGGL(mk_stage_kernel, dim3((B + 255) / 256), dim3(256), 0, s, stage_tok,
                      stage_pos, B, slot, tokens, i, start);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_chunk(int32_t *stage_tok, int32_t *stage_pos, int32_t *stage_rows, int B,
+                              const int32_t *tokens, int cnt, int start, int row, hipStream_t s) {
+  hipLaunchKernelGGL(mk_stage_chunk_kernel, dim3((B + 255) / 256), dim3(256), 0, s, stage_tok,
+                     stage_pos, stage_rows, B, tokens, cnt, start, row);
   return hipGetLastError();
 }
 

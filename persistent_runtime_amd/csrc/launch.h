@@ -23,6 +23,11 @@ hipError_t launch_phase(const DevPlan *d, const CallArgs &ca, int first, int cou
 hipError_t launch_stage(int32_t *stage_tok, int32_t *stage_pos, int B, int slot,
                         const int32_t *tokens, int i, int start, hipStream_t s);
 
+// Prompt-chunk staging: slot j < cnt gets tokens[j] at position start + j of
+// page-table row `row`; slots cnt..B-1 are empty.
+hipError_t launch_stage_chunk(int32_t *stage_tok, int32_t *stage_pos, int32_t *stage_rows, int B,
+                              const int32_t *tokens, int cnt, int start, int row, hipStream_t s);
+
 // Zero n words (counter reset between epochs).
 // p[0] += 1, skipping 0 (the data tag of graph-replayed steps)
 hipError_t launch_bump_tag(uint32_t *p, hipStream_t s);

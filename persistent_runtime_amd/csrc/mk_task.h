@@ -51,7 +51,7 @@ constexpr int kLdsWbufOff = kLdsXBytes - kCW * kLdsSlots * 1024;  // 72 KiB
 enum Op : int16_t {
   OP_EMBED = 1, OP_QKV = 2, OP_ATTN = 3, OP_MERGE = 4, OP_OPROJ = 5,
   OP_GATEUP = 6, OP_DOWN = 7, OP_ROUTER = 8, OP_TOPK = 9, OP_EGATEUP = 10,
-  OP_EDOWN = 11, OP_COMBINE = 12, OP_LMHEAD = 13, OP_ARGMAX = 14
+  OP_EDOWN = 11, OP_COMBINE = 12, OP_LMHEAD = 13, OP_ARGMAX = 14, OP_KVAPP = 15
 };
 
 // 64-byte task descriptor.  Field use per op:
@@ -73,6 +73,9 @@ enum Op : int16_t {
 //   combine inside EDOWN)
 //   LMHEAD  a1=row0 a2=rows a4=LM-head task index (argmax partial)
 //   ARGMAX  a0=slot
+//   KVAPP   a0=slot (shared-sequence plans: rotate the slot's new key, store
+//           key and value of every KV head into its page before any
+//           attention task of the layer runs)
 // a5 (every op): how many completions this task reports to its events.  A
 // worker that runs several consecutive tasks signalling the same events
 // reports them once, from the last task of the run (a5 = run length); the
@@ -158,11 +161,19 @@ struct DevPlan {
   int32_t trace_mode;      // 1: dependency tickets + times, 2: times only
   int32_t withhold;        // test hook: list index of a task whose counter
                            // signals are withheld, or -1
+  int32_t pt_rows;         // rows of the page table (the slots of the plan
+                           // that owns it; an internal prefill plan maps its
+                           // slots onto one of them)
+  int32_t kv_first;        // shared-sequence plan: KVAPP tasks store every
+                           // slot's key/value before the layer's attention,
+                           // which reads all positions (its own included)
+                           // from the cache
 };
 
 // Per-step arguments, passed by value next to a device copy of DevPlan.
 struct CallArgs {
   const int32_t *tokens, *positions;
+  const int32_t *rows;   // page-table row of each slot's sequence; null: row = slot
   int32_t *next_tokens;
   float *logits;
   uint32_t epoch;

@@ -346,6 +346,7 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
             hd = c.head_dim, B = c.max_batch;
   const bool moe = c.n_experts > 0;
   p.G = nq / nkv;
+  p.kv_first = o.shared_seqs > 0;
   p.max_pos = c.max_pages_per_seq * kPageSize;
 
   // attention splits: enough (slot, KV head, split) tasks to cover the CUs,
@@ -444,11 +445,13 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     for (int w = 0; w < n_workers - n_attn; ++w) oproj_w.push_back(w);
   }
   for (int l = 0; l < L; ++l) {
-    // QKV, group by group so a KV head's attention can start early
+    // QKV, group by group so a KV head's attention can start early (in
+    // shared-sequence plans one event for all groups: the key/value stores
+    // wait for every group)
     std::vector<int> grp(nkv);
     for (int g = 0; g < nkv; ++g) {
-      grp[g] = b.ev();
-      data_ev.push_back(grp[g]);  // q, k, v are tagged
+      grp[g] = (p.kv_first && g > 0) ? grp[0] : b.ev();
+      if (!p.kv_first || g == 0) data_ev.push_back(grp[g]);  // q, k, v are tagged
     }
     b.begin_phase();
     {
@@ -461,6 +464,16 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
       if (add_gemv(b, OP_QKV, l, segs, H, 1, n_workers, pmax_for(H), x_ev[l], 0, nullptr) < 0)
         ok = false;
     }
+    // Shared-sequence plans: every slot's key and value go into the cache
+    // before any attention task of the layer reads it (a prompt chunk's
+    // slots attend to each other's positions), a counter edge.
+    int app = -1;
+    if (p.kv_first) {
+      app = b.ev();
+      b.begin_phase();
+      for (int s = 0; s < B; ++s)
+        b.add(OP_KVAPP, l, s, 0, 0, 0, 0, {grp[0]}, {app}, 0);
+    }
     // attention splits; with several splits, the split that arrives last
     // for its (slot, KV head) merges them and reports the head group's one
     // completion (statically: the last split carries it)
@@ -468,9 +481,12 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
     b.begin_phase();
     for (int s = 0; s < B; ++s)
       for (int g = 0; g < nkv; ++g)
-        for (int sp = 0; sp < p.S; ++sp)
-          b.add(OP_ATTN, l, s, g, sp, 0, 0, {grp[g]}, {mrg}, 0,
+        for (int sp = 0; sp < p.S; ++sp) {
+          std::vector<int> waits{grp[g]};
+          if (app >= 0) waits.push_back(app);
+          b.add(OP_ATTN, l, s, g, sp, 0, 0, waits, {mrg}, 0,
                 attn_w.empty() ? -1 : attn_w[(s * nkv + g) * p.S + sp]);
+        }
     if (p.S > 1) p.ev_thr[mrg] = B * nkv;  // one merged group per (slot, KV head)
     // O projection + residual
     int xo = b.ev();

@@ -25,6 +25,8 @@ struct HostPlan {
   int max_pos = 0;
   bool mfma = false;                // static GEMVs as matrix-core tiles (16-row groups)
   bool attn_pool = false;           // attention tasks claimed at run time (persistent)
+  bool kv_first = false;            // several slots may hold one sequence: KVAPP
+                                    // tasks store keys/values before attention
   int lds_slots = 0;                // kLdsSlots when GEMV passes extend into LDS
   int tile_units = kMaxTileUnits16; // 1 KiB units per GEMV pass
   std::vector<Task> tasks;

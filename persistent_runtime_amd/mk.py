@@ -27,14 +27,14 @@ MK_EXEC_KERNEL_PER_OP = 1
 
 OPS = {1: "EMBED", 2: "QKV", 3: "ATTN", 4: "MERGE", 5: "OPROJ", 6: "GATEUP",
        7: "DOWN", 8: "ROUTER", 9: "TOPK", 10: "EGATEUP", 11: "EDOWN",
-       12: "COMBINE", 13: "LMHEAD", 14: "ARGMAX"}
+       12: "COMBINE", 13: "LMHEAD", 14: "ARGMAX", 15: "KVAPP"}
 OP_ID = {v: k for k, v in OPS.items()}
 
 # every function include/mk.h declares
 EXPORTS = ["mk_plan_options_default", "mk_build_plan", "mk_decode_step",
            "mk_prefill", "mk_plan_status", "mk_free", "mk_last_error",
            "mk_build_id", "mk_inspect_plan", "mk_read_trace", "mk_plan_info",
-           "mk_read_routing", "mk_build_plan_noalloc"]
+           "mk_read_routing", "mk_build_plan_noalloc", "mk_batch_step"]
 
 
 class mk_config(C.Structure):
@@ -72,7 +72,8 @@ class mk_plan_options(C.Structure):
                 ("spin_budget", C.c_int64), ("n_cus", C.c_int32),
                 ("graph_replay", C.c_int32), ("batched_mfma", C.c_int32),
                 ("attn_pool", C.c_int32), ("weight_lds", C.c_int32),
-                ("debug_withhold", C.c_int32), ("reserved", C.c_int32 * 2)]
+                ("debug_withhold", C.c_int32), ("shared_seqs", C.c_int32),
+                ("prefill_chunk", C.c_int32)]
 
 
 class mk_task_info(C.Structure):
@@ -107,6 +108,7 @@ def _load():
     lib.mk_build_plan_noalloc.argtypes = lib.mk_build_plan.argtypes
     lib.mk_decode_step.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.mk_prefill.argtypes = [vp, i32, vp, i32, i32, vp, vp, vp]
+    lib.mk_batch_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.mk_plan_status.argtypes = [vp, vp]
     lib.mk_free.argtypes = [vp]
     lib.mk_free.restype = None
@@ -117,7 +119,7 @@ def _load():
     lib.mk_plan_info.argtypes = [vp, pi32, pi32, pi32, pi32]
     lib.mk_read_routing.argtypes = [vp, vp, pi32, C.POINTER(C.c_float), i32]
     for f in ("mk_build_plan", "mk_build_plan_noalloc", "mk_decode_step", "mk_prefill",
-              "mk_plan_status",
+              "mk_plan_status", "mk_batch_step",
               "mk_inspect_plan", "mk_read_trace", "mk_plan_info", "mk_read_routing"):
         getattr(lib, f).restype = C.c_int
     return lib
@@ -244,6 +246,10 @@ class Plan:
     def decode_step(self, tokens, positions, next_tokens, logits=None, stream=None):
         _check(lib.mk_decode_step(self.handle, _ptr(tokens), _ptr(positions),
                                   self._stream(stream), _ptr(next_tokens), _ptr(logits)))
+
+    def batch_step(self, tokens, positions, seq_rows, next_tokens, logits=None, stream=None):
+        _check(lib.mk_batch_step(self.handle, _ptr(tokens), _ptr(positions), _ptr(seq_rows),
+                                 self._stream(stream), _ptr(next_tokens), _ptr(logits)))
 
     def prefill(self, slot, tokens, n, start_pos, next_token=None, logits=None, stream=None):
         _check(lib.mk_prefill(self.handle, slot, _ptr(tokens), n, start_pos,

@@ -113,9 +113,9 @@ def _check_graph(model, tasks, thr, B, mfma=False):
     return sig
 
 
-def _regions(model, t, B, S, mfma=False):
+def _regions(model, t, B, S, mfma=False, shared=False):
     """(reads, writes) of one task, as lists of (buffer, layer, slot, sub, lo, hi)."""
-    R, W = _regions_rows(model, t, B, S)
+    R, W = _regions_rows(model, t, B, S, shared)
     op = mk.OPS[t.op]
     if mfma and op in STATIC and op != "LMHEAD":
         # a split-K tile writes only its slice of the block's rows (summed
@@ -131,7 +131,7 @@ def _regions(model, t, B, S, mfma=False):
     return R, W
 
 
-def _regions_rows(model, t, B, S):
+def _regions_rows(model, t, B, S, shared=False):
     op = mk.OPS[t.op]
     l, H = t.layer, model["hidden"]
     nq, nkv, hd = model["n_q_heads"], model["n_kv_heads"], model["head_dim"]
@@ -149,10 +149,19 @@ def _regions_rows(model, t, B, S):
         for b in allb:
             R.append(("x", l, b, 0, 0, H))
             W.append((name, l, b, 0, t.a1, t.a1 + t.a2))
+    elif op == "KVAPP":
+        # shared-sequence plans, modelled as one prompt chunk: slot b holds
+        # the sequence's b-th new position and stores its key/value there
+        b = t.a0
+        R += [("k", l, b, 0, 0, nkv * hd), ("v", l, b, 0, 0, nkv * hd)]
+        W += [("cache", l, 0, g, b, b + 1) for g in range(nkv)]
     elif op == "ATTN":
         b, g, s = t.a0, t.a1, t.a2
-        R += [("q", l, b, 0, g * G * hd, (g + 1) * G * hd), ("k", l, b, 0, g * hd, (g + 1) * hd),
-              ("v", l, b, 0, g * hd, (g + 1) * hd)]
+        R.append(("q", l, b, 0, g * G * hd, (g + 1) * G * hd))
+        if shared:  # every chunk position up to its own, from the cache
+            R.append(("cache", l, 0, g, 0, b + 1))
+        else:
+            R += [("k", l, b, 0, g * hd, (g + 1) * hd), ("v", l, b, 0, g * hd, (g + 1) * hd)]
         if S > 1:
             # The split that arrives last merges the group's partials into
             # the attention output; an arrival counter, not an event, orders
@@ -212,6 +221,9 @@ def _bruteforce_deps(model, B, S=None, **optkw):
     opts = mk.default_options(n_cus=optkw.pop("n_cus", 8), **optkw)
     tasks, thr = mk.inspect_plan(_cfg(model, B=B, maxp=8), opts)
     mfma = B >= 16
+    shared = optkw.get("shared_seqs", 0) > 0
+    if shared:
+        assert sum(1 for t in tasks if mk.OPS[t.op] == "KVAPP") == B * model["n_layers"]
     sig = _check_graph(model, tasks, thr, B, mfma)
     # S actually used: count ATTN tasks per (layer 0, slot 0, head 0)
     S = sum(1 for t in tasks if mk.OPS[t.op] == "ATTN" and t.layer == 0 and t.a0 == 0 and t.a1 == 0)
@@ -223,7 +235,7 @@ def _bruteforce_deps(model, B, S=None, **optkw):
             for p in sig[t.wait_ev[k]]:
                 a |= anc[p] | (1 << p)
         anc[i] = a
-    regs = [_regions(model, t, B, S, mfma) for t in tasks]
+    regs = [_regions(model, t, B, S, mfma, shared) for t in tasks]
     written = []
     for i, (_, W) in enumerate(regs):
         for w in W:
@@ -261,6 +273,16 @@ def test_dependencies_match_region_overlap_batched_split_k():
     splits = [t for t in tasks if mk.OPS[t.op] == "DOWN" and _ksplit(TINY, t)[2] > 1]
     assert splits
     T, n = _bruteforce_deps(TINY, 16)
+    assert n > 0
+
+
+@pytest.mark.parametrize("B", [3, 16])
+def test_dependencies_match_region_overlap_shared_sequences(B):
+    """Shared-sequence plans (a prompt chunk's tokens in the slots): every
+    attention task depends on the key/value stores of its own and every
+    earlier position of the chunk (vector path at 3 slots, matrix cores with
+    split attention at 16)."""
+    T, n = _bruteforce_deps(TINY, B, shared_seqs=1, attn_splits=2)
     assert n > 0
 
 
