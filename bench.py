@@ -48,54 +48,87 @@ def read_traffic(workload):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(model, weight_seed):
-    """Oracle (numpy fp32) decode on a bounded sample of the same workload:
-    depth-truncated models with the real per-layer shapes (2 and 6 layers,
-    each with the full LM head), the fastest of 3 decode steps each after 2
-    warm-up steps; the per-layer and LM-head costs are separated from the two
-    depths and scaled to the full model."""
+def _host_info():
+    """Host cores this process may use, CPU model name and RAM in GiB."""
+    cores = len(os.sched_getaffinity(0))
+    name = ""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    ram = 0.0
+    try:
+        with open("/proc/meminfo") as fh:
+            for line in fh:
+                if line.startswith("MemTotal:"):
+                    ram = int(line.split()[1]) / 2 ** 20
+                    break
+    except OSError:
+        pass
+    return cores, name, ram
+
+
+def cpu_baseline(model, Wd, steps=3):
+    """The oracle (numpy fp32, unchanged) decoding on the host's cores, BLAS
+    threads = the cores this process may use: the same model (the device's
+    weights copied to the host), one warm-up step that also upcasts the
+    weights (not timed), then the median of `steps` decode steps at the
+    first positions of the prompt.  When the host's RAM cannot hold the
+    model's bf16 and fp32 copies, the model is depth-truncated to 2 and 6
+    layers (real per-layer shapes, full LM head) and the per-layer and
+    LM-head times are scaled to the full depth."""
     import numpy as np
-    import torch
 
     import oracle as O
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    depths = (2, 6)
-    times = {}
-    for depth in depths:
-        cfg = synth.truncated(model, depth)
-        Wd = synth.make_weights(cfg, device="cuda", seed=weight_seed)
-        Wn = {k: synth.to_numpy_bf16(v) for k, v in Wd.items()}
-        del Wd
-        torch.cuda.empty_cache()
+    from threadpoolctl import threadpool_limits
+    cores, cpu_name, ram = _host_info()
+    per_layer = sum(int(v[0].numel()) * 2 for k, v in Wd.items()
+                    if k not in ("embed", "lm_head", "final_norm"))
+    total = per_layer * model["n_layers"] + 2 * Wd["lm_head"].numel() * 2
+    full = ram * 2 ** 30 > 3.5 * total + 16 * 2 ** 30
+    prompt = synth.make_prompt(PROMPT, model["vocab"]).tolist()
+
+    def run(cfg):
+        Wn = {}
+        for k, v in Wd.items():
+            if k in ("embed", "lm_head", "final_norm"):
+                Wn[k] = synth.to_numpy_bf16(v)
+            else:
+                Wn[k] = synth.to_numpy_bf16(v[: cfg["n_layers"]])
         Wt = O.OracleWeights(Wn, cfg)
         cache = O.KVCache(cfg)
-        prompt = synth.make_prompt(PROMPT, cfg["vocab"]).tolist()
-        for p, t in enumerate(prompt[:2]):
-            O.decode_step(Wt, cfg, cache, t, p)  # warm-up (weights upcast once)
+        O.decode_step(Wt, cfg, cache, prompt[0], 0)  # warm-up: weights upcast once
         ts = []
-        for p in range(2, 5):
+        for p in range(1, 1 + steps):
             t0 = time.perf_counter()
             O.decode_step(Wt, cfg, cache, prompt[p], p)
             ts.append(time.perf_counter() - t0)
-        times[depth] = float(np.min(ts))
         del Wt, Wn
-    d0, d1 = depths
-    t_layer = (times[d1] - times[d0]) / (d1 - d0)
-    if t_layer <= 0:  # timing noise: fall back to the deeper model's mean
-        t_layer = times[d1] / d1
-    t_head = max(times[d0] - d0 * t_layer, 0.0)
-    t_step = model["n_layers"] * t_layer + t_head
-    return {"value": round(1.0 / t_step, 4), "unit": "tokens/s", "cores": int(threads),
+        return float(np.median(ts))
+
+    with threadpool_limits(limits=cores):
+        if full:
+            t_step = run(model)
+            how = f"full {model['n_layers']}-layer model"
+        else:
+            d0, d1 = 2, 6
+            t0_, t1_ = run(synth.truncated(model, d0)), run(synth.truncated(model, d1))
+            t_layer = max((t1_ - t0_) / (d1 - d0), 1e-9)
+            t_step = model["n_layers"] * t_layer + max(t0_ - d0 * t_layer, 0.0)
+            how = (f"{model['n_layers']}-layer model scaled from {d0}- and {d1}-layer "
+                   f"truncations (host RAM {ram:.0f} GiB too small for the full model)")
+    return {"value": round(1.0 / t_step, 4), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": (f"numpy fp32 oracle, {model['name']} shapes truncated to {d0} and {d1} "
-                       f"layers (+ LM head), fastest of 3 decode steps each at ctx 3-5; "
-                       f"per-layer {t_layer * 1e3:.1f} ms and LM head {t_head * 1e3:.1f} ms "
-                       f"scaled to {model['n_layers']} layers")}
+            "sample": (f"numpy fp32 oracle, {model['name']} {how}, median of {steps} decode "
+                       f"steps at positions 1-{steps} after one warm-up step (weight upcast "
+                       f"not timed); {t_step * 1e3:.1f} ms/step"),
+            "cpu_model": cpu_name, "host_ram_gib": round(ram, 1)}
 
 
 def run_decode(plan, tok_ring, pos_all, first, n, logits=None):
@@ -372,6 +405,21 @@ def main():
     info = plan.info()
     tok_ring = torch.zeros(W_ + K_ + 1, dtype=torch.int32, device=dev)
     start(plan, tok_ring)
+    prefill = None
+    if ctx_kind == "prompt":
+        # the prompt again (it rewrites the same cache entries), timed
+        prompt = synth.make_prompt(ctx0, model["vocab"]).to(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        plan.prefill(0, prompt, ctx0, 0, tok_ring[0:1])
+        e1.record()
+        torch.cuda.synchronize()
+        plan.check()
+        pms = e0.elapsed_time(e1)
+        prefill = {"tokens": ctx0, "ms": round(pms, 3), "tokens_per_s": round(ctx0 / pms * 1e3, 1),
+                   "chunk": 64}
+        log(f"[bench] prefill of {ctx0} tokens: {pms:.3f} ms")
     run_decode(plan, tok_ring, pos_all, 0, W_)
     plan.check()
     stream = torch.cuda.current_stream()
@@ -414,10 +462,11 @@ def main():
         kpo["persistent_speedup_vs_graph"] = round(gms / ms_step, 3)
         log(f"[bench] kernel-per-op in a HIP graph: {gms:.3f} ms/step")
 
+    plan.free()
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
-        cpu = cpu_baseline(model, synth.WEIGHT_SEED)
+        cpu = cpu_baseline(model, Wd)
         log(f"[bench] cpu baseline {cpu['value']} tok/s in {time.time() - t0:.1f}s")
 
     ctx_desc = (f"{ctx0}-token prompt" if ctx_kind == "prompt"
@@ -438,10 +487,16 @@ def main():
                      "traffic": traffic, "kernel": "mk_persistent_kernel",
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
         "kernel_per_op": kpo,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-    plan.free()
+    # release every device resource before the interpreter exits, so no HIP
+    # call runs from teardown (after a profiler's own finalisation)
+    del kv, Wd
+    torch.cuda.synchronize()
+    import gc
+    gc.collect()
 
 
 if __name__ == "__main__":

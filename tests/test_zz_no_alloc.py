@@ -47,8 +47,11 @@ def _compare(Wd, B, maxp, prompt_lens, n_steps, splits):
         kv = PagedKV(TINY, max_batch=B, max_pages_per_seq=maxp, device=DEV)
         for b in range(B):
             kv.assign(b, maxp * 16)
+        # (the allocation-free plan prefills token by token: it has no
+        # internal prompt-chunk plan; the allocating one is set to match)
         plan = mk.Plan(TINY, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=B,
-                       opts=mk.default_options(attn_splits=splits), noalloc=noalloc)
+                       opts=mk.default_options(attn_splits=splits, prefill_chunk=-1),
+                       noalloc=noalloc)
         res.append(_steps(plan, B, prompt_lens, n_steps, TINY["vocab"]))
         if noalloc:
             static_plan = plan
