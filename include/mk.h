@@ -255,6 +255,11 @@ typedef struct {
   int32_t rows_per_pass;     /* static-weight GEMVs: rows streamed per pass
                                 (one register tile); 0 for other tasks       */
   int64_t bytes;             /* algorithmic HBM bytes this task reads       */
+  int32_t data_edges;        /* bit k (k < 3): wait k is a data edge (the
+                                inputs carry the step's tag; no counter is
+                                polled); bit 3 + k: signal k is (the outputs
+                                are tagged; no counter is incremented)       */
+  int32_t pad_;
 } mk_task_info;
 
 int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts,

@@ -158,9 +158,15 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts, mk_task_i
       q.op = t.op; q.layer = t.layer;
       q.a0 = t.a0; q.a1 = t.a1; q.a2 = t.a2; q.a3 = t.a3; q.a4 = t.a4; q.sig_count = t.a5;
       q.n_wait = t.n_wait;
-      for (int k = 0; k < 3; ++k) q.wait_ev[k] = k < t.n_wait ? t.wait_ev[k] & ~kDataEdge : -1;
+      for (int k = 0; k < 3; ++k) {
+        q.wait_ev[k] = k < t.n_wait ? t.wait_ev[k] & ~kDataEdge : -1;
+        if (k < t.n_wait && (t.wait_ev[k] & kDataEdge)) q.data_edges |= 1 << k;
+      }
       q.n_sig = t.n_sig;
-      for (int k = 0; k < 2; ++k) q.sig_ev[k] = k < t.n_sig ? t.sig_ev[k] & ~kDataEdge : -1;
+      for (int k = 0; k < 2; ++k) {
+        q.sig_ev[k] = k < t.n_sig ? t.sig_ev[k] & ~kDataEdge : -1;
+        if (k < t.n_sig && (t.sig_ev[k] & kDataEdge)) q.data_edges |= 1 << (3 + k);
+      }
       q.phase = hp.task_phase[i];
       q.worker = hp.task_worker[i];
       q.rows_per_pass = t.rpp;

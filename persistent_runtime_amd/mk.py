@@ -83,7 +83,7 @@ class mk_task_info(C.Structure):
                 ("wait_ev", C.c_int32 * 3), ("n_sig", C.c_int32),
                 ("sig_ev", C.c_int32 * 2), ("phase", C.c_int32),
                 ("worker", C.c_int32), ("rows_per_pass", C.c_int32),
-                ("bytes", C.c_int64)]
+                ("bytes", C.c_int64), ("data_edges", C.c_int32), ("pad_", C.c_int32)]
 
 
 def _load():
