@@ -13,7 +13,8 @@ oracle timed on a bounded sample.
 
 Other batch-1 workloads: moe30b (48-layer MoE, 128 experts top-8, after an
 8192-token synthetic KV context), longctx (the 8B shape after a 131072-token
-synthetic context), llama70b (80 layers, hidden 8192), tiny.
+synthetic context; longctx256k: 262144 tokens), llama70b (80 layers, hidden
+8192), tiny.
 """
 from __future__ import annotations
 
@@ -147,6 +148,7 @@ WORKLOADS = {
     "llama70b": ("llama70b", "prompt", PROMPT),
     "moe30b": ("moe30b", "synthetic", 8192),
     "longctx": ("llama8b", "synthetic", 131072),
+    "longctx256k": ("llama8b", "synthetic", 262144),
 }
 
 
@@ -365,7 +367,8 @@ def main():
         return
     mname, ctx_kind, ctx0 = WORKLOADS[args.workload]
     model = synth.MODELS[mname]
-    default_steps = {"moe30b": 248, "longctx": 56, "llama70b": 120}.get(args.workload, 504)
+    default_steps = {"moe30b": 248, "longctx": 56, "longctx256k": 32,
+                     "llama70b": 120}.get(args.workload, 504)
     W_, K_ = args.warmup, args.steps if args.steps is not None else default_steps
     total = ctx0 + W_ + K_
     maxp = (total + 15) // 16

@@ -159,13 +159,22 @@ typedef struct {
 
 typedef struct mk_plan mk_plan;
 
-/* Fill *opts with defaults (persistent executor, auto sizes). */
+/* Fill *opts with defaults (persistent executor, auto sizes).  opts NULL is
+ * ignored. */
 void mk_plan_options_default(mk_plan_options *opts);
 
-/* Lower the model into a task list, validate it, allocate the plan's device
- * state (task table, event counters, activation scratch, RoPE table) on the
- * device and upload it.  Synchronous.  *out receives the plan (free with
- * mk_free).  opts may be NULL. */
+/* The host-side lowering (MPK summary, "Part 1. Compiler": the computation
+ * graph becomes a task graph of per-tile tasks joined by events; Cohere,
+ * "Egyetlen tartós kernelre épül a kiszolgálás": the blocks work from a task
+ * list prepared on the host, dependencies signalled by counters in global
+ * memory): lower the model into a task list, validate it, allocate the
+ * plan's device state (task table, event counters, activation scratch, RoPE
+ * table) on the device and upload it.  Synchronous.  *out receives the plan
+ * (free with mk_free); the plan keeps pointers to the caller's weights, pools
+ * and page table, which must outlive it.  opts may be NULL.  Errors:
+ * MK_ERR_INVALID_ARG (NULL or unaligned pointers, bad options),
+ * MK_ERR_INVALID_CONFIG / MK_ERR_UNSUPPORTED (shapes the kernels cannot run),
+ * MK_ERR_OOM, MK_ERR_HIP; *out is NULL on failure. */
 int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
                   const mk_plan_options *opts, mk_plan **out);
 
@@ -184,7 +193,14 @@ int mk_build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
 int mk_build_plan_noalloc(const mk_config *cfg, const mk_weights *w, const mk_kv *kv,
                           const mk_plan_options *opts, mk_plan **out);
 
-/* One decode step for all max_batch slots.
+/* One decode step for all max_batch slots, as one launch of the persistent
+ * kernel (Cohere, "Egyetlen tartós kernelre épül a kiszolgálás": one resident
+ * block per SM runs the whole forward pass from the task list; MPK summary,
+ * "Part 2. Runtime": workers run their task queues and bump event counters).
+ * Asynchronous on `stream`; returns MK_ERR_INVALID_ARG for NULL required
+ * pointers; device-side errors (a token outside the vocabulary, a position
+ * beyond the page table, a page id outside the pool, a dependency wait past
+ * its budget) are reported by mk_plan_status.
  *  tokens_dev[b]     input token of slot b (int32, device)
  *  positions_dev[b]  0-based position of that token (= number of tokens
  *                    already cached for the slot); < 0 marks an empty slot
@@ -224,11 +240,18 @@ int mk_prefill(mk_plan *plan, int32_t slot, const int32_t *tokens_dev,
                int32_t *next_token_dev, float *logits_dev);
 
 /* Synchronise `stream` and report a device-side error of this plan's last
- * steps (MK_ERR_TIMEOUT when a dependency wait exceeded its budget).  The
- * error is cleared and the plan's counters are reset. */
+ * steps (MK_ERR_TIMEOUT when a dependency wait exceeded its budget, the
+ * message naming the task and the event; MK_ERR_INVALID_ARG for a bad token,
+ * position, page id or page-table row).  The error is cleared and the plan's
+ * counters are reset, so the next step runs normally.  The event-counter
+ * protocol it watches is the MPK summary's ("Part 2. Runtime", event-based
+ * execution: a finished task bumps its event's counter, the event fires at
+ * its threshold). */
 int mk_plan_status(mk_plan *plan, void *stream);
 
-/* Release everything the plan allocated.  NULL is ignored. */
+/* Release everything the plan allocated (after synchronising its device).
+ * The caller's weights, pools and page table are untouched.  NULL is
+ * ignored. */
 void mk_free(mk_plan *plan);
 
 /* Message of the last failing call on this thread ("" if none). */
@@ -239,6 +262,8 @@ const char *mk_last_error(void);
 const char *mk_build_id(void);
 
 /* ---- introspection (host only; no GPU needed) ----------------------------
+ * The task graph of the MPK summary's "Part 1. Compiler" (tasks, events and
+ * the edges between them) as the planner builds it.
  * mk_inspect_plan runs the planner for `cfg` with opts->n_cus CUs and
  * opts->n_workgroups workers (0: 256 each) without touching a device and
  * copies the task graph into caller arrays (cap = capacity in elements;
@@ -269,17 +294,24 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts,
 /* Persistent-executor trace of the last step run with debug_trace = 1:
  * per task {start ticket, finish ticket, run count, workgroup,
  * deps-ready time, finish time (100 MHz ticks, low 32 bits)}, 6 x uint32
- * each.  Synchronises `stream`.  cap in tasks. */
+ * each (debug_trace = 2: words 0 and 1 hold intermediate times instead of
+ * tickets).  The check it serves: every task runs once, after every producer
+ * of its inputs (MPK summary, "Part 2. Runtime").  Synchronises `stream`.
+ * cap in tasks.  MK_ERR_INVALID_ARG for a plan built without debug_trace. */
 int mk_read_trace(mk_plan *plan, void *stream, uint32_t *out, int32_t cap);
 
-/* MoE plans: the expert ids (int32) and renormalised routing weights (fp32)
+/* MoE plans (Cohere, "Honnan jön a gyorsulás?": the router, then each expert
+ * down projection after its experts' up projections): the expert ids (int32)
+ * and renormalised routing weights (fp32)
  * the last step chose, [n_layers][max_batch][top_k] each, ids ascending per
  * (layer, slot).  Synchronises `stream`; cap in entries; either output may be
  * NULL.  MK_ERR_INVALID_ARG for a dense model. */
 int mk_read_routing(mk_plan *plan, void *stream, int32_t *ids, float *weights, int32_t cap);
 
-/* Number of tasks and events of a built plan, and the number of CUs it was
- * sized for. */
+/* Number of tasks and events of a built plan, the number of CUs it was
+ * sized for (the wave-quantization target of Cohere, "Honnan jön a
+ * gyorsulás?") and its launches per step under KERNEL_PER_OP.  Any output
+ * may be NULL. */
 int mk_plan_info(const mk_plan *plan, int32_t *n_tasks, int32_t *n_events,
                  int32_t *n_cus, int32_t *n_phases);
 

@@ -5,7 +5,9 @@ keys and values, the same values given to the oracle's cache).
 With one attention split per KV head, every wave of an attention task walks
 more than 64 pages, so the page-id chunks after the first are taken; the
 automatic split count is checked at the same contexts.  The full 131072-token
-context of the long-context workload is one of the cases; one case keeps the
+context of the long-context workload is one of the cases, and a 262136-token
+context (the 256K contexts of the Cohere article, "Folyamatos
+batchkezelés") another; one case keeps the
 GEMV passes in registers only (no LDS weight slots), where a task whose next
 task waits behind attention loads that task's first pass after its own
 outputs.
@@ -37,7 +39,7 @@ def _weights():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("ctx,splits,lds", [(20000, 1, 0), (20000, 0, 0), (131064, 1, 0),
-                                            (131064, 0, 0), (20000, 0, -1)])
+                                            (131064, 0, 0), (20000, 0, -1), (262136, 0, 0)])
 def test_long_context_attention_chunks(ctx, splits, lds):
     """lds = -1: GEMV passes in registers only (no LDS weight slots)."""
     Wd, Wt = _weights()
