@@ -204,6 +204,7 @@ def run_ragged(args, torch):
         log(f"[bench] ragged B={B}: {sum(sched['ctx0'])} cached tokens in {kv.n_pages} pages "
             f"({time.time() - t0:.1f}s)")
         opts = {} if args.attn_splits is None else {"attn_splits": args.attn_splits}
+        opts["attn_order"] = args.attn_order
 
         def run(plan, k0, k1, timed):
             tok = torch.as_tensor(synth.make_prompt(B, model["vocab"], seed=7 + k0),
@@ -268,6 +269,7 @@ def run_ragged(args, torch):
             "config": {"workload": f"llama8b ragged decode, batch {B}, contexts U[128,16384], "
                                    f"16-token shuffled pages, retire/join p=1/32 per step",
                        "batch": B, "attn_splits": args.attn_splits,
+                       "attn_order": args.attn_order,
                        "tasks_per_step": info["n_tasks"]},
             "sol_fraction": round(achieved / 8000.0, 4),
             "bytes_per_step": int(sum(nbytes) / kk),
@@ -331,6 +333,9 @@ def main():
     ap.add_argument("--attn-splits", type=int, default=None,
                     help="KV splits per (sequence, KV head); default: the planner's choice")
     ap.add_argument("--kpo-steps", type=int, default=64, help="kernel-per-op comparison steps")
+    ap.add_argument("--attn-order", type=int, default=0, choices=(-1, 0, 1),
+                    help="ragged: claim order of pooled attention (0: the plan's default, "
+                         "longest context first; -1: slot order)")
     ap.add_argument("--weight-lds", choices=("auto", "on", "off"), default="auto",
                     help="LDS weight slots of single-slot GEMV passes (auto: the planner's choice)")
     ap.add_argument("--no-weight-lds", action="store_true", help="the same as --weight-lds off")

@@ -155,6 +155,13 @@ typedef struct {
                             (64 when the model's row counts allow matrix-core
                             tiles, else token by token), -1 = one token per
                             decode step, 16..64 = that many                  */
+  int32_t attn_order;    /* claim order of pooled attention tasks (plans with
+                            claimed attention, at most 64 slots): 0 = auto
+                            (= 1); 1 = longest context first (throughput: the
+                            layer's last claims are its shortest tasks);
+                            2 = higher mk_batch_step priority first, then
+                            longest context (latency targets of some
+                            sequences ahead of others); -1 = slot order      */
 } mk_plan_options;
 
 typedef struct mk_plan mk_plan;
@@ -220,10 +227,13 @@ int mk_decode_step(mk_plan *plan, const int32_t *tokens_dev,
  * the consecutive positions of a prompt chunk of that sequence, each attending
  * causally to everything before it including the chunk's earlier tokens --
  * only in plans built with shared_seqs = 1; otherwise the rows must be
- * distinct.  Outputs as mk_decode_step (per slot). */
+ * distinct.  priorities_dev (optional, device int32 [max_batch], higher =
+ * more urgent) orders the claimed attention tasks of plans built with
+ * attn_order = 2 (MPK summary, "भविष्य की दिशा": priority-based task
+ * scheduling); it changes no result.  Outputs as mk_decode_step (per slot). */
 int mk_batch_step(mk_plan *plan, const int32_t *tokens_dev, const int32_t *positions_dev,
-                  const int32_t *seq_rows_dev, void *stream, int32_t *next_tokens_dev,
-                  float *logits_dev);
+                  const int32_t *seq_rows_dev, const int32_t *priorities_dev, void *stream,
+                  int32_t *next_tokens_dev, float *logits_dev);
 
 /* Feed n prompt tokens tokens_dev[0..n) of one slot at positions
  * start_pos..start_pos+n-1, filling its KV pages (other slots are left

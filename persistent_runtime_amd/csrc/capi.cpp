@@ -368,6 +368,10 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
       return fail(MK_ERR_INVALID_ARG, "unknown executor");
     if (o.prefill_chunk > 0 && (o.prefill_chunk < 16 || o.prefill_chunk > kMfmaMaxBatch))
       return fail(MK_ERR_INVALID_ARG, "prefill_chunk must be 0, -1 or 16..64");
+    if (o.attn_order < -1 || o.attn_order > 2)
+      return fail(MK_ERR_INVALID_ARG, "attn_order must be -1, 0, 1 or 2");
+    if (o.attn_order > 0 && cfg->max_batch > kMfmaMaxBatch)
+      return fail(MK_ERR_UNSUPPORTED, "attn_order needs max_batch <= 64");
     std::string err;
     int rc = check_config(*cfg, err);
     if (rc != MK_OK) return fail(rc, err);
@@ -522,6 +526,11 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     d.kcnt = d.att_cnt + c.n_layers * c.max_batch * c.n_kv_heads;
     d.pool_cnt = d.kcnt + hp.n_kcnt;
     d.attn_pool = hp.attn_pool ? 1 : 0;
+    // claim order: longest context first unless asked otherwise (measured on
+    // the 8B shape with contexts U[128, 16384]: 16 slots -3.3 %, 64 -0.6 %)
+    d.attn_order = !hp.attn_pool || o.attn_order < 0 || c.max_batch > kMfmaMaxBatch
+                       ? 0
+                       : (o.attn_order == 0 ? 1 : o.attn_order);
     d.tasks = d_tasks;
     d.n_tasks = T;
     d.worker_off = d_wq;
@@ -600,12 +609,14 @@ static bool stale_static(const mk_plan *plan) {
 }
 
 static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positions,
-                     const int32_t *rows, hipStream_t s, int32_t *next, float *logits) {
+                     const int32_t *rows, hipStream_t s, int32_t *next, float *logits,
+                     const int32_t *prio = nullptr) {
   const DevPlan &d = plan->d;
   CallArgs ca;
   ca.tokens = tokens;
   ca.positions = positions;
   ca.rows = rows;
+  ca.prio = prio;
   ca.next_tokens = next;
   ca.logits = logits;
   if (plan->graph_replay) {
@@ -660,8 +671,8 @@ int mk_decode_step(mk_plan *plan, const int32_t *tokens_dev, const int32_t *posi
 }
 
 int mk_batch_step(mk_plan *plan, const int32_t *tokens_dev, const int32_t *positions_dev,
-                  const int32_t *seq_rows_dev, void *stream, int32_t *next_tokens_dev,
-                  float *logits_dev) {
+                  const int32_t *seq_rows_dev, const int32_t *priorities_dev, void *stream,
+                  int32_t *next_tokens_dev, float *logits_dev) {
   try {
     if (!plan) return fail(MK_ERR_INVALID_ARG, "plan is NULL");
     if (!tokens_dev || !positions_dev || !seq_rows_dev || !next_tokens_dev)
@@ -670,7 +681,7 @@ int mk_batch_step(mk_plan *plan, const int32_t *tokens_dev, const int32_t *posit
       return fail(MK_ERR_INVALID_ARG, "a newer mk_build_plan_noalloc plan replaced this plan's state");
     DeviceGuard guard(plan->device);
     return step_impl(plan, tokens_dev, positions_dev, seq_rows_dev, (hipStream_t)stream,
-                     next_tokens_dev, logits_dev);
+                     next_tokens_dev, logits_dev, priorities_dev);
   } catch (const std::exception &ex) {
     return fail(MK_ERR_PLAN, ex.what());
   }

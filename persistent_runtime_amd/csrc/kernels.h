@@ -190,6 +190,7 @@ struct Smem {
   uint32_t ring[kRing][32];                                 // task descriptors
   float misc[64];
   int imisc[64];
+  int order[kMfmaMaxBatch];  // claimed attention: slot of each claim rank
 };
 
 // A task descriptor held in scalar registers.
@@ -2386,8 +2387,35 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
 // holds entries of the layer included, so step e's claims start at
 // e * (claims per step).  Every task still runs exactly once; each reports
 // its own completion as it would in a worker queue.
+// Claim order of pooled attention for this step (the MPK summary's roadmap,
+// "भविष्य की दिशा": priority-based and throughput-oriented task scheduling).
+// Slot b's rank is the number of slots whose key is larger, ties going to the
+// lower slot; the key is (priority, context length) for order 2 and the
+// context length for order 1, so the longest attention tasks of the most
+// urgent sequences are claimed first and the layer's last claims are the
+// shortest (longest-processing-time-first).  Empty slots rank last.
+DEV void claim_order(Smem &sm, CP &d, const CallArgs &ca) {
+  const int b = tidx();
+  if (b < d.B) {
+    auto key = [&](int s) -> int64_t {
+      const int p = ldg(ca.positions + s);
+      if (p < 0) return INT64_MIN;
+      const int64_t pr = (d.attn_order == 2 && ca.prio) ? (int64_t)ldg(ca.prio + s) : 0;
+      return (pr << 32) + p;
+    };
+    const int64_t kb = key(b);
+    int rank = 0;
+    for (int s = 0; s < d.B; ++s) {
+      const int64_t ks = key(s);
+      rank += ks > kb || (ks == kb && s < b);
+    }
+    sm.order[rank] = b;
+  }
+}
+
 DEV bool run_attn_pool(Smem &sm, CP &d, const CallArgs &ca, const TD &t0, WState &ws) {
   const int first = t0.a4, n = t0.rpp & 0xffff;
+  const int per_slot = n / d.B;  // the layer's tasks are slot-major
   const uint32_t per_step = (uint32_t)t0.rpp >> 16;
   uint32_t *cnt = d.pool_cnt + t0.layer;
   for (;;) {
@@ -2399,7 +2427,8 @@ DEV bool run_attn_pool(Smem &sm, CP &d, const CallArgs &ca, const TD &t0, WState
     const int idx = uni(sm.imisc[3]);
     __syncthreads();  // every wave has read the claim
     if (idx < 0 || idx >= n) return true;
-    const TD t = td_from_table(d.tasks, ((const AS4 int *)d.task_pos)[first + idx]);
+    const int k = d.attn_order ? sm.order[idx / per_slot] * per_slot + idx % per_slot : idx;
+    const TD t = td_from_table(d.tasks, ((const AS4 int *)d.task_pos)[first + k]);
     if (!run_small(sm, d, ca, t, true, ws)) return false;
   }
 }
@@ -2493,6 +2522,7 @@ __global__ void __launch_bounds__(kThreads)
   CP &d = *(CP *)dplan;
   const CallArgs ca = resolve_args(d, ca_in);
   if (tidx() == 0) sm.imisc[2] = 0;  // no tagged-data failure (the tag is never 0)
+  if (d.attn_pool && d.attn_order) claim_order(sm, d, ca);  // read after the barrier below
   const int wid = blockIdx.x;
   const int beg = ((const AS4 int *)d.worker_off)[wid];
   const int end = ((const AS4 int *)d.worker_off)[wid + 1];

@@ -149,6 +149,9 @@ struct DevPlan {
   uint32_t *kcnt;          // split-K arrivals per matrix-core row block, after att_cnt
   uint32_t *pool_cnt;      // claimed-attention counters per layer, after kcnt
   int32_t attn_pool;       // persistent workers claim attention tasks at run time
+  int32_t attn_order;      // claim order of pooled attention: 0 slot order,
+                           // 1 longest context first, 2 caller priority first
+                           // (then longest context)
   float *kpart;            // split-K partial products, kpart_slot(B) floats per tile
   uint32_t *ctrl;
   const Task *tasks;           // worker-major: each worker's queue is contiguous
@@ -174,6 +177,7 @@ struct DevPlan {
 struct CallArgs {
   const int32_t *tokens, *positions;
   const int32_t *rows;   // page-table row of each slot's sequence; null: row = slot
+  const int32_t *prio;   // per-slot priority (higher first) for attn_order 2, or null
   int32_t *next_tokens;
   float *logits;
   uint32_t epoch;

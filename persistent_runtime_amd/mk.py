@@ -73,7 +73,7 @@ class mk_plan_options(C.Structure):
                 ("graph_replay", C.c_int32), ("batched_mfma", C.c_int32),
                 ("attn_pool", C.c_int32), ("weight_lds", C.c_int32),
                 ("debug_withhold", C.c_int32), ("shared_seqs", C.c_int32),
-                ("prefill_chunk", C.c_int32)]
+                ("prefill_chunk", C.c_int32), ("attn_order", C.c_int32)]
 
 
 class mk_task_info(C.Structure):
@@ -108,7 +108,7 @@ def _load():
     lib.mk_build_plan_noalloc.argtypes = lib.mk_build_plan.argtypes
     lib.mk_decode_step.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.mk_prefill.argtypes = [vp, i32, vp, i32, i32, vp, vp, vp]
-    lib.mk_batch_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.mk_batch_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     lib.mk_plan_status.argtypes = [vp, vp]
     lib.mk_free.argtypes = [vp]
     lib.mk_free.restype = None
@@ -247,9 +247,11 @@ class Plan:
         _check(lib.mk_decode_step(self.handle, _ptr(tokens), _ptr(positions),
                                   self._stream(stream), _ptr(next_tokens), _ptr(logits)))
 
-    def batch_step(self, tokens, positions, seq_rows, next_tokens, logits=None, stream=None):
+    def batch_step(self, tokens, positions, seq_rows, next_tokens, logits=None, stream=None,
+                   priorities=None):
         _check(lib.mk_batch_step(self.handle, _ptr(tokens), _ptr(positions), _ptr(seq_rows),
-                                 self._stream(stream), _ptr(next_tokens), _ptr(logits)))
+                                 _ptr(priorities), self._stream(stream), _ptr(next_tokens),
+                                 _ptr(logits)))
 
     def prefill(self, slot, tokens, n, start_pos, next_token=None, logits=None, stream=None):
         _check(lib.mk_prefill(self.handle, slot, _ptr(tokens), n, start_pos,
