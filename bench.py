@@ -470,6 +470,25 @@ def main():
         kpo["persistent_speedup_vs_graph"] = round(gms / ms_step, 3)
         log(f"[bench] kernel-per-op in a HIP graph: {gms:.3f} ms/step")
 
+    sched = None
+    if not args.no_kpo:
+        # the MPK-style executor (scheduler wavefronts and worker queues) on
+        # the same workload
+        plan_s = build(mk.MK_EXEC_SCHEDULED)
+        ring3 = torch.zeros(W_ + K_ + 1, dtype=torch.int32, device=dev)
+        start(plan_s, ring3)
+        n = min(args.kpo_steps, W_ + K_)
+        run_decode(plan_s, ring3, pos_all, 0, 2)
+        _, sel, _ = timed_steps(plan_s, ring3, pos_all, 2, n - 2, stream, torch)
+        plan_s.check()
+        sms = sel * 1e3 / (n - 2)
+        sched = {"ms_per_step": round(sms, 4), "tokens_per_s": round(1e3 / sms, 2),
+                 "schedulers": 4, "workers": plan_s.info()["n_cus"] - 1,
+                 "persistent_speedup": round(sms / ms_step, 3),
+                 "same_tokens_first_steps": bool(torch.equal(ring3[:n], tok_ring[:n]))}
+        log(f"[bench] scheduled (MPK-style) executor: {sms:.3f} ms/step")
+        plan_s.free()
+
     plan.free()
     cpu = None
     if not args.no_cpu_baseline:
@@ -495,6 +514,7 @@ def main():
                      "traffic": traffic, "kernel": "mk_persistent_kernel",
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4)},
         "kernel_per_op": kpo,
+        "scheduled_executor": sched,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

@@ -53,8 +53,16 @@ enum {
  * each workgroup running its own planner-assigned queue of tasks in list
  * order, ordered across workgroups by HBM event counters.
  * KERNEL_PER_OP: the same task code, one launch per operation of each layer,
- * stream order standing in for the counters (the launch-overhead baseline). */
-enum { MK_EXEC_PERSISTENT = 0, MK_EXEC_KERNEL_PER_OP = 1 };
+ * stream order standing in for the counters (the launch-overhead baseline).
+ * SCHEDULED: the MPK runtime's other design (MPK summary, "Part 2. Runtime":
+ * Worker, Scheduler, event-based execution): one launch per step; workgroup 0
+ * holds four scheduler wavefronts, every other workgroup is a worker with a
+ * task queue in HBM.  A worker runs the tasks dispatched to its queue in
+ * arrival order and bumps their events' counters; the task that completes an
+ * event activates it into a scheduler's queue; the scheduler counts the event
+ * for each dependent task and dispatches the tasks whose events have all
+ * fired.  Single-slot and vector multi-slot plans (no matrix-core tiles). */
+enum { MK_EXEC_PERSISTENT = 0, MK_EXEC_KERNEL_PER_OP = 1, MK_EXEC_SCHEDULED = 2 };
 
 /* Task operations (values of mk_task_info.op). */
 enum {

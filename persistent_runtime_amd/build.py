@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
-SOURCES = ["kernels_m1.hip", "kernels_m2.hip", "kernels_m0.hip", "kernels.hip",
-           "planner.cpp", "capi.cpp"]
+SOURCES = ["kernels_m1.hip", "kernels_m2.hip", "kernels_m0.hip", "kernels_sched.hip",
+           "kernels.hip", "planner.cpp", "capi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

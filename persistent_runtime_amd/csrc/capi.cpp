@@ -144,6 +144,7 @@ int mk_inspect_plan(const mk_config *cfg, const mk_plan_options *opts, mk_task_i
     if (opts) o = *opts;
     int n_cus = o.n_cus > 0 ? o.n_cus : 256;
     int n_workers = o.n_workgroups > 0 ? o.n_workgroups : n_cus;
+    if (o.executor == MK_EXEC_SCHEDULED) n_workers -= 1;  // workgroup 0 schedules
     HostPlan hp;
     std::string err;
     int rc = build_host_plan(*cfg, o, n_cus, n_workers, hp, err);
@@ -364,8 +365,10 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     mk_plan_options o;
     mk_plan_options_default(&o);
     if (opts) o = *opts;
-    if (o.executor != MK_EXEC_PERSISTENT && o.executor != MK_EXEC_KERNEL_PER_OP)
+    if (o.executor != MK_EXEC_PERSISTENT && o.executor != MK_EXEC_KERNEL_PER_OP &&
+        o.executor != MK_EXEC_SCHEDULED)
       return fail(MK_ERR_INVALID_ARG, "unknown executor");
+    const bool sched = o.executor == MK_EXEC_SCHEDULED;
     if (o.prefill_chunk > 0 && (o.prefill_chunk < 16 || o.prefill_chunk > kMfmaMaxBatch))
       return fail(MK_ERR_INVALID_ARG, "prefill_chunk must be 0, -1 or 16..64");
     if (o.attn_order < -1 || o.attn_order > 2)
@@ -412,7 +415,10 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     p->grid = o.n_workgroups > 0 ? o.n_workgroups : hw_cus;
     if (p->grid > hw_cus)
       return fail(MK_ERR_INVALID_ARG, "more persistent workers than CUs (one resident workgroup per CU)");
-    rc = build_host_plan(*cfg, o, n_cus, p->grid, p->hp, err);
+    if (sched && p->grid < 2)
+      return fail(MK_ERR_INVALID_ARG, "the scheduled executor needs at least 2 workgroups");
+    // scheduled executor: workgroup 0 holds the schedulers, the rest are workers
+    rc = build_host_plan(*cfg, o, n_cus, sched ? p->grid - 1 : p->grid, p->hp, err);
     if (rc != MK_OK) return fail(rc, err);
     HostPlan &hp = p->hp;
     const mk_config &c = hp.cfg;
@@ -426,6 +432,38 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     max_thr = std::max(max_thr, kMaxKSplit);  // split-K arrival counters
     for (const Task &t : hp.tasks)              // claimed-attention counters
       if (t.op == OP_ATTN && hp.attn_pool) max_thr = std::max(max_thr, t.rpp >> 16);
+    // scheduled executor: per-task dependency counts, queue reservations
+    std::vector<int32_t> s_cons_off, s_cons, s_deps, s_worker, s_wcount, s_woff, s_scount,
+        s_soff, s_roots;
+    const int NS = 4;
+    if (sched) {
+      const int W = hp.n_workers;
+      s_cons_off.assign(E + 1, 0);
+      s_deps.assign(T, 0);
+      s_worker.assign(hp.task_worker.begin(), hp.task_worker.end());
+      for (int i = 0; i < T; ++i) {
+        s_deps[i] = hp.tasks[i].n_wait;
+        for (int k = 0; k < hp.tasks[i].n_wait; ++k)
+          s_cons_off[(hp.tasks[i].wait_ev[k] & ~kDataEdge) + 1]++;
+        if (hp.tasks[i].n_wait == 0) s_roots.push_back(i);
+      }
+      for (int e = 0; e < E; ++e) s_cons_off[e + 1] += s_cons_off[e];
+      s_cons.assign(s_cons_off[E], 0);
+      std::vector<int32_t> fill(s_cons_off.begin(), s_cons_off.end() - 1);
+      for (int i = 0; i < T; ++i)
+        for (int k = 0; k < hp.tasks[i].n_wait; ++k)
+          s_cons[fill[hp.tasks[i].wait_ev[k] & ~kDataEdge]++] = i;
+      s_wcount.assign(W, 0);
+      for (int i = 0; i < T; ++i) s_wcount[hp.task_worker[i]]++;
+      s_woff.assign(W + 1, 0);
+      for (int w = 0; w < W; ++w) s_woff[w + 1] = s_woff[w] + s_wcount[w];
+      s_scount.assign(NS, 0);
+      for (int e = 0; e < E; ++e) s_scount[e % NS]++;
+      s_soff.assign(NS + 1, 0);
+      for (int k = 0; k < NS; ++k) s_soff[k + 1] = s_soff[k] + s_scount[k];
+      for (int v : s_wcount) max_thr = std::max(max_thr, v);
+      for (int v : s_scount) max_thr = std::max(max_thr, v);
+    }
     p->epoch_limit = (uint32_t)(((1u << 31) - 1u) / (uint32_t)max_thr) - 2u;
 
     // device allocations
@@ -435,6 +473,8 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     if ((rc = p->alloc(&d_wq, hp.worker_off.size() + hp.worker_list.size(), "worker queues")))
       return rc;
     p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads + hp.n_kcnt + c.n_layers;
+    const int n_sched_cnt = sched ? T + hp.n_workers + NS : 0;  // pending, wtail, stail
+    p->n_att_cnt += n_sched_cnt;
     p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
     const int64_t n_kpart = hp.n_kpart * kpart_slot(B);
@@ -451,6 +491,17 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     if ((rc = p->alloc(&rope, (size_t)2 * hp.max_pos * half, "rope tables"))) return rc;
     uint32_t *trace = nullptr;
     if (p->trace && (rc = p->alloc(&trace, (size_t)T * 6, "trace"))) return rc;
+    int32_t *sched_ints = nullptr;
+    uint64_t *sched_rings = nullptr;
+    const size_t n_sched_ints = s_cons_off.size() + s_cons.size() + s_deps.size() +
+                                s_worker.size() + s_wcount.size() + s_woff.size() +
+                                s_scount.size() + s_soff.size() + s_roots.size() +
+                                (sched ? (size_t)E : 0);
+    if (sched) {
+      if ((rc = p->alloc(&sched_ints, n_sched_ints, "scheduler tables"))) return rc;
+      if ((rc = p->alloc(&sched_rings, (size_t)T + E, "scheduler queues"))) return rc;
+      HIP_TRY(hipMemset(sched_rings, 0, ((size_t)T + E) * 8), "zero queues");
+    }
     if ((rc = p->alloc(&p->stage_logits, (size_t)B * c.vocab, "prefill logits"))) return rc;
 
     // uploads
@@ -538,7 +589,36 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     d.n_workers = hp.n_workers;
     d.spin_budget = o.spin_budget > 0 ? o.spin_budget : 100000000LL;  // 1 s at 100 MHz
     d.trace = trace;
-    d.trace_mode = o.debug_trace;
+    d.trace_mode = sched && trace ? 3 : o.debug_trace;
+    if (sched) {
+      int32_t *q = sched_ints;
+      auto put = [&](const std::vector<int32_t> &v) -> const int32_t * {
+        int32_t *at = q;
+        if (!v.empty())
+          (void)hipMemcpy(at, v.data(), v.size() * 4, hipMemcpyHostToDevice);
+        q += v.size();
+        return at;
+      };
+      d.cons_off = put(s_cons_off);
+      d.cons = put(s_cons);
+      d.n_deps = put(s_deps);
+      d.t_worker = put(s_worker);
+      d.w_count = put(s_wcount);
+      d.w_off = put(s_woff);
+      d.s_count = put(s_scount);
+      d.s_off = put(s_soff);
+      d.roots = put(s_roots);
+      d.ev_thr = put(hp.ev_thr);
+      d.n_roots = (int32_t)s_roots.size();
+      d.n_sched = NS;
+      HIP_TRY(hipDeviceSynchronize(), "upload scheduler tables");
+      d.wring = sched_rings;
+      d.sring = sched_rings + T;
+      // counters after the arrival counters: reset with them
+      d.pending = p->ctrl + CTRL_WORDS + E + (p->n_att_cnt - n_sched_cnt);
+      d.wtail = d.pending + T;
+      d.stail = d.wtail + hp.n_workers;
+    }
     if (o.debug_withhold < 0 || o.debug_withhold > T)
       return fail(MK_ERR_INVALID_ARG, "debug_withhold names no task of the plan");
     d.withhold = o.debug_withhold - 1;
@@ -632,7 +712,13 @@ static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positi
     ca.tag = plan->tag;
   }
   ca.epoch = plan->epoch;
-  if (plan->executor == MK_EXEC_PERSISTENT) {
+  if (plan->executor == MK_EXEC_SCHEDULED) {
+    if (plan->trace) {
+      HIP_TRY(launch_zero_u32(d.trace, (int)plan->hp.tasks.size() * 6, s), "trace reset");
+      HIP_TRY(launch_zero_u32(plan->ctrl + CTRL_CLOCK, 1, s), "trace reset");
+    }
+    HIP_TRY(launch_sched(plan->d_dev, ca, plan->grid, s), "scheduled launch");
+  } else if (plan->executor == MK_EXEC_PERSISTENT) {
     if (plan->trace) {
       HIP_TRY(launch_zero_u32(d.trace, (int)plan->hp.tasks.size() * 6, s), "trace reset");
       HIP_TRY(launch_zero_u32(plan->ctrl + CTRL_CLOCK, 1, s), "trace reset");

@@ -372,7 +372,7 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws,
 // start / finish time (100 MHz).  Trace mode 2 keeps times only and uses
 // words 0 and 1 for intermediate time stamps.
 DEV void trace_start(CP &d, const TD &t) {
-  if (d.trace && tidx() == 0) {
+  if (d.trace && d.trace_mode != 3 && tidx() == 0) {
     uint32_t *tr = d.trace + (size_t)t.gidx * 6;
     if (d.trace_mode == 1) stg(tr + 0, atomicAdd(&d.ctrl[CTRL_CLOCK], 1u));
     atomicAdd(&tr[2], 1u);
@@ -381,7 +381,7 @@ DEV void trace_start(CP &d, const TD &t) {
   }
 }
 DEV void trace_finish(CP &d, const TD &t) {
-  if (d.trace && tidx() == 0) {
+  if (d.trace && d.trace_mode != 3 && tidx() == 0) {
     uint32_t *tr = d.trace + (size_t)t.gidx * 6;
     if (d.trace_mode == 1) stg(tr + 1, atomicAdd(&d.ctrl[CTRL_CLOCK], 1u));
     stg(tr + 5, (uint32_t)wall_clock64());

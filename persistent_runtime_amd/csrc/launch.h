@@ -13,6 +13,10 @@ namespace mk {
 hipError_t launch_persistent(const DevPlan *d, const CallArgs &ca, int grid, int mode,
                              hipStream_t s);
 
+// Scheduled executor: workgroup 0 runs the schedulers, 1..grid-1 the
+// workers (d must hold the scheduled executor's queues and tables).
+hipError_t launch_sched(const DevPlan *d, const CallArgs &ca, int grid, hipStream_t s);
+
 // Kernel-per-op: tasks [first, first+count) of one launch phase, one
 // workgroup per task, no counters (stream order orders the phases).
 hipError_t launch_phase(const DevPlan *d, const CallArgs &ca, int first, int count,

@@ -160,8 +160,22 @@ struct DevPlan {
   const int32_t *task_pos;     // list index -> position in `tasks`
   int32_t n_workers;
   int64_t spin_budget;     // in s_memrealtime ticks (100 MHz)
+  // scheduled executor (null otherwise): consumers of each event
+  // [cons_off[e], cons_off[e+1]) in cons, counter waits per task, worker of
+  // each task; per-worker queue sizes and offsets into wring, per-scheduler
+  // activation counts and offsets into sring; the monotonic counters
+  // pending[T], wtail[W], stail[NS] (after the arrival counters, reset with
+  // them)
+  const int32_t *cons_off, *cons, *n_deps, *t_worker;
+  const int32_t *w_count, *w_off, *s_count, *s_off;
+  const int32_t *roots, *ev_thr;  // tasks with no waits; per-step thresholds
+  int32_t n_roots;
+  uint32_t *pending, *wtail, *stail;
+  uint64_t *wring, *sring;
+  int32_t n_sched;
   uint32_t *trace;         // 6 u32 per task, or null
-  int32_t trace_mode;      // 1: dependency tickets + times, 2: times only
+  int32_t trace_mode;      // 1: dependency tickets + times, 2: times only,
+                           // 3: the scheduled executor records (tickets + times)
   int32_t withhold;        // test hook: list index of a task whose counter
                            // signals are withheld, or -1
   int32_t pt_rows;         // rows of the page table (the slots of the plan

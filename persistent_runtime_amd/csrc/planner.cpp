@@ -369,7 +369,11 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   if (o.attn_pool >= 0 && B >= 16)
     p.S = std::max(1, std::min({std::max(2, 2 * n_workers / (nkv * B)), std::max(1, ctx / 256), 64}));
   if (o.attn_splits > 0) p.S = std::min(o.attn_splits, 128);  // merge keeps G*S pairs in LDS
-  p.attn_pool = o.attn_pool > 0 || (o.attn_pool == 0 && B > 1 && (int64_t)B * nkv * p.S > n_workers);
+  // (the scheduled executor dispatches tasks one by one: no claimed pool, no
+  // split-K tiles that wait for their siblings, every edge a counter event)
+  const bool sched = o.executor == MK_EXEC_SCHEDULED;
+  p.attn_pool = !sched && (o.attn_pool > 0 ||
+                           (o.attn_pool == 0 && B > 1 && (int64_t)B * nkv * p.S > n_workers));
   if (p.attn_pool && (int64_t)B * nkv * p.S > 0x7fff) {
     err = "too many attention tasks per layer for a claimed pool";
     return MK_ERR_UNSUPPORTED;
@@ -381,7 +385,7 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   {
     const bool rows16 = H % 16 == 0 && (nq * hd) % 16 == 0 && hd % 16 == 0 &&
                         c.vocab % 16 == 0 && (moe ? c.n_experts % 16 == 0 : c.ffn_dim % 16 == 0);
-    p.mfma = o.batched_mfma >= 0 && B >= 16 && B <= kMfmaMaxBatch && rows16;
+    p.mfma = !sched && o.batched_mfma >= 0 && B >= 16 && B <= kMfmaMaxBatch && rows16;
   }
   // single slot: GEMV passes extend into the LDS above the staged
   // activations when the longest staged row leaves that space free.  Auto
@@ -665,7 +669,7 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   // Data edges: the reader checks the tags of the vector it stages instead of
   // waiting for the counter, and the writers do not signal.  (Matrix-core
   // batches stage their activations in slices, so they keep the counters.)
-  if (!p.mfma) {
+  if (!p.mfma && !sched) {
     std::vector<char> is_data(p.ev_thr.size(), 0);
     for (int e : data_ev) is_data[e] = 1;
     for (auto &t : p.tasks) {

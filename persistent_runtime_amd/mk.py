@@ -24,6 +24,7 @@ MK_ERR_TIMEOUT = -6
 MK_ERR_UNSUPPORTED = -7
 MK_EXEC_PERSISTENT = 0
 MK_EXEC_KERNEL_PER_OP = 1
+MK_EXEC_SCHEDULED = 2
 
 OPS = {1: "EMBED", 2: "QKV", 3: "ATTN", 4: "MERGE", 5: "OPROJ", 6: "GATEUP",
        7: "DOWN", 8: "ROUTER", 9: "TOPK", 10: "EGATEUP", 11: "EDOWN",
