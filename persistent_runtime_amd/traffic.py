@@ -53,17 +53,20 @@ def main():
     ap.add_argument("--calib-bytes", type=float, required=True,
                     help="bytes one copy dispatch reads (= bytes it writes)")
     ap.add_argument("--out", required=True)
+    ap.add_argument("--kernel", default=KERNEL + "<1>",
+                    help="kernel name substring (the single-slot variant by default; "
+                         "prompt chunks run another variant)")
     ap.add_argument("--command", action="append", default=[],
                     help="profiling command lines to record")
     a = ap.parse_args()
-    fk = statistics.median(_values(a.fetch, "FETCH_SIZE", KERNEL))
-    wk = statistics.median(_values(a.write, "WRITE_SIZE", KERNEL))
+    fk = statistics.median(_values(a.fetch, "FETCH_SIZE", a.kernel))
+    wk = statistics.median(_values(a.write, "WRITE_SIZE", a.kernel))
     cf = statistics.median(_values(a.calib_fetch, "FETCH_SIZE", COPY))
     cw = statistics.median(_values(a.calib_write, "WRITE_SIZE", COPY))
     sf = a.calib_bytes / (cf * 1024.0)   # bytes per counted KiB
     sw = a.calib_bytes / (cw * 1024.0)
     rec = {
-        "kernel": KERNEL, "kernel_source_hash": kernel_source_hash(),
+        "kernel": a.kernel, "kernel_source_hash": kernel_source_hash(),
         "fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
         "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_bytes": a.calib_bytes,
         "fetch_scale": sf, "write_scale": sw,
