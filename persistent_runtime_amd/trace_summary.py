@@ -40,12 +40,19 @@ def main():
     from persistent_runtime_amd.kvcache import PagedKV
 
     ap = argparse.ArgumentParser()
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "moe30b", "llama70b"])
+    ap.add_argument("--workload", default="llama8b",
+                    choices=["llama8b", "moe30b", "llama70b", "ragged"])
+    ap.add_argument("--batch", type=int, default=64,
+                    help="ragged: slots (8B shape, contexts U[128, 16384])")
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--layer", type=int, default=None, help="layer of the critical-path table")
+    ap.add_argument("--save", default=None, help="also write the raw trace and task table (.npz)")
+    ap.add_argument("--steps", type=int, default=1, help="traced steps (tables use the last)")
     a = ap.parse_args()
-    model = synth.MODELS[a.workload]
     dev = torch.device("cuda:0")
+    if a.workload == "ragged":
+        return ragged(a, dev)
+    model = synth.MODELS[a.workload]
     ctx0 = 8192 if a.workload == "moe30b" else 39
     total = ctx0 + a.warmup + 2
     maxp = (total + 15) // 16
@@ -67,11 +74,65 @@ def main():
         pos[0] = ctx0 + i
         plan.decode_step(tok, pos, tok)
     plan.check()
-    tr = plan.read_trace().astype(np.int64)
+    traces = [plan.read_trace().astype(np.int64)]
+    for i in range(1, a.steps):
+        pos[0] = ctx0 + a.warmup + i
+        plan.decode_step(tok, pos, tok)
+        plan.check()
+        traces.append(plan.read_trace().astype(np.int64))
+    tr = traces[-1]
     tasks, _ = mk.inspect_plan(plan.cfg, mk.default_options(
         debug_trace=2, planned_ctx=total, n_cus=plan.info()["n_cus"]))
     plan.free()
-    summarize(model, tasks, tr, ctx0 + a.warmup, a.layer, " ".join(sys.argv))
+    if a.save:
+        np.savez_compressed(a.save, traces=np.stack(traces),
+                            op=np.array([t.op for t in tasks]),
+                            layer=np.array([t.layer for t in tasks]),
+                            worker=np.array([t.worker for t in tasks]),
+                            nbytes=np.array([t.bytes for t in tasks]))
+    summarize(dict(model, name=f"{model['name']}, batch 1"), tasks, tr, ctx0 + a.warmup, a.layer,
+              " ".join(sys.argv))
+
+
+def ragged(a, dev):
+    """The 8B shape with `a.batch` slots of synthetic cached contexts uniform in
+    [128, 16384] (the continuous-batching workload), one traced step."""
+    import torch
+
+    import synth
+    from persistent_runtime_amd import mk
+    from persistent_runtime_amd.kvcache import PagedKV
+    model = synth.MODELS["llama8b"]
+    B = a.batch
+    sched = synth.ragged_schedule(B, 1)
+    ctx = sched["ctx0"]
+    Wd = synth.make_weights(model, device=dev)
+    maxp = (16384 + a.warmup + 2 + 15) // 16
+    kv = PagedKV(model, max_batch=B, max_pages_per_seq=maxp,
+                 n_pages=sum((c + a.warmup + 2 + 15) // 16 for c in ctx) + B, device=dev)
+    for b in range(B):
+        K, V = synth.make_kv_values(model, ctx[b], stream_id=sched["sid0"][b], device=dev)
+        kv.write_tokens(b, K, V)
+        kv.assign(b, ctx[b] + a.warmup + 2)
+        del K, V
+    opts = dict(debug_trace=2, planned_ctx=16384)
+    plan = mk.Plan(model, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=B,
+                   opts=mk.default_options(**opts))
+    tok = torch.as_tensor(synth.make_prompt(B, model["vocab"], seed=7), dtype=torch.int32).to(dev)
+    for i in range(a.warmup + 1):
+        pos = torch.as_tensor([c + i for c in ctx], dtype=torch.int32).to(dev)
+        plan.decode_step(tok, pos, tok)
+    plan.check()
+    tr = plan.read_trace().astype(np.int64)
+    tasks, _ = mk.inspect_plan(plan.cfg, mk.default_options(n_cus=plan.info()["n_cus"], **opts))
+    plan.free()
+    if a.save:
+        np.savez_compressed(a.save, traces=tr[None], op=np.array([t.op for t in tasks]),
+                            layer=np.array([t.layer for t in tasks]),
+                            worker=np.array([t.worker for t in tasks]),
+                            nbytes=np.array([t.bytes for t in tasks]))
+    summarize(dict(model, name=f"llama8b ragged, {B} slots"), tasks, tr, max(ctx) + a.warmup,
+              a.layer, " ".join(sys.argv))
 
 
 def summarize(model, tasks, tr, pos, layer, cmd):
@@ -91,7 +152,7 @@ def summarize(model, tasks, tr, pos, layer, cmd):
         prev[w] = t_out[i]
     ops = [mk_op(t) for t in tasks]
     L = model["n_layers"]
-    print(f"# Decode-step timing: {model['name']}, batch 1, position {pos}\n")
+    print(f"# Decode-step timing: {model['name']}, position {pos}\n")
     print(f"Command: `{cmd}`\n")
     print(f"Step (first inputs-complete to last finish): {step * TICK_US:.1f} us; "
           f"{T} tasks on {len(set(wk.tolist()))} workers.\n")
@@ -117,6 +178,20 @@ def summarize(model, tasks, tr, pos, layer, cmd):
         gap = "" if last is None else f"{(s0 - last) * TICK_US:.2f}"
         print(f"| {op} | {s0 * TICK_US:.1f} | {s1 * TICK_US:.1f} | {(s1 - s0) * TICK_US:.2f} | {gap} |")
         last = s1
+    print(f"\n## Spread within each operation of layer {l} (us from the layer's first "
+          f"inputs-complete)\n")
+    print("| op | inputs complete p0 / p50 / p100 | finish p0 / p50 / p100 | run min / p50 / max |")
+    print("|---|---|---|---|")
+    first = None
+    for op in dict.fromkeys(ops[i] for i in range(T) if tasks[i].layer == l):
+        idx = [i for i in range(T) if tasks[i].layer == l and ops[i] == op]
+        if first is None:
+            first = int(t_in[idx].min())
+        a = (t_in[idx] - first) * TICK_US
+        f = (t_out[idx] - first) * TICK_US
+        r = (t_out[idx] - t_in[idx]) * TICK_US
+        q = lambda x: " / ".join(f"{v:.1f}" for v in np.percentile(x, [0, 50, 100]))
+        print(f"| {op} | {q(a)} | {q(f)} | {q(r)} |")
     per_layer = []
     for ll in range(L):
         idx = [i for i in range(T) if tasks[i].layer == ll]
