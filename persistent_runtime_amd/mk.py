@@ -193,7 +193,9 @@ class Plan:
 
     `W` is the synth weight dictionary (bf16 tensors on the device, per-layer
     tensors stacked on axis 0); `k_pool`, `v_pool` bf16
-    [L, n_pages, nkv, 16, hd]; `page_table` int32 [max_batch, max_pages].
+    [L, n_pages, nkv, 16, hd] and [L, n_pages, nkv, hd, 16] (values transposed
+    within a page, as include/mk.h states); `page_table` int32
+    [max_batch, max_pages].
     The Plan keeps references to all of them.
     """
 
