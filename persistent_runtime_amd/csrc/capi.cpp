@@ -478,8 +478,13 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
     const int64_t n_kpart = hp.n_kpart * kpart_slot(B);
-    const int64_t nf = 2 * (hp.n_x + hp.n_xmid + hp.n_attn + hp.n_h + hp.n_q + 2 * hp.n_k + hp.n_rl) +
-                       hp.n_part + hp.n_tk + hp.n_he + hp.n_amax + n_kpart;
+    // matrix-core plans: the values-only copy of the tagged vectors (x
+    // through rl), half their span, placed first so every buffer after it
+    // keeps the base's alignment
+    const int64_t n_tagged =
+        2 * (hp.n_x + hp.n_xmid + hp.n_q + 2 * hp.n_k + hp.n_attn + hp.n_h + hp.n_rl) + hp.n_part;
+    const int64_t n_shadow = hp.mfma ? (n_tagged / 2 + 63) / 64 * 64 : 0;
+    const int64_t nf = n_shadow + n_tagged + hp.n_tk + hp.n_he + hp.n_amax + n_kpart;
     float *fs;
     if ((rc = p->alloc(&fs, (size_t)nf, "activation scratch"))) return rc;
     int32_t *is;
@@ -556,6 +561,7 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     d.page_table = kv->page_table;
     float *f = fs;
     auto take = [&](int64_t n) { float *r = n ? f : nullptr; f += n; return r; };
+    d.shadow = take(n_shadow);
     d.x = take(2 * hp.n_x); d.xmid = take(2 * hp.n_xmid); d.q = take(2 * hp.n_q);
     d.k = take(2 * hp.n_k); d.v = take(2 * hp.n_k); d.part = take(hp.n_part);
     d.attn = take(2 * hp.n_attn);
@@ -563,6 +569,7 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     d.rl = take(2 * hp.n_rl); d.tk_w = take(hp.n_tk); d.he = take(hp.n_he);
     d.amax_v = take(hp.n_amax);
     d.kpart = take(n_kpart);
+    d.pair0 = d.shadow ? d.x : nullptr;
     d.tk_ids = hp.n_tk ? is : nullptr;
     d.amax_i = is + hp.n_tk;
     p->stage_tok = is + hp.n_tk + hp.n_amax;

@@ -160,6 +160,16 @@ DEV void stt(float *pairs, size_t i, float v, uint32_t tag) {
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 DEV float ldv(const float *pairs, size_t i) { return lda(pairs + 2 * i); }
+// The values-only copy of a tagged vector (matrix-core plans; see DevPlan).
+DEV const float *shadow_of(CP &d, const float *pairs) {
+  return d.shadow + (pairs - d.pair0) / 2;
+}
+// stt, plus the value into the copy when the plan keeps one: for the
+// vectors matrix-core tiles read (x, x_mid, attention output, h)
+DEV void stv(CP &d, float *pairs, size_t i, float v, uint32_t tag) {
+  stt(pairs, i, v, tag);
+  if (d.shadow) sta(const_cast<float *>(shadow_of(d, pairs)) + i, v);
+}
 constexpr int kCpolSc1 = 16;  // cache-policy bit: device-scope coherent
 DEV __amdgpu_buffer_rsrc_t rsrc(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
@@ -979,10 +989,10 @@ DEV void gemv_epilogue(CP &d, const CallArgs &ca, const TD &t, const float *rsum
     const size_t e = (size_t)(b0 + bi) * os + i;  // output element (slot b0+bi, row i)
     switch (op) {
       case OP_OPROJ: case OP_DOWN:  // residual add (first outputs: preloaded); tagged
-        stt(t.dst, e, (idx < 64 ? aux0 : ldv(t.aux, e)) + y, ca.tag);
+        stv(d, t.dst, e, (idx < 64 ? aux0 : ldv(t.aux, e)) + y, ca.tag);
         break;
       case OP_GATEUP:  // SwiGLU of the gate and up rows; tagged
-        stt(t.dst, e, silu(y) * at(bi, i, 1), ca.tag);
+        stv(d, t.dst, e, silu(y) * at(bi, i, 1), ca.tag);
         break;
       case OP_EGATEUP:
         sta(t.dst + e, silu(y) * at(bi, i, 1));
@@ -1244,7 +1254,7 @@ DEV bool down_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
     trace_start(d, t);
     if (persistent) trace_finish(d, t);
-    for (int i = lane; i < t.a2; i += 64) stt(t.dst, i, 0.f, ca.tag);
+    for (int i = lane; i < t.a2; i += 64) stv(d, t.dst, i, 0.f, ca.tag);
   } else {
     int id;
     float w;
@@ -1263,7 +1273,7 @@ DEV bool down_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     for (int i = lane; i < t.a2; i += 64) {
       float acc = 0.f;
       for (int j = 0; j < d.topk; ++j) acc = fmaf(lanef(w, j), rsum[j * t.a2 + i], acc);
-      stt(t.dst, i, (i < 64 ? aux0 : ldv(t.aux, i)) + acc, ca.tag);
+      stv(d, t.dst, i, (i < 64 ? aux0 : ldv(t.aux, i)) + acc, ca.tag);
     }
   }
   if (persistent) {
@@ -1336,9 +1346,12 @@ DEV bool down_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
 // slice of activations (all slots) into LDS in the B layout (lane l: slot
 // l%16 of a 16-slot tile, the same 8 columns), split into a bf16 value and
 // a bf16 remainder: two products per tile keep about 16 bits of the fp32
-// activation.  Slices are double-buffered, one barrier per pass.  With a
-// gain the staged values are x*g and the outputs are scaled by 1/rms of
-// their slot at the end; the sums of squares are accumulated while staging.
+// activation.  It copies the slice from the plan's values-only copy of the
+// input with LDS-DMA (no registers, so a whole slice is in flight at once)
+// and converts it in place.  Slices are double-buffered, one barrier per
+// pass, each slice's copy issued a pass ahead.  With a gain the staged
+// values are x*g and the outputs are scaled by 1/rms of their slot at the
+// end; the sums of squares are accumulated while converting.
 // The accumulators (16 rows x 16 slots per tile) go to LDS after the last
 // pass and the control wave writes the outputs.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1413,12 +1426,10 @@ DEV void mload(const MGeo &g, Buf &w, int cw) {
 // One pass of wave cw: the products of its chunks with the staged slice
 // `xb`; each register slot is refilled right after use with the same chunk
 // of the next pass, or (after the last pass) of the next task's first pass.
-template <int NKB>
+template <int NKB, int B16>
 DEV void mpass(const MGeo &g, Buf &w, f32x4 (&acc)[2][4], const char *xb, int cw, int p,
                bool pre, const MGeo &gn) {
   const int lane = tidx() & 63;
-  const int B16 = g.B16;
-  const char *xlo = xb + g.nkb * B16 * 1024;
   const bool last = p + 1 == g.P;
 #pragma unroll
   for (int j = 0; j < kMaxChunks; ++j) {
@@ -1432,11 +1443,11 @@ DEV void mpass(const MGeo &g, Buf &w, f32x4 (&acc)[2][4], const char *xb, int cw
       // products accumulate into different tiles
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const char *src = half ? xlo : xb;
         bf16x8 xv[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st)
-          if (st < B16) xv[st] = *(const bf16x8 *)(src + ((kb * B16 + st) * 64 + lane) * 16);
+          if (st < B16)
+            xv[st] = *(const bf16x8 *)(xb + (kb * B16 + st) * 2048 + half * 1024 + lane * 16);
 #pragma unroll
         for (int st = 0; st < 4; ++st)
           if (st < B16)
@@ -1451,83 +1462,82 @@ DEV void mpass(const MGeo &g, Buf &w, f32x4 (&acc)[2][4], const char *xb, int cw
 }
 
 // Staging of slice p of the activations (all slots) into LDS buffer pb.  A
-// unit is 64 lanes x 8 columns of one slot (lane l: slot st*16 + l%16,
-// columns 8(l/16)..+8 of k-block kb), times the gain, stored as bf16 value +
-// bf16 remainder in the B layout.  Every load is issued (units beyond the
-// slice read unit 0 and are not stored), which keeps the compiler's waits
-// per load instead of for the whole queue.
-template <int NQ> struct XStage {
-  uint32_t v[NQ][8];   // the 8 values of a unit (their tags are not read)
-  u32x4 g[NQ];
-};
+// unit is one 16-slot tile (st) of one 32-column k-block (kb) in 2 KiB.  The
+// copy puts the fp32 values there, lane l's 32 bytes at l*32: slot
+// st*16 + l%16, columns 8(l/16)..+8 of the k-block; the conversion rewrites
+// the unit as 64 x 16 bytes of bf16 values of x*gain (lane l at l*16, the B
+// layout) followed by 64 x 16 bytes of their bf16 remainders.
 DEV int mx_units(const MGeo &g, int p) { return (min(g.Ks, g.K - p * g.Ks) >> 5) * g.B16; }
-// Units u0 .. u0+NQ-1 of slice p.
-template <int NQ>
-DEV void mx_load(CP &d, const MGeo &g, const TD &t, int p, int u0, XStage<NQ> &xs) {
-  const int lane = tidx() & 63;
-  const int nu = mx_units(g, p), B = d.B;
-  const __amdgpu_buffer_rsrc_t r = rsrc(t.src);
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    int u = u0 + q;
-    u = u < nu ? u : 0;
-    const int kb = u / g.B16, st = u - kb * g.B16;
-    const int col = g.k0 + p * g.Ks + kb * 32 + 8 * (lane >> 4);
-    int b = st * 16 + (lane & 15);
-    b = b < B ? b : 0;
-    xs.g[q] = t.gain ? ldg((const u32x4 *)(t.gain + col))
-                     : (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-    const uint32_t off = (uint32_t)(((size_t)b * g.ld + col) * 8);
-    // cached loads of the values alone: the task's dependency wait ended
-    // with an agent-scope acquire (persistent) or the launch boundary did
-    // (kernel-per-op), and matrix-core plans do not check tags
-#pragma unroll
-    for (int e = 0; e < 8; ++e) xs.v[q][e] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 8 * e, 0, 0);
-  }
+DEV uint32_t mx_buf(const Smem &sm, const MGeo &g, int pb) {
+  return (uint32_t)(uintptr_t)sm.xs + (uint32_t)(pb * (g.nkb * g.B16 * 2048));
 }
-template <int NQ>
-DEV void mx_store(Smem &sm, CP &d, const MGeo &g, int p, int pb, int u0, const XStage<NQ> &xs,
-                  float (&ssl)[4]) {
-  const int lane = tidx() & 63;
-  const int nu = mx_units(g, p), B16 = g.B16;
-  char *xb = (char *)sm.xs + pb * (g.nkb * B16 * 2048);
-  char *xlo = xb + g.nkb * B16 * 1024;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int u = u0 + q;
-    if (u >= nu) break;
-    const int kb = u / B16, st = u - kb * B16;
-    const bool live = st * 16 + (lane & 15) < d.B;
-    const u32x4 gq = xs.g[q];
-    const f32x8 gf = {bf_lo(gq.x), bf_hi(gq.x), bf_lo(gq.y), bf_hi(gq.y),
-                      bf_lo(gq.z), bf_hi(gq.z), bf_lo(gq.w), bf_hi(gq.w)};
-    f32x8 x = {__uint_as_float(xs.v[q][0]), __uint_as_float(xs.v[q][1]),
-               __uint_as_float(xs.v[q][2]), __uint_as_float(xs.v[q][3]),
-               __uint_as_float(xs.v[q][4]), __uint_as_float(xs.v[q][5]),
-               __uint_as_float(xs.v[q][6]), __uint_as_float(xs.v[q][7])};
-    x = live ? x : (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-      if (s2 == st) ssl[s2] += ss;
-    const f32x8 v = x * gf;
-    const bf16x8 h = __builtin_convertvector(v, bf16x8);
-    const bf16x8 lo = __builtin_convertvector(v - __builtin_convertvector(h, f32x8), bf16x8);
-    const int o = ((kb * B16 + st) * 64 + lane) * 16;
-    *(bf16x8 *)(xb + o) = h;
-    *(bf16x8 *)(xlo + o) = lo;
-  }
-}
-// Control wave: the whole slice, eight units per round.  The compute waves
-// never wait for these loads: their queues hold weight loads only.
-DEV void mx_stage(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb, float (&ssl)[4]) {
+// Control wave: the LDS-DMA copies of slice p, two 16-byte copies per lane
+// and unit (copy i, lane j: bytes 16j.. of the unit's half i, i.e. half j%2
+// of value lane 32i + j/2).  Lanes of slots beyond the batch copy nothing;
+// the conversion zeroes those slots.  Nothing waits here: mx_convert does.
+DEV void mx_dma(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb) {
+  const int lane = tidx() & 63, B16 = g.B16;
   const int nu = mx_units(g, p);
-  for (int u0 = 0; u0 < nu; u0 += 8) {
-    XStage<8> xs;
-    mx_load<8>(d, g, t, p, u0, xs);
-    mx_store<8>(sm, d, g, p, pb, u0, xs, ssl);
+  const float *src = shadow_of(d, t.src);
+  const uint32_t xb = mx_buf(sm, g, pb);
+  for (int u = 0; u < nu; ++u) {
+    const int kb = u / B16, st = u - kb * B16;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int L = 32 * i + (lane >> 1);
+      const int b = st * 16 + (L & 15);
+      const int col = g.k0 + p * g.Ks + kb * 32 + 8 * (L >> 4) + 4 * (lane & 1);
+      if (b < d.B)
+        dma16((uint64_t)(src + (size_t)b * g.ld + col), xb + (uint32_t)(u * 2048 + i * 1024));
+    }
+  }
+}
+// Control wave: wait for this wave's copies (all of them: the next slice's
+// are issued after this), then convert slice p in place, unit by unit: each
+// lane reads its 32 bytes, and only then (the same wave, in order) writes
+// its 16 + 16 bytes of the unit.  The gains of eight k-blocks are loaded
+// together, ahead of the wait.
+DEV void mx_convert(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb,
+                    float (&ssl)[4]) {
+  const int lane = tidx() & 63, B16 = g.B16;
+  const int nkb = mx_units(g, p) / B16;
+  char *xb = (char *)sm.xs + pb * (g.nkb * B16 * 2048);
+  const bool live[4] = {lane % 16 < d.B, 16 + lane % 16 < d.B, 32 + lane % 16 < d.B,
+                        48 + lane % 16 < d.B};
+  for (int k0 = 0; k0 < nkb; k0 += 8) {
+    u32x4 gq[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = g.k0 + p * g.Ks + (k0 + j) * 32 + 8 * (lane >> 4);
+      gq[j] = (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+      if (t.gain && k0 + j < nkb) gq[j] = ldg((const u32x4 *)(t.gain + col));
+    }
+    if (k0 == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (k0 + j >= nkb) break;
+      const u32x4 gv = gq[j];
+      const f32x8 gf = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y),
+                        bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (st >= B16) break;
+        char *ub = xb + ((k0 + j) * B16 + st) * 2048;
+        const f32x4 a0 = *(const f32x4 *)(ub + lane * 32);
+        const f32x4 a1 = *(const f32x4 *)(ub + lane * 32 + 16);
+        f32x8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        x = live[st] ? x : (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+        ssl[st] += ss;
+        const f32x8 v = x * gf;
+        const bf16x8 h = __builtin_convertvector(v, bf16x8);
+        const bf16x8 lo = __builtin_convertvector(v - __builtin_convertvector(h, f32x8), bf16x8);
+        *(bf16x8 *)(ub + lane * 16) = h;
+        *(bf16x8 *)(ub + 1024 + lane * 16) = lo;
+      }
+    }
   }
 }
 // Every wave's sums of squares to LDS (sm.red as [wave][lane][tile]); after
@@ -1598,11 +1608,11 @@ DEV void mepilogue(CP &d, const CallArgs &ca, const TD &t, int R, int Bp, int r0
       const float y = y_at(i, b);
       const size_t e = (size_t)b * os + r0 + i;
       if (op == OP_GATEUP)
-        stt(t.dst, e, silu(y) * y_at(R + i, b), ca.tag);
-      else if (op == OP_OPROJ || op == OP_DOWN || op == OP_QKV)
-        stt(t.dst, e, a[u] + y, ca.tag);  // QKV adds zero
+        stv(d, t.dst, e, silu(y) * y_at(R + i, b), ca.tag);
+      else if (op == OP_OPROJ || op == OP_DOWN)
+        stv(d, t.dst, e, a[u] + y, ca.tag);
       else
-        stt(t.dst, e, y, ca.tag);  // ROUTER
+        stt(t.dst, e, y, ca.tag);  // QKV, ROUTER
     }
   }
 }
@@ -1729,12 +1739,15 @@ DEV bool gemv_mfma_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
   trace_start(d, t);
   const MGeo g = mgeo_of(d, t);
   float ssl[4] = {0.f, 0.f, 0.f, 0.f};
-  mx_stage(sm, d, g, t, 0, 0, ssl);
+  mx_dma(sm, d, g, t, 0, 0);
+  mx_convert(sm, d, g, t, 0, 0, ssl);
+  if (g.P > 1) mx_dma(sm, d, g, t, 1, 1);
   trace_mark(d, t, 0);
   __syncthreads();  // slice 0 staged
   for (int p = 0; p < g.P; ++p) {
-    if (p + 1 < g.P) mx_stage(sm, d, g, t, p + 1, (p + 1) & 1, ssl);
+    if (p + 1 < g.P) mx_convert(sm, d, g, t, p + 1, (p + 1) & 1, ssl);
     __syncthreads();  // pass p done, slice p + 1 staged
+    if (p + 2 < g.P) mx_dma(sm, d, g, t, p + 2, p & 1);  // into the buffer pass p read
   }
   mss_publish(sm, ssl);
   __syncthreads();  // accumulators and sums of squares in LDS
@@ -1784,10 +1797,22 @@ DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
   __syncthreads();  // slice 0 staged
   for (int p = 0; p < g.P; ++p) {
     const char *xb = (const char *)sm.xs + (p & 1) * (g.nkb * g.B16 * 2048);
-    if (g.nkb >= 16)
-      mpass<16>(g, w, acc, xb, cw, p, pre, gn);
-    else
-      mpass<8>(g, w, acc, xb, cw, p, pre, gn);
+    // the slot-tile count as a constant: no branch around any product
+    if (g.nkb >= 16) {
+      switch (g.B16) {
+        case 1: mpass<16, 1>(g, w, acc, xb, cw, p, pre, gn); break;
+        case 2: mpass<16, 2>(g, w, acc, xb, cw, p, pre, gn); break;
+        case 3: mpass<16, 3>(g, w, acc, xb, cw, p, pre, gn); break;
+        default: mpass<16, 4>(g, w, acc, xb, cw, p, pre, gn); break;
+      }
+    } else {
+      switch (g.B16) {
+        case 1: mpass<8, 1>(g, w, acc, xb, cw, p, pre, gn); break;
+        case 2: mpass<8, 2>(g, w, acc, xb, cw, p, pre, gn); break;
+        case 3: mpass<8, 3>(g, w, acc, xb, cw, p, pre, gn); break;
+        default: mpass<8, 4>(g, w, acc, xb, cw, p, pre, gn); break;
+      }
+    }
     __syncthreads();  // pass p done, slice p + 1 staged (by the control wave)
   }
   mss_publish(sm, ssl);
@@ -1929,7 +1954,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     for (int idx = tid; idx < G * HD; idx += kThreads) {
       const int h = idx / HD, dd = idx - h * HD;
       if (S == 1) {
-        stt(d.attn, (head0 + h) * HD + dd, 0.f, ca.tag);
+        stv(d, d.attn, (head0 + h) * HD + dd, 0.f, ca.tag);
       } else {
         float *pp = d.part + ((head0 + h) * S + sp) * PS;
         sta(pp + dd, 0.f);
@@ -2165,7 +2190,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
       }
     }
     if (S == 1) {
-      stt(d.attn, (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f, ca.tag);
+      stv(d, d.attn, (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f, ca.tag);
     } else {
       float *pp = d.part + ((head0 + h) * S + sp) * PS;
       sta(pp + dd, Os);
@@ -2280,10 +2305,10 @@ DEV void run_merge(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
     for (int q = 1; q < nsub; ++q) sum += red[q * nvec + vv];
     const int hh = vv / hv, d0 = (vv - hh * hv) * 4;
     const size_t e = (head0 + hh) * HD + d0;
-    stt(d.attn, e + 0, sum.x, ca.tag);
-    stt(d.attn, e + 1, sum.y, ca.tag);
-    stt(d.attn, e + 2, sum.z, ca.tag);
-    stt(d.attn, e + 3, sum.w, ca.tag);
+    stv(d, d.attn, e + 0, sum.x, ca.tag);
+    stv(d, d.attn, e + 1, sum.y, ca.tag);
+    stv(d, d.attn, e + 2, sum.z, ca.tag);
+    stv(d, d.attn, e + 3, sum.w, ca.tag);
   }
 }
 
@@ -2298,7 +2323,7 @@ DEV void run_embed(CP &d, const CallArgs &ca, const TD &t) {
     set_error(d, DEVERR_BAD_INPUT, tix, -3, (uint32_t)tok, (uint32_t)d.V);
   const uint16_t *e = d.embed + (size_t)(ok ? tok : 0) * H;
   for (int i = tidx(); i < H; i += kThreads)
-    stt(d.x, (size_t)b * H + i, ok ? bf1(ldg(e + i)) : 0.f, ca.tag);
+    stv(d, d.x, (size_t)b * H + i, ok ? bf1(ldg(e + i)) : 0.f, ca.tag);
 }
 
 // Softmax router top-k: k rounds of (max, lowest index) over the logits not

@@ -139,6 +139,11 @@ struct DevPlan {
   // scratch (fp32 unless noted); layouts in planner.cpp
   float *x, *xmid, *q, *k, *v, *part, *attn, *h;   // all but part: tagged pairs
   float *rl;                                        // router logits: tagged pairs
+  // matrix-core plans: an fp32 copy (values only) of every tagged vector
+  // that matrix-core tiles read; element i of the pairs at p lives at
+  // shadow[(p + 2i - pair0) / 2] (null in other plans)
+  const float *pair0;
+  float *shadow;
   float *tk_w, *he, *amax_v;
   int32_t *tk_ids, *amax_i;
   const float *rope_cos, *rope_sin;                     // [max_pos][hd/2]

@@ -32,6 +32,10 @@ sys.path.insert(0, os.path.dirname(HERE))
 TICK_US = 0.01  # 100 MHz
 
 
+def _command():
+    return "python -m persistent_runtime_amd.trace_summary " + " ".join(sys.argv[1:])
+
+
 def main():
     import torch
 
@@ -91,7 +95,7 @@ def main():
                             worker=np.array([t.worker for t in tasks]),
                             nbytes=np.array([t.bytes for t in tasks]))
     summarize(dict(model, name=f"{model['name']}, batch 1"), tasks, tr, ctx0 + a.warmup, a.layer,
-              " ".join(sys.argv))
+              _command())
 
 
 def ragged(a, dev):
@@ -132,7 +136,7 @@ def ragged(a, dev):
                             worker=np.array([t.worker for t in tasks]),
                             nbytes=np.array([t.bytes for t in tasks]))
     summarize(dict(model, name=f"llama8b ragged, {B} slots"), tasks, tr, max(ctx) + a.warmup,
-              a.layer, " ".join(sys.argv))
+              a.layer, _command())
 
 
 def summarize(model, tasks, tr, pos, layer, cmd):
