@@ -1497,8 +1497,9 @@ DEV void mx_dma(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb) {
 // lane reads its 32 bytes, and only then (the same wave, in order) writes
 // its 16 + 16 bytes of the unit.  The gains of eight k-blocks are loaded
 // together, ahead of the wait.
-DEV void mx_convert(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb,
-                    float (&ssl)[4]) {
+template <bool GAIN, bool RAGGED>
+DEV void mx_convert_t(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb,
+                      float (&ssl)[4]) {
   const int lane = tidx() & 63, B16 = g.B16;
   const int nkb = mx_units(g, p) / B16;
   char *xb = (char *)sm.xs + pb * (g.nkb * B16 * 2048);
@@ -1510,7 +1511,7 @@ DEV void mx_convert(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb,
     for (int j = 0; j < 8; ++j) {
       const int col = g.k0 + p * g.Ks + (k0 + j) * 32 + 8 * (lane >> 4);
       gq[j] = (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-      if (t.gain && k0 + j < nkb) gq[j] = ldg((const u32x4 *)(t.gain + col));
+      if (GAIN && k0 + j < nkb) gq[j] = ldg((const u32x4 *)(t.gain + col));
     }
     if (k0 == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
@@ -1526,18 +1527,40 @@ DEV void mx_convert(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb,
         const f32x4 a0 = *(const f32x4 *)(ub + lane * 32);
         const f32x4 a1 = *(const f32x4 *)(ub + lane * 32 + 16);
         f32x8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        x = live[st] ? x : (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float ss = 0.f;
+        if (RAGGED) x = live[st] ? x : (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        f32x8 v = x;
+        if (GAIN) {
+          float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-        ssl[st] += ss;
-        const f32x8 v = x * gf;
+          for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+          ssl[st] += ss;
+          v = x * gf;
+        }
+        // the bf16 values, widened back from their packed bits (low half of
+        // each word: even element), and the bf16 remainders
         const bf16x8 h = __builtin_convertvector(v, bf16x8);
-        const bf16x8 lo = __builtin_convertvector(v - __builtin_convertvector(h, f32x8), bf16x8);
+        const u32x4 hb = __builtin_bit_cast(u32x4, h);
+        const f32x8 hf = {__uint_as_float(hb.x << 16), __uint_as_float(hb.x & 0xffff0000u),
+                          __uint_as_float(hb.y << 16), __uint_as_float(hb.y & 0xffff0000u),
+                          __uint_as_float(hb.z << 16), __uint_as_float(hb.z & 0xffff0000u),
+                          __uint_as_float(hb.w << 16), __uint_as_float(hb.w & 0xffff0000u)};
+        const bf16x8 lo = __builtin_convertvector(v - hf, bf16x8);
         *(bf16x8 *)(ub + lane * 16) = h;
         *(bf16x8 *)(ub + 1024 + lane * 16) = lo;
       }
     }
+  }
+}
+// with or without a gain, with or without slots beyond the batch in a tile
+DEV void mx_convert(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb,
+                    float (&ssl)[4]) {
+  const bool ragged = g.B16 * 16 > d.B;
+  if (t.gain) {
+    if (ragged) mx_convert_t<true, true>(sm, d, g, t, p, pb, ssl);
+    else mx_convert_t<true, false>(sm, d, g, t, p, pb, ssl);
+  } else {
+    if (ragged) mx_convert_t<false, true>(sm, d, g, t, p, pb, ssl);
+    else mx_convert_t<false, false>(sm, d, g, t, p, pb, ssl);
   }
 }
 // Every wave's sums of squares to LDS (sm.red as [wave][lane][tile]); after
