@@ -205,6 +205,7 @@ def run_ragged(args, torch):
             f"({time.time() - t0:.1f}s)")
         opts = {} if args.attn_splits is None else {"attn_splits": args.attn_splits}
         opts["attn_order"] = args.attn_order
+        opts["batched_mfma"] = args.batched_mfma
 
         def run(plan, k0, k1, timed):
             tok = torch.as_tensor(synth.make_prompt(B, model["vocab"], seed=7 + k0),
@@ -270,6 +271,7 @@ def run_ragged(args, torch):
                                    f"16-token shuffled pages, retire/join p=1/32 per step",
                        "batch": B, "attn_splits": args.attn_splits,
                        "attn_order": args.attn_order,
+                       "batched_mfma": args.batched_mfma,
                        "tasks_per_step": info["n_tasks"]},
             "sol_fraction": round(achieved / 8000.0, 4),
             "bytes_per_step": int(sum(nbytes) / kk),
@@ -333,6 +335,8 @@ def main():
     ap.add_argument("--attn-splits", type=int, default=None,
                     help="KV splits per (sequence, KV head); default: the planner's choice")
     ap.add_argument("--kpo-steps", type=int, default=64, help="kernel-per-op comparison steps")
+    ap.add_argument("--batched-mfma", type=int, default=0, choices=(-1, 0, 1),
+                    help="ragged: GEMVs as matrix-core tiles (0 auto, 1 for any batch >= 2, -1 off)")
     ap.add_argument("--attn-order", type=int, default=0, choices=(-1, 0, 1),
                     help="ragged: claim order of pooled attention (0: the plan's default, "
                          "longest context first; -1: slot order)")

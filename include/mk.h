@@ -131,9 +131,10 @@ typedef struct {
                             HIP graph can be replayed; 0: counters stay
                             monotonic across steps (no clearing launch)       */
   int32_t batched_mfma;  /* static-weight GEMVs as bf16 matrix-core tiles for
-                            batches of 16..64 slots: 0 = auto (on when
-                            max_batch >= 16 and every row count is a multiple
-                            of 16), -1 = off (vector path)                   */
+                            batches of up to 64 slots: 0 = auto (on when
+                            max_batch >= 3 and every row count is a multiple
+                            of 16), 1 = on from 2 slots, -1 = off (vector
+                            path)                                            */
   int32_t attn_pool;     /* persistent executor: attention tasks of a layer are
                             claimed at run time from a shared counter by the
                             workers that reach them (balances sequences of

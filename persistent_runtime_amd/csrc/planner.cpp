@@ -385,7 +385,8 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   {
     const bool rows16 = H % 16 == 0 && (nq * hd) % 16 == 0 && hd % 16 == 0 &&
                         c.vocab % 16 == 0 && (moe ? c.n_experts % 16 == 0 : c.ffn_dim % 16 == 0);
-    p.mfma = !sched && o.batched_mfma >= 0 && B >= 16 && B <= kMfmaMaxBatch && rows16;
+    p.mfma = !sched && B <= kMfmaMaxBatch && rows16 &&
+             (o.batched_mfma > 0 ? B >= 2 : o.batched_mfma == 0 && B >= 3);
   }
   // single slot: GEMV passes extend into the LDS above the staged
   // activations when the longest staged row leaves that space free.  Auto

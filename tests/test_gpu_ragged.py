@@ -1,8 +1,8 @@
 """Continuous batching on the Llama-3-8B shape at full size: 4, 16 and 64
-slots (the vector multi-slot tiles, and the matrix-core tiles with split-K
-at 16 and 64) with seeded synthetic cached contexts uniform in [128, 16384]
-over shuffled 16-token pages, in the launch configuration the ragged
-benchmark times.
+slots (the matrix-core tiles with split-K, the default from three slots,
+and at 4 slots also the vector multi-slot tiles) with seeded synthetic
+cached contexts uniform in [128, 16384] over shuffled 16-token pages, in
+the launch configuration the ragged benchmark times.
 
 Three decode steps.  Before the second, one sequence retires and a new one
 (fresh context and KV) joins its slot; during the third, one slot is empty
@@ -42,8 +42,9 @@ def _host_kv(cfg, ctx, sid):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("B", [4, 16, 64])
-def test_llama8b_ragged_batch_join_retire(llama8b, B):
+@pytest.mark.parametrize("B,mfma", [(4, 0), (4, -1), (16, 0), (64, 0)],
+                         ids=["4", "4-vector", "16", "64"])
+def test_llama8b_ragged_batch_join_retire(llama8b, B, mfma):
     cfg = LLAMA8B
     Wd, Wt = llama8b
     sched = synth.ragged_schedule(B, 3)
@@ -64,7 +65,7 @@ def test_llama8b_ragged_batch_join_retire(llama8b, B):
             caches[b] = O.KVCache(cfg, K=list(Kh), V=list(Vh))
         del K, V
     plan = mk.Plan(cfg, Wd, kv.k_pool, kv.v_pool, kv.page_table, max_batch=B,
-                   opts=mk.default_options(planned_ctx=16384))
+                   opts=mk.default_options(planned_ctx=16384, batched_mfma=mfma))
     tok_d = torch.zeros(B, dtype=torch.int32, device="cuda")
     pos_d = torch.zeros(B, dtype=torch.int32, device="cuda")
     nxt_d = torch.zeros(B, dtype=torch.int32, device="cuda")

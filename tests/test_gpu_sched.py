@@ -46,12 +46,15 @@ def test_scheduled_tiny_teacher_forced(tiny, splits):
 
 
 def test_scheduled_equals_static_bitwise_batch(tiny):
-    """Three slots with split attention and an empty slot: the scheduled and
-    the static-queue executors give the same ids and logits bit for bit."""
+    """Three sequences with split attention and an empty slot: the scheduled
+    and the static-queue executors give the same ids and logits bit for bit
+    (both on the vector tiles: the scheduled executor has no matrix-core
+    tiles)."""
     Wd, _ = tiny
     out = []
     for ex in (mk.MK_EXEC_PERSISTENT, SCHED):
-        r = Runner(TINY, Wd, B=4, maxp=8, attn_splits=3, executor=ex, prefill_chunk=-1)
+        r = Runner(TINY, Wd, B=4, maxp=8, attn_splits=3, executor=ex, prefill_chunk=-1,
+                   batched_mfma=-1)
         for b in range(3):
             r.prefill(b, synth.make_prompt(20 + 5 * b, 1024).tolist())
         ids, lg = r.step([7, 8, 9, 0], [20, 25, 30, -1])

@@ -99,12 +99,15 @@ def test_tiny_free_running_greedy_matches(tiny):
     r.plan.free()
 
 
+@pytest.mark.parametrize("mfma", [0, -1], ids=["matrix_cores", "vector"])
 @pytest.mark.parametrize("pool", [-1, 1], ids=["static_attention", "claimed_attention"])
-def test_tiny_batch_with_empty_slot(tiny, pool):
+def test_tiny_batch_with_empty_slot(tiny, pool, mfma):
     """Three slots: two sequences of different lengths and one empty slot;
-    attention tasks placed statically or claimed at run time."""
+    attention tasks placed statically or claimed at run time; GEMVs as
+    matrix-core tiles (the default from three slots: one 16-slot tile, 13 of
+    its slots padding) or on the vector path."""
     Wd, Wt = tiny
-    r = Runner(TINY, Wd, B=3, maxp=8, attn_splits=2, attn_pool=pool)
+    r = Runner(TINY, Wd, B=3, maxp=8, attn_splits=2, attn_pool=pool, batched_mfma=mfma)
     pa, pb = _prompt(39), synth.make_prompt(21, 1024, seed=7).tolist()
     ca, cb = O.KVCache(TINY), O.KVCache(TINY)
     for p, t in enumerate(pa):
@@ -129,15 +132,18 @@ def test_tiny_batch_with_empty_slot(tiny, pool):
     r.plan.free()
 
 
+@pytest.mark.parametrize("mfma", [0, 1], ids=["vector", "matrix_cores"])
 @pytest.mark.parametrize("pool", [-1, 1], ids=["static_attention", "claimed_attention"])
-def test_trace_dependencies_and_run_once(tiny, pool):
+def test_trace_dependencies_and_run_once(tiny, pool, mfma):
     """Integer invariants of the persistent scheduler: every task ran exactly
     once and started only after every producer of its inputs finished (also
-    when the attention tasks are claimed from a shared counter)."""
+    when the attention tasks are claimed from a shared counter, and with the
+    matrix-core tiles, whose split-K siblings exchange partial products)."""
     Wd, _ = tiny
-    r = Runner(TINY, Wd, B=2, maxp=8, debug_trace=1, attn_splits=3, attn_pool=pool)
+    r = Runner(TINY, Wd, B=2, maxp=8, debug_trace=1, attn_splits=3, attn_pool=pool,
+               batched_mfma=mfma)
     tasks, thr = mk.inspect_plan(r.plan.cfg, mk.default_options(
-        n_cus=r.plan.info()["n_cus"], attn_splits=3, attn_pool=pool))
+        n_cus=r.plan.info()["n_cus"], attn_splits=3, attn_pool=pool, batched_mfma=mfma))
     sig = {}
     for i, t in enumerate(tasks):
         for k in range(t.n_sig):

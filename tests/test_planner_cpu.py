@@ -61,6 +61,15 @@ def _split_rows(t, ns, ks):
     return lo, min(t.a2, lo + rs)
 
 
+def _mfma(B, batched_mfma=0):
+    """Whether a plan's static-weight GEMVs are matrix-core tiles: from 3 slots
+    by default, from 2 on request, never beyond 64 (the models here have
+    every row count a multiple of 16)."""
+    if B > 64 or batched_mfma < 0:
+        return False
+    return B >= (2 if batched_mfma > 0 else 3)
+
+
 def _check_graph(model, tasks, thr, B, mfma=False):
     T = len(tasks)
     sig = {}
@@ -220,7 +229,7 @@ def _overlap(a, b):
 def _bruteforce_deps(model, B, S=None, **optkw):
     opts = mk.default_options(n_cus=optkw.pop("n_cus", 8), **optkw)
     tasks, thr = mk.inspect_plan(_cfg(model, B=B, maxp=8), opts)
-    mfma = B >= 16
+    mfma = _mfma(B, optkw.get("batched_mfma", 0))
     shared = optkw.get("shared_seqs", 0) > 0
     if shared:
         assert sum(1 for t in tasks if mk.OPS[t.op] == "KVAPP") == B * model["n_layers"]
@@ -254,9 +263,9 @@ def _bruteforce_deps(model, B, S=None, **optkw):
     return T, n_edges
 
 
-@pytest.mark.parametrize("B", [1, 3])
-def test_dependencies_match_region_overlap_tiny(B):
-    T, n = _bruteforce_deps(TINY, B)
+@pytest.mark.parametrize("B,mfma", [(1, 0), (3, 0), (3, -1), (2, 1)])
+def test_dependencies_match_region_overlap_tiny(B, mfma):
+    T, n = _bruteforce_deps(TINY, B, batched_mfma=mfma)
     assert T > 0 and n > 0
 
 
@@ -276,13 +285,13 @@ def test_dependencies_match_region_overlap_batched_split_k():
     assert n > 0
 
 
-@pytest.mark.parametrize("B", [3, 16])
-def test_dependencies_match_region_overlap_shared_sequences(B):
+@pytest.mark.parametrize("B,mfma", [(3, 0), (3, -1), (16, 0)])
+def test_dependencies_match_region_overlap_shared_sequences(B, mfma):
     """Shared-sequence plans (a prompt chunk's tokens in the slots): every
     attention task depends on the key/value stores of its own and every
-    earlier position of the chunk (vector path at 3 slots, matrix cores with
-    split attention at 16)."""
-    T, n = _bruteforce_deps(TINY, B, shared_seqs=1, attn_splits=2)
+    earlier position of the chunk (matrix cores at 3 and 16 slots, the vector
+    path at 3, split attention)."""
+    T, n = _bruteforce_deps(TINY, B, shared_seqs=1, attn_splits=2, batched_mfma=mfma)
     assert n > 0
 
 
@@ -298,7 +307,7 @@ def test_full_size_plans_are_valid(model):
     for B in (1, 4):
         opts = mk.default_options(n_cus=256)
         tasks, thr = mk.inspect_plan(_cfg(model, B=B, maxp=40), opts)
-        _check_graph(model, tasks, thr, B)
+        _check_graph(model, tasks, thr, B, mfma=_mfma(B))
         # weight bytes the tiles read = the model's per-step weight bytes
         wbytes = sum(t.bytes for t in tasks if mk.OPS[t.op] != "EMBED")
         assert wbytes > 0
@@ -419,7 +428,7 @@ def test_claimed_attention_annotations():
     for B in (16, 64):
         tasks, thr = mk.inspect_plan(_cfg(LLAMA8B, B=B, maxp=1024),
                                      mk.default_options(n_cus=256, planned_ctx=16384))
-        _check_graph(LLAMA8B, tasks, thr, B, mfma=B >= 16)
+        _check_graph(LLAMA8B, tasks, thr, B, mfma=_mfma(B))
         attn = [(i, t) for i, t in enumerate(tasks) if mk.OPS[t.op] == "ATTN"]
         assert len(attn) > 256, (B, len(attn))  # more tasks than workers: claimed
         by_layer = {}
@@ -445,7 +454,8 @@ def test_claimed_attention_annotations():
 def test_lds_weight_slots_only_where_the_stage_leaves_room():
     """Single-slot plans extend passes into LDS (up to 168 KiB) when every
     staged activation row fits 72 KiB; the 70B shape (28672-wide down
-    projection rows) and batches keep register-only passes (112 KiB)."""
+    projection rows) and batches on the vector path keep register-only passes
+    (112 KiB)."""
     from synth.configs import LLAMA70B
 
     def max_pass(model, B, **kw):
@@ -460,7 +470,7 @@ def test_lds_weight_slots_only_where_the_stage_leaves_room():
     assert 7 * 16 * 1024 < max_pass(LLAMA8B, 1) <= 7 * 24 * 1024
     assert max_pass(LLAMA8B, 1, weight_lds=-1) <= 7 * 16 * 1024
     assert max_pass(LLAMA70B, 1) <= 7 * 16 * 1024
-    assert max_pass(LLAMA8B, 4) <= 7 * 16 * 1024
+    assert max_pass(LLAMA8B, 4, batched_mfma=-1) <= 7 * 16 * 1024
     # MoE: off unless asked for
     assert max_pass(MOE30B, 1) <= 7 * 16 * 1024 < max_pass(MOE30B, 1, weight_lds=1)
 
