@@ -1492,19 +1492,47 @@ DEV void mx_dma(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb) {
     }
   }
 }
-// Control wave: wait for this wave's copies (all of them: the next slice's
-// are issued after this), then convert slice p in place, unit by unit: each
-// lane reads its 32 bytes, and only then (the same wave, in order) writes
-// its 16 + 16 bytes of the unit.  The gains of eight k-blocks are loaded
-// together, ahead of the wait.
+// One unit in place: lane's 32 bytes of fp32 values (zero for a slot
+// beyond the batch when `live` is false), times the gains gv (8 bf16), into
+// the unit's bf16 values and remainders; their sum of squares to ss.
+template <bool GAIN, bool RAGGED>
+DEV void mx_unit(char *ub, u32x4 gv, bool live, float &ss) {
+  const int lane = tidx() & 63;
+  const f32x4 a0 = *(const f32x4 *)(ub + lane * 32);
+  const f32x4 a1 = *(const f32x4 *)(ub + lane * 32 + 16);
+  f32x8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  if (RAGGED) x = live ? x : (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  f32x8 v = x;
+  if (GAIN) {
+    const f32x8 gf = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y),
+                      bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    v = x * gf;
+  }
+  // the bf16 values, widened back from their packed bits (low half of each
+  // word: even element), and the bf16 remainders
+  const bf16x8 h = __builtin_convertvector(v, bf16x8);
+  const u32x4 hb = __builtin_bit_cast(u32x4, h);
+  const f32x8 hf = {__uint_as_float(hb.x << 16), __uint_as_float(hb.x & 0xffff0000u),
+                    __uint_as_float(hb.y << 16), __uint_as_float(hb.y & 0xffff0000u),
+                    __uint_as_float(hb.z << 16), __uint_as_float(hb.z & 0xffff0000u),
+                    __uint_as_float(hb.w << 16), __uint_as_float(hb.w & 0xffff0000u)};
+  const bf16x8 lo = __builtin_convertvector(v - hf, bf16x8);
+  *(bf16x8 *)(ub + lane * 16) = h;
+  *(bf16x8 *)(ub + 1024 + lane * 16) = lo;
+}
+// Control wave, slices after the first: wait for this wave's copies (all of
+// them: the next slice's are issued after this), then convert slice p in
+// place, unit by unit: each lane reads its 32 bytes, and only then (the same
+// wave, in order) writes its 16 + 16 bytes of the unit.  The gains of eight
+// k-blocks are loaded together, ahead of the wait.
 template <bool GAIN, bool RAGGED>
 DEV void mx_convert_t(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb,
                       float (&ssl)[4]) {
   const int lane = tidx() & 63, B16 = g.B16;
   const int nkb = mx_units(g, p) / B16;
   char *xb = (char *)sm.xs + pb * (g.nkb * B16 * 2048);
-  const bool live[4] = {lane % 16 < d.B, 16 + lane % 16 < d.B, 32 + lane % 16 < d.B,
-                        48 + lane % 16 < d.B};
   for (int k0 = 0; k0 < nkb; k0 += 8) {
     u32x4 gq[8];
 #pragma unroll
@@ -1517,36 +1545,11 @@ DEV void mx_convert_t(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (k0 + j >= nkb) break;
-      const u32x4 gv = gq[j];
-      const f32x8 gf = {bf_lo(gv.x), bf_hi(gv.x), bf_lo(gv.y), bf_hi(gv.y),
-                        bf_lo(gv.z), bf_hi(gv.z), bf_lo(gv.w), bf_hi(gv.w)};
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         if (st >= B16) break;
-        char *ub = xb + ((k0 + j) * B16 + st) * 2048;
-        const f32x4 a0 = *(const f32x4 *)(ub + lane * 32);
-        const f32x4 a1 = *(const f32x4 *)(ub + lane * 32 + 16);
-        f32x8 x = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        if (RAGGED) x = live[st] ? x : (f32x8){0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        f32x8 v = x;
-        if (GAIN) {
-          float ss = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-          ssl[st] += ss;
-          v = x * gf;
-        }
-        // the bf16 values, widened back from their packed bits (low half of
-        // each word: even element), and the bf16 remainders
-        const bf16x8 h = __builtin_convertvector(v, bf16x8);
-        const u32x4 hb = __builtin_bit_cast(u32x4, h);
-        const f32x8 hf = {__uint_as_float(hb.x << 16), __uint_as_float(hb.x & 0xffff0000u),
-                          __uint_as_float(hb.y << 16), __uint_as_float(hb.y & 0xffff0000u),
-                          __uint_as_float(hb.z << 16), __uint_as_float(hb.z & 0xffff0000u),
-                          __uint_as_float(hb.w << 16), __uint_as_float(hb.w & 0xffff0000u)};
-        const bf16x8 lo = __builtin_convertvector(v - hf, bf16x8);
-        *(bf16x8 *)(ub + lane * 16) = h;
-        *(bf16x8 *)(ub + 1024 + lane * 16) = lo;
+        mx_unit<GAIN, RAGGED>(xb + ((k0 + j) * B16 + st) * 2048, gq[j],
+                              st * 16 + lane % 16 < d.B, ssl[st]);
       }
     }
   }
@@ -1561,6 +1564,45 @@ DEV void mx_convert(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb,
   } else {
     if (ragged) mx_convert_t<false, true>(sm, d, g, t, p, pb, ssl);
     else mx_convert_t<false, false>(sm, d, g, t, p, pb, ssl);
+  }
+}
+// The first slice is converted by every wave (the compute waves have nothing
+// else to do before it): the control wave copies it and puts its gains in
+// LDS (sm.red, bf16 pairs) before a barrier; then wave w converts units w,
+// w+8, ... with gains from LDS, so no wave waits for a vector memory load.
+DEV uint32_t *mx_gains(Smem &sm) { return (uint32_t *)&sm.red[0][0]; }
+DEV void mx_copy0(Smem &sm, CP &d, const MGeo &g, const TD &t) {
+  const int lane = tidx() & 63;
+  mx_dma(sm, d, g, t, 0, 0);
+  const int n16 = min(g.Ks, g.K) / 8;  // 16-byte chunks of gains (Ks <= 512: one per lane)
+  if (t.gain && lane < n16)
+    ((u32x4 *)mx_gains(sm))[lane] = ldg((const u32x4 *)(t.gain + g.k0) + lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+template <bool GAIN, bool RAGGED>
+DEV void mx_convert0_t(Smem &sm, CP &d, const MGeo &g, float (&ssl)[4]) {
+  const int lane = tidx() & 63, wave = uni(tidx() >> 6), B16 = g.B16;
+  const int nu = mx_units(g, 0);
+  const u32x4 *gl = (const u32x4 *)mx_gains(sm);
+  for (int u = wave; u < nu; u += kWaves) {
+    const int kb = u / B16, st = u - kb * B16;
+    const u32x4 gv = GAIN ? gl[kb * 4 + (lane >> 4)]
+                          : (u32x4){0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+    float ss = 0.f;
+    mx_unit<GAIN, RAGGED>((char *)sm.xs + u * 2048, gv, st * 16 + lane % 16 < d.B, ss);
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+      if (s2 == st) ssl[s2] += ss;
+  }
+}
+DEV void mx_convert0(Smem &sm, CP &d, const MGeo &g, const TD &t, float (&ssl)[4]) {
+  const bool ragged = g.B16 * 16 > d.B;
+  if (t.gain) {
+    if (ragged) mx_convert0_t<true, true>(sm, d, g, ssl);
+    else mx_convert0_t<true, false>(sm, d, g, ssl);
+  } else {
+    if (ragged) mx_convert0_t<false, true>(sm, d, g, ssl);
+    else mx_convert0_t<false, false>(sm, d, g, ssl);
   }
 }
 // Every wave's sums of squares to LDS (sm.red as [wave][lane][tile]); after
@@ -1762,8 +1804,9 @@ DEV bool gemv_mfma_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
   trace_start(d, t);
   const MGeo g = mgeo_of(d, t);
   float ssl[4] = {0.f, 0.f, 0.f, 0.f};
-  mx_dma(sm, d, g, t, 0, 0);
-  mx_convert(sm, d, g, t, 0, 0, ssl);
+  mx_copy0(sm, d, g, t);
+  __syncthreads();  // slice 0 copied, its gains in LDS
+  mx_convert0(sm, d, g, t, ssl);
   if (g.P > 1) mx_dma(sm, d, g, t, 1, 1);
   trace_mark(d, t, 0);
   __syncthreads();  // slice 0 staged
@@ -1815,8 +1858,10 @@ DEV bool gemv_mfma_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool pe
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  const float ssl[4] = {0.f, 0.f, 0.f, 0.f};  // the control wave stages the activations
+  float ssl[4] = {0.f, 0.f, 0.f, 0.f};  // (the control wave stages the later slices)
   const KSplit k = ksplit_of(t);
+  __syncthreads();  // slice 0 copied, its gains in LDS
+  mx_convert0(sm, d, g, t, ssl);
   __syncthreads();  // slice 0 staged
   for (int p = 0; p < g.P; ++p) {
     const char *xb = (const char *)sm.xs + (p & 1) * (g.nkb * g.B16 * 2048);
