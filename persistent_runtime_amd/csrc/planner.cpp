@@ -176,7 +176,12 @@ static int add_gemv_mfma(Builder &b, int op, int layer, const std::vector<RowSeg
   for (size_t i = 0; i < segs.size(); ++i) {
     const int rows = segs[i].rows;
     if (rows % 16) return -1;
-    const int g = rows / 16, nb = (rows + Rmax - 1) / Rmax;
+    const int g = rows / 16;
+    int nb = (rows + Rmax - 1) / Rmax;
+    // more blocks than workers (the LM head): a whole number of blocks per
+    // worker, so every worker streams the same share
+    if (segs.size() == 1 && nb > n_workers)
+      nb = std::min(g, (nb + n_workers - 1) / n_workers * n_workers);
     for (int k = 0; k < nb; ++k) {
       const int g0 = (int)((int64_t)g * k / nb), g1 = (int)((int64_t)g * (k + 1) / nb);
       blocks.push_back({i, segs[i].row0 + 16 * g0, 16 * (g1 - g0)});
