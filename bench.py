@@ -206,6 +206,7 @@ def run_ragged(args, torch):
         opts = {} if args.attn_splits is None else {"attn_splits": args.attn_splits}
         opts["attn_order"] = args.attn_order
         opts["batched_mfma"] = args.batched_mfma
+        opts["attn_pool"] = args.attn_pool
 
         def run(plan, k0, k1, timed):
             tok = torch.as_tensor(synth.make_prompt(B, model["vocab"], seed=7 + k0),
@@ -271,7 +272,7 @@ def run_ragged(args, torch):
                                    f"16-token shuffled pages, retire/join p=1/32 per step",
                        "batch": B, "attn_splits": args.attn_splits,
                        "attn_order": args.attn_order,
-                       "batched_mfma": args.batched_mfma,
+                       "batched_mfma": args.batched_mfma, "attn_pool": args.attn_pool,
                        "tasks_per_step": info["n_tasks"]},
             "sol_fraction": round(achieved / 8000.0, 4),
             "bytes_per_step": int(sum(nbytes) / kk),
@@ -335,6 +336,8 @@ def main():
     ap.add_argument("--attn-splits", type=int, default=None,
                     help="KV splits per (sequence, KV head); default: the planner's choice")
     ap.add_argument("--kpo-steps", type=int, default=64, help="kernel-per-op comparison steps")
+    ap.add_argument("--attn-pool", type=int, default=0, choices=(-1, 0, 1),
+                    help="ragged: attention claimed at run time (0 auto, 1 on, -1 static)")
     ap.add_argument("--batched-mfma", type=int, default=0, choices=(-1, 0, 1),
                     help="ragged: GEMVs as matrix-core tiles (0 auto, 1 for any batch >= 2, -1 off)")
     ap.add_argument("--attn-order", type=int, default=0, choices=(-1, 0, 1),

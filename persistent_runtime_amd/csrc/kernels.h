@@ -341,10 +341,13 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws,
       uint32_t seen = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if ((int32_t)(seen - want) < 0) {
         const uint64_t t0 = wall_clock64();
-        for (;;) {
+        // one memory round trip per retry: the error word and the clock are
+        // looked at every 16th
+        for (int it = 1;; ++it) {
           __builtin_amdgcn_s_sleep(1);
           seen = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if ((int32_t)(seen - want) >= 0) break;
+          if (it % 16) continue;
           if (error_set(d)) { ok = 0; break; }
           if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
             set_error(d, DEVERR_TIMEOUT, t.gidx, t.wait_ev[i], seen, want);
@@ -728,15 +731,19 @@ DEV u32x4 wait_pairs(Smem &sm, CP &d, const CallArgs &ca, const TD &t,
                      __amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   const uint32_t tag = ca.tag;
   const uint64_t t0 = wall_clock64();
-  while (v.y != tag || v.w != tag) {
-    if (error_set(d)) {
-      sm.imisc[2] = (int)tag;
-      break;
-    }
-    if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
-      set_error(d, DEVERR_TIMEOUT, t.gidx, -4, v.y != tag ? v.y : v.w, tag);
-      sm.imisc[2] = (int)tag;
-      break;
+  // one memory round trip per retry: the error word and the clock are
+  // looked at before every 16th
+  for (int it = 0; v.y != tag || v.w != tag; ++it) {
+    if (it % 16 == 15) {
+      if (error_set(d)) {
+        sm.imisc[2] = (int)tag;
+        break;
+      }
+      if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
+        set_error(d, DEVERR_TIMEOUT, t.gidx, -4, v.y != tag ? v.y : v.w, tag);
+        sm.imisc[2] = (int)tag;
+        break;
+      }
     }
     __builtin_amdgcn_s_sleep(1);
     v = __builtin_bit_cast(u32x4, lda4(r, off));
@@ -751,15 +758,17 @@ DEV float ldt_wait(Smem &sm, CP &d, const CallArgs &ca, const TD &t, const float
   uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if ((uint32_t)(v >> 32) != ca.tag) {
     const uint64_t t0 = wall_clock64();
-    while ((uint32_t)(v >> 32) != ca.tag) {
-      if (error_set(d)) {
-        sm.imisc[2] = (int)ca.tag;
-        break;
-      }
-      if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
-        set_error(d, DEVERR_TIMEOUT, t.gidx, -4, (uint32_t)(v >> 32), ca.tag);
-        sm.imisc[2] = (int)ca.tag;
-        break;
+    for (int it = 0; (uint32_t)(v >> 32) != ca.tag; ++it) {
+      if (it % 16 == 15) {  // (as in wait_pairs)
+        if (error_set(d)) {
+          sm.imisc[2] = (int)ca.tag;
+          break;
+        }
+        if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
+          set_error(d, DEVERR_TIMEOUT, t.gidx, -4, (uint32_t)(v >> 32), ca.tag);
+          sm.imisc[2] = (int)ca.tag;
+          break;
+        }
       }
       __builtin_amdgcn_s_sleep(1);
       v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1743,10 +1752,11 @@ DEV bool ksplit_arrive(Smem &sm, CP &d, const CallArgs &ca, const TD &t, const K
     int ok = 1;
     if ((int32_t)(seen - want) < 0) {
       const uint64_t t0 = wall_clock64();
-      for (;;) {
+      for (int it = 1;; ++it) {  // (the error word and the clock every 16th retry)
         __builtin_amdgcn_s_sleep(1);
         seen = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((int32_t)(seen - want) >= 0) break;
+        if (it % 16) continue;
         if (error_set(d)) { ok = 0; break; }
         if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
           set_error(d, DEVERR_TIMEOUT, t.gidx, -5, seen, want);

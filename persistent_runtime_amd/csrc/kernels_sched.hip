@@ -39,10 +39,11 @@ DEV int poll_entry(CP &d, const CallArgs &ca, const uint64_t *p, int who, int wh
   uint64_t v = ld64(p);
   if ((uint32_t)(v >> 32) == ca.tag) return (int)(uint32_t)v;
   const uint64_t t0 = wall_clock64();
-  for (;;) {
+  for (int it = 1;; ++it) {  // (the error word and the clock every 16th retry)
     __builtin_amdgcn_s_sleep(1);
     v = ld64(p);
     if ((uint32_t)(v >> 32) == ca.tag) return (int)(uint32_t)v;
+    if (it % 16) continue;
     if (error_set(d)) return 0;
     if ((int64_t)(wall_clock64() - t0) > d.spin_budget) {
       set_error(d, DEVERR_TIMEOUT, who, what, (uint32_t)(v >> 32), ca.tag);
