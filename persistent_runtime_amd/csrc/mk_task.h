@@ -54,7 +54,7 @@ enum Op : int16_t {
   OP_EDOWN = 11, OP_COMBINE = 12, OP_LMHEAD = 13, OP_ARGMAX = 14, OP_KVAPP = 15
 };
 
-// 64-byte task descriptor.  Field use per op:
+// 128-byte task descriptor.  Field use per op:
 //   EMBED   a0=slot
 //   QKV     a0=matrix (0 q, 1 k, 2 v) a1=row0 a2=rows
 //   ATTN    a0=slot a1=kv head a2=split; claimed plans also a3 = this
