@@ -74,7 +74,8 @@ struct mk_plan {
   float *stage_logits = nullptr;
   uint32_t *ctrl = nullptr;  // CTRL_WORDS control words, the event counters, then
                              // the split-attention and split-K arrival counters
-  int n_att_cnt = 0;         // arrival counters (both kinds)
+  int n_ev_words = 0;        // event counters, kCtrStride words each
+  int n_att_cnt = 0;         // words of the arrival and claim counters after them
   int n_ctrl_words = 0;
   // Plans built by mk_build_plan_noalloc carve their device state out of the
   // device's static scratch array instead of allocating it.
@@ -472,10 +473,11 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     int32_t *d_wq;
     if ((rc = p->alloc(&d_wq, hp.worker_off.size() + hp.worker_list.size(), "worker queues")))
       return rc;
-    p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads + hp.n_kcnt + c.n_layers;
+    p->n_ev_words = E * kCtrStride;
+    p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads + (hp.n_kcnt + c.n_layers) * kCtrStride;
     const int n_sched_cnt = sched ? T + hp.n_workers + NS : 0;  // pending, wtail, stail
     p->n_att_cnt += n_sched_cnt;
-    p->n_ctrl_words = CTRL_WORDS + E + p->n_att_cnt;
+    p->n_ctrl_words = CTRL_WORDS + p->n_ev_words + p->n_att_cnt;
     if ((rc = p->alloc(&p->ctrl, p->n_ctrl_words, "event counters"))) return rc;
     const int64_t n_kpart = hp.n_kpart * kpart_slot(B);
     // matrix-core plans: the values-only copy of the tagged vectors (x
@@ -580,9 +582,9 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     d.rope_sin = rope + (size_t)hp.max_pos * half;
     d.ctrl = p->ctrl;
     d.ev = p->ctrl + CTRL_WORDS;
-    d.att_cnt = d.ev + E;
+    d.att_cnt = d.ev + p->n_ev_words;
     d.kcnt = d.att_cnt + c.n_layers * c.max_batch * c.n_kv_heads;
-    d.pool_cnt = d.kcnt + hp.n_kcnt;
+    d.pool_cnt = d.kcnt + (size_t)hp.n_kcnt * kCtrStride;
     d.attn_pool = hp.attn_pool ? 1 : 0;
     // claim order: longest context first unless asked otherwise (measured on
     // the 8B shape with contexts U[128, 16384]: 16 slots -3.3 %, 64 -0.6 %)
@@ -622,7 +624,7 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
       d.wring = sched_rings;
       d.sring = sched_rings + T;
       // counters after the arrival counters: reset with them
-      d.pending = p->ctrl + CTRL_WORDS + E + (p->n_att_cnt - n_sched_cnt);
+      d.pending = p->ctrl + CTRL_WORDS + p->n_ev_words + (p->n_att_cnt - n_sched_cnt);
       d.wtail = d.pending + T;
       d.stail = d.wtail + hp.n_workers;
     }
@@ -709,7 +711,7 @@ static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positi
   if (plan->graph_replay) {
     // a replayable step: counters from zero and a data tag bumped on the
     // device, no state carried on the host
-    HIP_TRY(launch_zero_u32(d.ev, (int)plan->hp.ev_thr.size() + plan->n_att_cnt, s),
+    HIP_TRY(launch_zero_u32(d.ev, plan->n_ev_words + plan->n_att_cnt, s),
             "counter clear");
     HIP_TRY(launch_bump_tag(plan->ctrl + CTRL_TAG, s), "tag bump");
     plan->epoch = 0;
@@ -740,7 +742,7 @@ static int step_impl(mk_plan *plan, const int32_t *tokens, const int32_t *positi
   // counters are monotonic per step (both executors count split-attention
   // arrivals); reset them before they could wrap
   if (!plan->graph_replay && ++plan->epoch >= plan->epoch_limit) {
-    HIP_TRY(launch_zero_u32(d.ev, (int)plan->hp.ev_thr.size() + plan->n_att_cnt, s),
+    HIP_TRY(launch_zero_u32(d.ev, plan->n_ev_words + plan->n_att_cnt, s),
             "counter reset");
     plan->epoch = 0;
   }

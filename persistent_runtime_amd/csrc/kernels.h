@@ -336,7 +336,7 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws,
       if (i < i0) continue;
       if (i >= i1 || !ok) break;
       if (t.wait_ev[i] & kDataEdge) continue;
-      uint32_t *c = d.ev + t.wait_ev[i];
+      uint32_t *c = d.ev + (size_t)t.wait_ev[i] * kCtrStride;
       const uint32_t want = (ca.epoch + 1u) * (uint32_t)t.wait_thr[i];
       uint32_t seen = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if ((int32_t)(seen - want) < 0) {
@@ -411,7 +411,7 @@ DEV void signal_count(CP &d, const TD &t, int count) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       if (i < t.n_sig && !(t.sig_ev[i] & kDataEdge))
-        __hip_atomic_fetch_add(d.ev + t.sig_ev[i], (uint32_t)count, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(d.ev + (size_t)t.sig_ev[i] * kCtrStride, (uint32_t)count, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -1745,7 +1745,7 @@ DEV void ksplit_publish(Smem &sm, CP &d, const MGeo &g, const KSplit &k) {
 // step is abandoned.
 DEV bool ksplit_arrive(Smem &sm, CP &d, const CallArgs &ca, const TD &t, const KSplit &k) {
   if (tidx() == 0) {
-    uint32_t *c = d.kcnt + t.a4;
+    uint32_t *c = d.kcnt + (size_t)t.a4 * kCtrStride;
     const uint32_t want = (ca.epoch + 1u) * (uint32_t)k.ns;
     uint32_t seen =
         __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
@@ -2520,7 +2520,7 @@ DEV bool run_attn_pool(Smem &sm, CP &d, const CallArgs &ca, const TD &t0, WState
   const int first = t0.a4, n = t0.rpp & 0xffff;
   const int per_slot = n / d.B;  // the layer's tasks are slot-major
   const uint32_t per_step = (uint32_t)t0.rpp >> 16;
-  uint32_t *cnt = d.pool_cnt + t0.layer;
+  uint32_t *cnt = d.pool_cnt + (size_t)t0.layer * kCtrStride;
   for (;;) {
     if (tidx() == 0) {
       const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -105,6 +105,12 @@ struct alignas(16) Task {
 };
 static_assert(sizeof(Task) == 128, "task descriptor is 128 bytes");
 
+// Event counters, split-K arrival counters and claimed-attention counters
+// are polled by many workgroups at once: each sits alone in a 128-byte line
+// (stride in u32 words), so polls and atomics on one counter do not queue
+// behind those on its neighbours.
+constexpr int kCtrStride = 32;
+
 // control words (u32) at the head of the counter buffer
 enum Ctrl {
   CTRL_TICKET = 0, CTRL_DONE = 1, CTRL_ERR = 2, CTRL_ERR_TASK = 3,
