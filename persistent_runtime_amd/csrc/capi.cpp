@@ -474,7 +474,7 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     if ((rc = p->alloc(&d_wq, hp.worker_off.size() + hp.worker_list.size(), "worker queues")))
       return rc;
     p->n_ev_words = E * kCtrStride;
-    p->n_att_cnt = c.n_layers * c.max_batch * c.n_kv_heads + (hp.n_kcnt + c.n_layers) * kCtrStride;
+    p->n_att_cnt = (c.n_layers * c.max_batch * c.n_kv_heads + hp.n_kcnt + c.n_layers) * kCtrStride;
     const int n_sched_cnt = sched ? T + hp.n_workers + NS : 0;  // pending, wtail, stail
     p->n_att_cnt += n_sched_cnt;
     p->n_ctrl_words = CTRL_WORDS + p->n_ev_words + p->n_att_cnt;
@@ -583,7 +583,7 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     d.ctrl = p->ctrl;
     d.ev = p->ctrl + CTRL_WORDS;
     d.att_cnt = d.ev + p->n_ev_words;
-    d.kcnt = d.att_cnt + c.n_layers * c.max_batch * c.n_kv_heads;
+    d.kcnt = d.att_cnt + (size_t)c.n_layers * c.max_batch * c.n_kv_heads * kCtrStride;
     d.pool_cnt = d.kcnt + (size_t)hp.n_kcnt * kCtrStride;
     d.attn_pool = hp.attn_pool ? 1 : 0;
     // claim order: longest context first unless asked otherwise (measured on

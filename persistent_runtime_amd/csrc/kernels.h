@@ -2459,7 +2459,7 @@ DEV bool run_small(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persis
     if (persistent) trace_finish(d, t);
     if (tidx() == 0) {
       const uint32_t old = __hip_atomic_fetch_add(
-          d.att_cnt + ((size_t)t.layer * d.B + t.a0) * d.nkv + t.a1, 1u, __ATOMIC_RELAXED,
+          d.att_cnt + (((size_t)t.layer * d.B + t.a0) * d.nkv + t.a1) * kCtrStride, 1u, __ATOMIC_RELAXED,
           __HIP_MEMORY_SCOPE_AGENT);
       sm.imisc[1] = old == (ca.epoch + 1u) * (uint32_t)d.S - 1u;
     }

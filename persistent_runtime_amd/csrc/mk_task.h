@@ -105,8 +105,9 @@ struct alignas(16) Task {
 };
 static_assert(sizeof(Task) == 128, "task descriptor is 128 bytes");
 
-// Event counters, split-K arrival counters and claimed-attention counters
-// are polled by many workgroups at once: each sits alone in a 128-byte line
+// Event counters, split-attention and split-K arrival counters and
+// claimed-attention counters are polled or counted on by many workgroups at
+// once: each sits alone in a 128-byte line
 // (stride in u32 words), so polls and atomics on one counter do not queue
 // behind those on its neighbours.
 constexpr int kCtrStride = 32;
