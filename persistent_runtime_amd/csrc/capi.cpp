@@ -74,7 +74,8 @@ struct mk_plan {
   float *stage_logits = nullptr;
   uint32_t *ctrl = nullptr;  // CTRL_WORDS control words, the event counters, then
                              // the split-attention and split-K arrival counters
-  int n_ev_words = 0;        // event counters, kCtrStride words each
+  int ev_rep = 1;            // replicas per event counter
+  int n_ev_words = 0;        // event counters, kCtrStride words per replica
   int n_att_cnt = 0;         // words of the arrival and claim counters after them
   int n_ctrl_words = 0;
   // Plans built by mk_build_plan_noalloc carve their device state out of the
@@ -473,7 +474,8 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     int32_t *d_wq;
     if ((rc = p->alloc(&d_wq, hp.worker_off.size() + hp.worker_list.size(), "worker queues")))
       return rc;
-    p->n_ev_words = E * kCtrStride;
+    p->ev_rep = sched ? 1 : kEvReplicas;
+    p->n_ev_words = E * p->ev_rep * kCtrStride;
     p->n_att_cnt = (c.n_layers * c.max_batch * c.n_kv_heads + hp.n_kcnt + c.n_layers) * kCtrStride;
     const int n_sched_cnt = sched ? T + hp.n_workers + NS : 0;  // pending, wtail, stail
     p->n_att_cnt += n_sched_cnt;
@@ -582,6 +584,7 @@ static int build_plan(const mk_config *cfg, const mk_weights *w, const mk_kv *kv
     d.rope_sin = rope + (size_t)hp.max_pos * half;
     d.ctrl = p->ctrl;
     d.ev = p->ctrl + CTRL_WORDS;
+    d.ev_rep = p->ev_rep;
     d.att_cnt = d.ev + p->n_ev_words;
     d.kcnt = d.att_cnt + (size_t)c.n_layers * c.max_batch * c.n_kv_heads * kCtrStride;
     d.pool_cnt = d.kcnt + (size_t)hp.n_kcnt * kCtrStride;

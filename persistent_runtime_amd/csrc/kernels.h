@@ -301,6 +301,21 @@ DEV void set_error(CP &d, uint32_t code, int task, int ev, uint32_t seen, uint32
     __hip_atomic_store(&d.ctrl[CTRL_ERR_WANT], want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
+// Event counter e is ev_rep replicas, each in a line of its own: a worker
+// counts its completions on replica (worker % ev_rep), a waiter adds them
+// up, so the signals of an operation's tiles spread over ev_rep lines.
+DEV uint32_t *ev_word(CP &d, int e, int r) {
+  return d.ev + ((size_t)e * d.ev_rep + r) * kCtrStride;
+}
+// Control wave: the count of event e over its replicas (lane r loads r).
+DEV uint32_t ev_count(CP &d, int e) {
+  const int lane = tidx() & 63;
+  uint32_t v = 0;
+  if (lane < d.ev_rep) v = __hip_atomic_load(ev_word(d, e, lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t s = 0;
+  for (int r = 0; r < d.ev_rep; ++r) s += (uint32_t)__builtin_amdgcn_readlane((int)v, r);
+  return s;
+}
 DEV bool error_set(CP &d) {
   return __hip_atomic_load(&d.ctrl[CTRL_ERR], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
@@ -329,23 +344,23 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws,
     need = need || !seen;
   }
   if (!need) return true;
-  if (tidx() == 0) {
+  if (uni(tidx() >> 6) == 0) {  // the control wave polls (lane r: replica r)
     int ok = 1;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       if (i < i0) continue;
       if (i >= i1 || !ok) break;
       if (t.wait_ev[i] & kDataEdge) continue;
-      uint32_t *c = d.ev + (size_t)t.wait_ev[i] * kCtrStride;
+      const int e = t.wait_ev[i];
       const uint32_t want = (ca.epoch + 1u) * (uint32_t)t.wait_thr[i];
-      uint32_t seen = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t seen = ev_count(d, e);
       if ((int32_t)(seen - want) < 0) {
         const uint64_t t0 = wall_clock64();
         // one memory round trip per retry: the error word and the clock are
         // looked at every 16th
         for (int it = 1;; ++it) {
           __builtin_amdgcn_s_sleep(1);
-          seen = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          seen = ev_count(d, e);
           if ((int32_t)(seen - want) >= 0) break;
           if (it % 16) continue;
           if (error_set(d)) { ok = 0; break; }
@@ -361,7 +376,7 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws,
     // XCD stages the same activations): acquire at agent scope, which
     // drops lines the XCD's L2 may hold from before the producers wrote.
     if (ok && d.mfma) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    sm.imisc[0] = ok;
+    if (tidx() == 0) sm.imisc[0] = ok;
   }
   __syncthreads();
   const bool ok = sm.imisc[0] != 0;
@@ -408,10 +423,11 @@ DEV void trace_mark(CP &d, const TD &t, int word) {
 // run reports them).  The caller (thread 0) has drained its wave's stores.
 DEV void signal_count(CP &d, const TD &t, int count) {
   if (tidx() == 0 && count > 0 && t.gidx != d.withhold) {
+    const int r = (int)(blockIdx.x % (uint32_t)d.ev_rep);  // this worker's replica
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       if (i < t.n_sig && !(t.sig_ev[i] & kDataEdge))
-        __hip_atomic_fetch_add(d.ev + (size_t)t.sig_ev[i] * kCtrStride, (uint32_t)count, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(ev_word(d, t.sig_ev[i], r), (uint32_t)count, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
   }
 }

@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(kThreads)
         const int e = t.sig_ev[i] & ~kDataEdge;
         if (cnt == 0) continue;
         const uint32_t want = (ca.epoch + 1u) * (uint32_t)ldg(d.ev_thr + e);
-        if (add32(d.ev + (size_t)e * kCtrStride, cnt) + cnt == want) activate(d, ca, e);
+        if (add32(d.ev + (size_t)e * kCtrStride, cnt) + cnt == want) activate(d, ca, e);  // (ev_rep 1)
       }
       sm.imisc[4] = 0;
     }

@@ -111,6 +111,11 @@ static_assert(sizeof(Task) == 128, "task descriptor is 128 bytes");
 // (stride in u32 words), so polls and atomics on one counter do not queue
 // behind those on its neighbours.
 constexpr int kCtrStride = 32;
+// An event counter is kEvReplicas such lines: each worker counts on one of
+// them and waiters add them up, so the completions of an operation's tiles
+// (one atomic each, all at about the same time) and the waiters' polls do
+// not all queue on one line (8, 16 and 32 replicas measured alike).
+constexpr int kEvReplicas = 8;
 
 // control words (u32) at the head of the counter buffer
 enum Ctrl {
@@ -156,6 +161,7 @@ struct DevPlan {
   const float *rope_cos, *rope_sin;                     // [max_pos][hd/2]
   // control
   uint32_t *ev;            // event counters, after CTRL_WORDS control words
+  int32_t ev_rep;          // replicas per event counter (1 in scheduled plans)
   uint32_t *att_cnt;       // split-attention arrivals per (layer, slot, KV head),
                            // after the event counters; monotonic like them
   uint32_t *kcnt;          // split-K arrivals per matrix-core row block, after att_cnt
