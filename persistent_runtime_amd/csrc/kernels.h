@@ -82,7 +82,8 @@ enum : int {
   DPP_XOR1 = 0xB1,        // quad_perm [1,0,3,2]
   DPP_XOR2 = 0x4E,        // quad_perm [2,3,0,1]
   DPP_HALF_MIRROR = 0x141,  // lane i <- lane 7-i within 8
-  DPP_MIRROR = 0x140        // lane i <- lane 15-i within 16
+  DPP_MIRROR = 0x140,       // lane i <- lane 15-i within 16
+  DPP_ROR8 = 0x128          // lane i <- lane i^8 within 16 (row rotate by 8)
 };
 template <int CTRL> DEV float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -1402,6 +1403,7 @@ DEV MGeo mgeo(const uint16_t *w0, const uint16_t *w1, int rows, int K, int B, in
   const int maxg = (g.nseg == 2 || g.NGs > kCW) ? 2 : 1;
   int ks = (kMaxChunks / maxg) * 32;                       // register slots
   ks = min(ks, kLdsXBytes / (2 * g.B16 * 16 * 4));         // two slices of hi+lo bf16
+  ks = ks / 64 * 64;                                       // whole 64-column pairs
   ks = min(ks, K);
   g.Ks = ks;
   g.nkb = ks >> 5;
@@ -1429,16 +1431,40 @@ DEV bool mgroup(const MGeo &g, int cw, int gi, int &seg, int &slot) {
 
 // Address of lane's 16 bytes of register slot j (group j / NKB, k-block
 // j % NKB) of wave cw in pass p; slots without a chunk read the idle line.
+// Slots are loaded in pairs (k-blocks 2i, 2i+1: 64 columns, one 128-byte
+// line of each of the group's 16 rows), so every load covers 8 whole lines:
+// the even slot P takes rows 0-7, the odd one Q rows 8-15.  Lane l = 16q + r
+// of slot h loads row 8h + r%8, columns 8q..+8 of k-block 0 of the pair
+// when r/8 == h (exactly its own A operand of that k-block), else of
+// k-block 1 (the A operand lane l^8 needs for k-block 1).  mpair then
+// builds both A operands with a select and a rotate within 16 lanes.
+// Lanes whose columns lie beyond the tile read the idle line (tiles are
+// whole pairs wide; this only guards memory).
 template <int NKB>
 DEV uint64_t maddr(const MGeo &g, int cw, int j, int p) {
-  const int lane = tidx() & 63;
-  const int gi = j / NKB, kb = j % NKB;
+  const int lane = tidx() & 63, r = lane & 15, q = lane >> 4;
+  const int gi = j / NKB, kb = j % NKB, h = kb & 1;
   int seg = 0, slot = 0;
-  const int k = p * g.Ks + kb * 32;
-  const bool ok = gi < 2 && mgroup(g, cw, gi, seg, slot) && kb < g.nkb && k < g.K;
+  const int k2 = p * g.Ks + (kb & ~1) * 32;  // the pair's first column
+  const int col = k2 + 8 * (q + 4 * ((r >> 3) ^ h));
+  const bool ok = gi < 2 && mgroup(g, cw, gi, seg, slot) && (kb & ~1) < g.nkb && col < g.K;
   const uint16_t *base = seg ? g.s1 : g.s0;
-  const uint64_t a = (uint64_t)(base + (size_t)(slot * 16 + (lane & 15)) * g.ld + k + 8 * (lane >> 4));
+  const int row = slot * 16 + (r & 7) + 8 * h;
+  const uint64_t a = (uint64_t)(base + (size_t)row * g.ld + col);
   return ok ? a : idle_addr();
+}
+// A loaded pair into the A operands of its two k-blocks, in place: lanes
+// r < 8 hold their k-block-0 operand in P, lanes r >= 8 in Q; the
+// k-block-1 operand of lane l sits in lane l^8 (of Q for r < 8, of P for
+// r >= 8): a select, then a rotate by 8 within each row of 16 lanes.
+DEV void mpair(u32x4 &P, u32x4 &Q) {
+  const bool lo = (tidx() & 15) < 8;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int p = (int)P[e], qq = (int)Q[e];
+    P[e] = (uint32_t)(lo ? p : qq);
+    Q[e] = (uint32_t)dppi<DPP_ROR8>(lo ? qq : p);
+  }
 }
 DEV uint64_t maddr_any(const MGeo &g, int cw, int j, int p) {
   return g.nkb >= 16 ? maddr<16>(g, cw, j, p) : maddr<8>(g, cw, j, p);
@@ -1457,31 +1483,40 @@ DEV void mpass(const MGeo &g, Buf &w, f32x4 (&acc)[2][4], const char *xb, int cw
   const int lane = tidx() & 63;
   const bool last = p + 1 == g.P;
 #pragma unroll
-  for (int j = 0; j < kMaxChunks; ++j) {
+  for (int j = 0; j < kMaxChunks; j += 2) {  // slot pairs: k-blocks kb, kb + 1
     const int gi = j / NKB, kb = j % NKB;
     int seg, slot;
-    const bool ok = gi < 2 && mgroup(g, cw, gi, seg, slot) && kb < g.nkb &&
-                    p * g.Ks + kb * 32 < g.K;
-    if (ok) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, w[j]);
-      // value parts of every slot tile, then the remainders: consecutive
-      // products accumulate into different tiles
+    const bool has = gi < 2 && mgroup(g, cw, gi, seg, slot) && kb < g.nkb;
+    const bool ok0 = has && p * g.Ks + kb * 32 < g.K;
+    const bool ok1 = has && p * g.Ks + (kb + 1) * 32 < g.K;
+    if (ok0) {
+      mpair(w[j], w[j + 1]);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 xv[4];
+      for (int m = 0; m < 2; ++m) {
+        if (m == 1 && !ok1) break;
+        const bf16x8 a = __builtin_bit_cast(bf16x8, w[j + m]);
+        // value parts of every slot tile, then the remainders: consecutive
+        // products accumulate into different tiles
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          if (st < B16)
-            xv[st] = *(const bf16x8 *)(xb + (kb * B16 + st) * 2048 + half * 1024 + lane * 16);
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 xv[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          if (st < B16)
-            acc[gi][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xv[st], acc[gi][st], 0, 0, 0);
+          for (int st = 0; st < 4; ++st)
+            if (st < B16)
+              xv[st] = *(const bf16x8 *)(xb + ((kb + m) * B16 + st) * 2048 + half * 1024 + lane * 16);
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            if (st < B16)
+              acc[gi][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xv[st], acc[gi][st], 0, 0, 0);
+        }
       }
     }
-    const uint64_t na = !last ? maddr<NKB>(g, cw, j, p + 1)
-                              : (pre ? maddr_any(gn, cw, j, 0) : idle_addr());
-    w[j] = ldnt((const u32x4 *)na);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint64_t na = !last ? maddr<NKB>(g, cw, j + m, p + 1)
+                                : (pre ? maddr_any(gn, cw, j + m, 0) : idle_addr());
+      w[j + m] = ldnt((const u32x4 *)na);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }

@@ -193,7 +193,7 @@ static int add_gemv_mfma(Builder &b, int op, int layer, const std::vector<RowSeg
   if (op != OP_LMHEAD && NB < n_workers)
     ns = std::max(1, std::min({n_workers / NB, K / 256, kMaxKSplit}));
   int kc = (K + ns - 1) / ns;
-  kc = (kc + 31) / 32 * 32;
+  kc = (kc + 63) / 64 * 64;  // whole 64-column pairs (a tile loads 128-byte lines)
   ns = (K + kc - 1) / kc;
   if (ns > 1) {
     if (kc > 0xffff || NB > 0x7fff) return -1;
@@ -387,10 +387,11 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
 
   bool ok = true;
   // batched decode: matrix-core GEMV tiles when every static row count is a
-  // whole number of 16-row groups
+  // whole number of 16-row groups and every input row a whole number of
+  // 64-column pairs (a tile loads whole 128-byte lines)
   {
-    const bool rows16 = H % 16 == 0 && (nq * hd) % 16 == 0 && hd % 16 == 0 &&
-                        c.vocab % 16 == 0 && (moe ? c.n_experts % 16 == 0 : c.ffn_dim % 16 == 0);
+    const bool rows16 = H % 64 == 0 && (nq * hd) % 64 == 0 && hd % 16 == 0 &&
+                        c.vocab % 16 == 0 && (moe ? c.n_experts % 16 == 0 : c.ffn_dim % 64 == 0);
     p.mfma = !sched && B <= kMfmaMaxBatch && rows16 &&
              (o.batched_mfma > 0 ? B >= 2 : o.batched_mfma == 0 && B >= 3);
   }

@@ -366,15 +366,16 @@ def test_graph_replay_matches_eager(tiny, executor):
     r.plan.free()
 
 
-@pytest.mark.parametrize("mfma", [0, -1], ids=["matrix_cores", "vector"])
-def test_tiny_batch16(tiny, mfma):
+@pytest.mark.parametrize("B,mfma", [(16, 0), (16, -1), (40, 0)],
+                         ids=["matrix_cores", "vector", "matrix_cores_40"])
+def test_tiny_batch16(tiny, B, mfma):
     """16 slots (the matrix-core GEMV tiles by default, the vector path when
-    switched off): every slot's logits against the oracle decoding that slot
-    alone, over prompts of different lengths and three teacher-forced steps;
-    one slot stays empty throughout."""
+    switched off) and 40 slots (three 16-slot tiles, so a 320-column
+    activation slice per pass): every slot's logits against the oracle
+    decoding that slot alone, over prompts of different lengths and three
+    teacher-forced steps; one slot stays empty throughout."""
     Wd, Wt = tiny
-    B = 16
-    r = Runner(TINY, Wd, B=B, maxp=8, batched_mfma=mfma)
+    r = Runner(TINY, Wd, B=B, maxp=(10 + 3 * B + 3 + 15) // 16, batched_mfma=mfma)
     prompts = [synth.make_prompt(10 + 3 * b, TINY["vocab"], seed=100 + b).tolist() for b in range(B)]
     caches, refs = {}, {}
     for b in range(B - 1):
