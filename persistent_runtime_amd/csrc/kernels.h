@@ -770,9 +770,14 @@ DEV u32x4 wait_pairs(Smem &sm, CP &d, const CallArgs &ca, const TD &t,
 
 // Value of element i of a tagged vector, loaded until it carries this step's
 // tag (or the step is abandoned: sm.imisc[2] = tag).
-DEV float ldt_wait(Smem &sm, CP &d, const CallArgs &ca, const TD &t, const float *pairs, size_t i) {
+DEV uint64_t ldt_raw(const float *pairs, size_t i) {
+  return __hip_atomic_load((const AS1 uint64_t *)pairs + i, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+// ldt_wait, given the pair's first load v (issued earlier, beside others)
+DEV float ldt_then(Smem &sm, CP &d, const CallArgs &ca, const TD &t, const float *pairs, size_t i,
+                   uint64_t v) {
   const AS1 uint64_t *p = (const AS1 uint64_t *)pairs + i;
-  uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if ((uint32_t)(v >> 32) != ca.tag) {
     const uint64_t t0 = wall_clock64();
     for (int it = 0; (uint32_t)(v >> 32) != ca.tag; ++it) {
@@ -792,6 +797,9 @@ DEV float ldt_wait(Smem &sm, CP &d, const CallArgs &ca, const TD &t, const float
     }
   }
   return __uint_as_float((uint32_t)v);
+}
+DEV float ldt_wait(Smem &sm, CP &d, const CallArgs &ca, const TD &t, const float *pairs, size_t i) {
+  return ldt_then(sm, d, ca, t, pairs, i, ldt_raw(pairs, i));
 }
 
 // Stage nb rows of a tagged vector into LDS exactly as stage_x does (x*g,
@@ -2096,28 +2104,39 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
   const float *cs = d.rope_cos + (size_t)pos * (HD / 2);
   const float *sn = d.rope_sin + (size_t)pos * (HD / 2);
-  // q, k, v are tagged: the loads double as the wait for the projections
+  // q, k, v are tagged: the loads double as the wait for the projections.
+  // A thread's first loads of its key/value and query elements are issued
+  // together; only stale ones are then polled, one after another.
   const size_t q0 = head0 * HD;
+  const size_t kvo = (((size_t)l * B + b) * nkv + g) * HD;
+  uint64_t kra = 0, krc = 0, vr = 0;
+  if (has_cur && tid < HD) {
+    const int i0 = tid & (HD / 2 - 1);
+    kra = ldt_raw(d.k, kvo + i0);
+    krc = ldt_raw(d.k, kvo + i0 + HD / 2);
+    vr = ldt_raw(d.v, kvo + tid);
+  }
   for (int idx = tid; idx < G * HD; idx += kThreads) {
     const int h = idx / HD, i = idx - h * HD, i0 = i & (HD / 2 - 1);
-    const float a = ldt_wait(sm, d, ca, t, d.q, q0 + h * HD + i0);
-    const float c2 = ldt_wait(sm, d, ca, t, d.q, q0 + h * HD + i0 + HD / 2);
+    const uint64_t ra = ldt_raw(d.q, q0 + h * HD + i0);
+    const uint64_t rc = ldt_raw(d.q, q0 + h * HD + i0 + HD / 2);
+    const float a = ldt_then(sm, d, ca, t, d.q, q0 + h * HD + i0, ra);
+    const float c2 = ldt_then(sm, d, ca, t, d.q, q0 + h * HD + i0 + HD / 2, rc);
     const float cv = ldg(cs + i0), sv = ldg(sn + i0);
     const float r = (i < HD / 2) ? a * cv - c2 * sv : a * sv + c2 * cv;
     qs[h * QROW + (i / (HD / 4)) * QQ + (i & (HD / 4 - 1))] = r * scale;
   }
   if (has_cur) {
-    const size_t kvo = (((size_t)l * B + b) * nkv + g) * HD;
     const int pg = uni(ldg(prow + pos / kPageSize));
     const bool pg_ok = pg >= 0 && pg < d.npages;
     if (!pg_ok && tid == 0) set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pg, (uint32_t)d.npages);
-    for (int i = tid; i < HD; i += kThreads) {
+    for (int i = tid; i < HD; i += kThreads) {  // (HD <= kThreads: i == tid)
       const int i0 = i & (HD / 2 - 1);
-      const float a = ldt_wait(sm, d, ca, t, d.k, kvo + i0);
-      const float c2 = ldt_wait(sm, d, ca, t, d.k, kvo + i0 + HD / 2);
+      const float a = ldt_then(sm, d, ca, t, d.k, kvo + i0, kra);
+      const float c2 = ldt_then(sm, d, ca, t, d.k, kvo + i0 + HD / 2, krc);
       const float cv = ldg(cs + i0), sv = ldg(sn + i0);
       const float kr = (i < HD / 2) ? a * cv - c2 * sv : a * sv + c2 * cv;
-      const uint16_t kb = f2bf(kr), vb = f2bf(ldt_wait(sm, d, ca, t, d.v, kvo + i));
+      const uint16_t kb = f2bf(kr), vb = f2bf(ldt_then(sm, d, ca, t, d.v, kvo + i, vr));
       kc[i] = bf1(kb);
       vc[i] = bf1(vb);
       if (pg_ok) {
