@@ -329,6 +329,7 @@ DEV bool error_set(CP &d) {
 // Only the task's waits i0 .. i1-1 are considered (a task may wait for its
 // inputs in stages).  Returns false when the step is being drained after an
 // error.
+DEV bool static_weights(int op);
 DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws, int i0 = 0,
                    int i1 = 3) {
   i1 = min(i1, t.n_wait);
@@ -376,7 +377,11 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws,
     // Matrix-core plans read their inputs through the L2 (every CU of an
     // XCD stages the same activations): acquire at agent scope, which
     // drops lines the XCD's L2 may hold from before the producers wrote.
-    if (ok && d.mfma) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // Plans whose tiles copy their activations device-coherently (mx_sc1)
+    // skip it for those tiles: every other input of a tile (residuals,
+    // split-K partials) is read with coherent loads as well.
+    if (ok && d.mfma && !(d.mx_sc1 && static_weights(t.op)))
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tidx() == 0) sm.imisc[0] = ok;
   }
   __syncthreads();
@@ -509,6 +514,13 @@ DEV uint32_t wslot(const float *xs, int cw, int s) {
 DEV void dma16(uint64_t src, uint32_t lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
+}
+// The same, device-coherent (sc1): reads what other CUs wrote through to
+// memory without an L2 invalidate.
+DEV void dma16_sc1(uint64_t src, uint32_t lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off sc1" ::"v"(src), "s"(m0)
                : "memory", "m0");
 }
 // All kLdsSlots slots of a pass at once: the last slot's DMA (and so every
@@ -1555,8 +1567,11 @@ DEV void mx_dma(Smem &sm, CP &d, const MGeo &g, const TD &t, int p, int pb) {
       const int L = 32 * i + (lane >> 1);
       const int b = st * 16 + (L & 15);
       const int col = g.k0 + p * g.Ks + kb * 32 + 8 * (L >> 4) + 4 * (lane & 1);
-      if (b < d.B)
-        dma16((uint64_t)(src + (size_t)b * g.ld + col), xb + (uint32_t)(u * 2048 + i * 1024));
+      if (b < d.B) {
+        const uint64_t a = (uint64_t)(src + (size_t)b * g.ld + col);
+        const uint32_t l = xb + (uint32_t)(u * 2048 + i * 1024);
+        if (d.mx_sc1) dma16_sc1(a, l); else dma16(a, l);
+      }
     }
   }
 }

@@ -133,6 +133,9 @@ struct DevPlan {
   int32_t max_pos, n_lm_tiles;
   int32_t mfma;            // static GEMVs as matrix-core tiles (batch 16..64)
   int32_t lds_slots;       // kLdsSlots when passes extend into LDS, else 0
+  int32_t mx_sc1;          // matrix-core tiles copy their activations with
+                           // device-coherent (sc1) LDS-DMA and wait without
+                           // the agent-scope acquire fence
   float eps;
   // weights (bf16 as uint16)
   const uint16_t *embed, *lm_head, *final_norm;
