@@ -2206,7 +2206,10 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
         set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pid, (uint32_t)d.npages);
       break;
     }
-    for (int i = 0; i < nc; i += 2) {
+    for (int i = 0;; i += 2) {
+      // (the wave's last pair issues no loads: a load left in flight at the
+      // end of the loop would be waited for before its registers are reused)
+      const bool more = i + 2 < nc;
       // scores of pages i, i+1: lane = head r16, positions 4*grp + j
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -2218,11 +2221,12 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
         sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[kb], sa, 0, 0, 0);
         sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kz, ql[kb], sb, 0, 0, 0);
       }
-      // the next pair's keys (no load is skipped by a branch: past the end
-      // the last page is read again)
+      // the next pair's keys (an odd count reads its last page twice)
       const int n0 = min(i + 2, nc - 1), n1 = min(i + 3, nc - 1);
-      load_keys(pid, n0, kq[0]);
-      load_keys(pid, n1, kq[1]);
+      if (more) {
+        load_keys(pid, n0, kq[0]);
+        load_keys(pid, n1, kq[1]);
+      }
       const int pa = (blk0 + wave + (c0 + i) * kWaves) * kPageSize + 4 * grp;
       const int pz = pa + kWaves * kPageSize;
       const bool has_z = i + 1 < nc;
@@ -2305,6 +2309,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
         o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vv, o[nn], 0, 0, 0);
         o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vv, o[nn], 0, 0, 0);
       }
+      if (!more) break;
       load_values(pid, n0, n1);  // the next pair's values
     }
   }
