@@ -2096,6 +2096,19 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   // (shared-sequence plans: this step writes into the pages, so they are
   // read only after the wait)
   if (!kvf) first_pair();
+  // The rotation of this position (a thread's query and key elements all
+  // use element (tid mod HD) mod HD/2 of it) and the page of the current
+  // position do not depend on this step's data either: loaded before the
+  // wait as well.
+  const bool has_cur = pos_ok && !kvf && hi == n;
+  float cv = 0.f, sv = 0.f;
+  int pg = 0;
+  if (pos_ok) {
+    const int i0 = (tid % HD) & (HD / 2 - 1);
+    cv = ldg(d.rope_cos + (size_t)pos * (HD / 2) + i0);
+    sv = ldg(d.rope_sin + (size_t)pos * (HD / 2) + i0);
+    if (has_cur) pg = uni(ldg(prow + pos / kPageSize));
+  }
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
   if (kvf) first_pair();
   if (!pos_ok) {
@@ -2115,10 +2128,7 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     }
     return true;
   }
-  const bool has_cur = !kvf && hi == n;
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
-  const float *cs = d.rope_cos + (size_t)pos * (HD / 2);
-  const float *sn = d.rope_sin + (size_t)pos * (HD / 2);
   // q, k, v are tagged: the loads double as the wait for the projections.
   // A thread's first loads of its key/value and query elements are issued
   // together; only stale ones are then polled, one after another.
@@ -2137,19 +2147,16 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
     const uint64_t rc = ldt_raw(d.q, q0 + h * HD + i0 + HD / 2);
     const float a = ldt_then(sm, d, ca, t, d.q, q0 + h * HD + i0, ra);
     const float c2 = ldt_then(sm, d, ca, t, d.q, q0 + h * HD + i0 + HD / 2, rc);
-    const float cv = ldg(cs + i0), sv = ldg(sn + i0);
     const float r = (i < HD / 2) ? a * cv - c2 * sv : a * sv + c2 * cv;
     qs[h * QROW + (i / (HD / 4)) * QQ + (i & (HD / 4 - 1))] = r * scale;
   }
   if (has_cur) {
-    const int pg = uni(ldg(prow + pos / kPageSize));
     const bool pg_ok = pg >= 0 && pg < d.npages;
     if (!pg_ok && tid == 0) set_error(d, DEVERR_BAD_INPUT, tix, -2, (uint32_t)pg, (uint32_t)d.npages);
     for (int i = tid; i < HD; i += kThreads) {  // (HD <= kThreads: i == tid)
       const int i0 = i & (HD / 2 - 1);
       const float a = ldt_then(sm, d, ca, t, d.k, kvo + i0, kra);
       const float c2 = ldt_then(sm, d, ca, t, d.k, kvo + i0 + HD / 2, krc);
-      const float cv = ldg(cs + i0), sv = ldg(sn + i0);
       const float kr = (i < HD / 2) ? a * cv - c2 * sv : a * sv + c2 * cv;
       const uint16_t kb = f2bf(kr), vb = f2bf(ldt_then(sm, d, ca, t, d.v, kvo + i, vr));
       kc[i] = bf1(kb);
