@@ -356,11 +356,14 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
 
   // attention splits: enough (slot, KV head, split) tasks to cover the CUs,
   // but at least 128 keys per split (a page for each of a task's waves) and
-  // at most 256 partials (G heads x S splits) for the merging split to read
+  // at most 128 partials (G heads x S splits) for the merging split to read
+  // (measured on the MoE shape, G = 8, 8192 keys: 16 splits 3.37 ms/step,
+  // 32 splits 3.42, 12 splits 3.50; on the 8B shape, G = 4, 32 splits stay
+  // ahead of 16 at 131072 keys, 6.24 against 7.07 ms)
   int ctx = o.planned_ctx > 0 ? std::min(o.planned_ctx, p.max_pos) : p.max_pos;
   int want = std::max(1, n_cus / (nkv * B));
   int by_len = std::max(1, ctx / 128);
-  p.S = std::max(1, std::min({want, by_len, std::max(1, 256 / (nq / nkv)), 64}));
+  p.S = std::max(1, std::min({want, by_len, std::max(1, 128 / (nq / nkv)), 64}));
   // a single sequence with a short context (at most 48 pages, six per wave
   // of one task): one split, as the merge's extra hop costs more than the
   // shorter page loops save (measured on the 8B shape: one split ahead at
