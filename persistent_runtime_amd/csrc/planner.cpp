@@ -373,9 +373,12 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   // and changing lengths): the persistent workers claim a layer's attention
   // tasks at run time from a shared counter, longest first; about two tasks
   // per worker keep the last ones to finish short without multiplying the
-  // per-task cost (8B shape, contexts U[128, 16384]: 4 splits best at 16
-  // slots, 2 at 32, 1 at 64, where 2 splits took 2.3 % longer per step).
-  if (o.attn_pool >= 0 && B >= 16)
+  // per-task cost (8B shape, contexts U[128, 16384]: 8 splits best at 8
+  // slots, 6.72 against 6.97 ms/step with 4; 4 at 16 slots, 9.06 against
+  // 9.44 with 8; 2 at 32, 12.89 against 13.24 with 4; 1 at 64, where 2
+  // splits took 2.3 % longer per step; at 4 slots the covering count, 8,
+  // stays ahead of 16, 5.93 against 6.29).
+  if (o.attn_pool >= 0 && B >= 8)
     p.S = std::max(1, std::min({2 * n_workers / (nkv * B), std::max(1, ctx / 256), 64}));
   if (o.attn_splits > 0) p.S = std::min(o.attn_splits, 128);  // merge keeps G*S pairs in LDS
   // (the scheduled executor dispatches tasks one by one: no claimed pool, no

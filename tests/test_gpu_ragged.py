@@ -1,5 +1,6 @@
-"""Continuous batching on the Llama-3-8B shape at full size: 4, 16 and 64
-slots (the matrix-core tiles with split-K, the default from three slots,
+"""Continuous batching on the Llama-3-8B shape at full size: 4, 8, 16 and 64
+slots (the matrix-core tiles with split-K, the default from three slots;
+from 8 slots the attention tasks are claimed from a shared pool;
 and at 4 slots also the vector multi-slot tiles) with seeded synthetic
 cached contexts uniform in [128, 16384] over shuffled 16-token pages, in
 the launch configuration the ragged benchmark times.
@@ -42,8 +43,8 @@ def _host_kv(cfg, ctx, sid):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("B,mfma", [(4, 0), (4, -1), (16, 0), (64, 0)],
-                         ids=["4", "4-vector", "16", "64"])
+@pytest.mark.parametrize("B,mfma", [(4, 0), (4, -1), (8, 0), (16, 0), (64, 0)],
+                         ids=["4", "4-vector", "8", "16", "64"])
 def test_llama8b_ragged_batch_join_retire(llama8b, B, mfma):
     cfg = LLAMA8B
     Wd, Wt = llama8b
