@@ -51,7 +51,7 @@ def test_llama8b_ragged_batch_join_retire(llama8b, B, mfma):
     sched = synth.ragged_schedule(B, 3)
     ctx = list(sched["ctx0"])
     sid = list(sched["sid0"])
-    join_slot, empty_slot = (1, 2) if B < 8 else (5, 9)
+    join_slot, empty_slot = (1, 2) if B < 8 else (5, min(9, B - 1))
     join_ctx, join_sid = 3001, 10_000
     sample = sorted({join_slot, int(np.argmax(ctx)), int(np.argmin(ctx)), 0} - {empty_slot})
     print(f"ragged B={B}: contexts {ctx}; oracle sample {sample}", flush=True)
