@@ -259,7 +259,8 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
   int64_t total = 0;
   for (auto &sg : segs) total += sg.rows;
   int added = 0;
-  if (segs.size() > 1 && (int64_t)segs.size() <= n_workers) {
+  const int nwk = only ? (int)only->size() : n_workers;  // the workers taking rows
+  if (segs.size() > 1 && (int64_t)segs.size() <= nwk) {
     // Several matrices (the q, k, v rows of each KV group): workers are
     // shared out over the segments in proportion to their rows (largest
     // remainder, at least one each), and each segment's rows evenly over its
@@ -268,19 +269,19 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
     std::vector<int> nw(ns);
     int given = 0;
     for (int i = 0; i < ns; ++i) {
-      nw[i] = std::max(1, (int)((double)segs[i].rows * n_workers / (double)total));
+      nw[i] = std::max(1, (int)((double)segs[i].rows * nwk / (double)total));
       given += nw[i];
     }
     // then one worker at a time to the segment with the largest share per
     // worker (or away from the one whose share grows least)
     auto share = [&](int i, int k) { return (double)segs[i].rows / k; };
-    while (given < n_workers) {
+    while (given < nwk) {
       int bi = 0;
       for (int i = 1; i < ns; ++i)
         if (share(i, nw[i]) > share(bi, nw[bi])) bi = i;
       nw[bi]++, given++;
     }
-    while (given > n_workers) {
+    while (given > nwk) {
       int bi = -1;
       for (int i = 0; i < ns; ++i)
         if (nw[i] > 1 && (bi < 0 || share(i, nw[i] - 1) < share(bi, nw[bi] - 1))) bi = i;
@@ -299,7 +300,7 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
           int rpp = (int)((n + P - 1) / P);
           rpp += (unit - rpp % unit) % unit;
           b.add(op, layer, sg.a0, (int)(sg.row0 + lo), (int)n, sg.a3, 0, waits, {sg.sig},
-                n * row_bytes + extra_bytes, w, rpp);
+                n * row_bytes + extra_bytes, only ? (*only)[w] : w, rpp);
           ++added;
           lo += n;
         }
@@ -308,7 +309,7 @@ int add_gemv(Builder &b, int op, int layer, const std::vector<RowSeg> &segs, int
     return added;
   }
   // (a single matrix: the workers in `only` when given, else all of them)
-  const int nw = only ? (int)only->size() : n_workers;
+  const int nw = nwk;
   size_t si = 0;
   int64_t seg_base = 0;  // rows before segs[si]
   for (int i = 0; i < nw; ++i) {
@@ -454,6 +455,13 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
   // attention cannot load its projection rows ahead, so its share would
   // finish last and hold back the next operation.  (Longer shares stream
   // mostly after the wait anyway; there the attention workers would idle.)
+  // The QKV rows go to the others as well, so an attention task starts
+  // waiting for its query, key and value while they are computed: after a
+  // QKV tile of its own, its first loads would queue behind that tile's
+  // output stores, which the memory side acknowledges only after their
+  // write-through, and the task would start polling after the last
+  // projection tile had finished (measured: 8B 3.24 -> 3.12 ms/step, MoE
+  // 3.39 -> 3.24).
   const int n_attn = B * nkv * p.S;
   const int64_t oproj_share = (int64_t)H * nq * hd * 2 / n_workers;
   std::vector<int> attn_w, oproj_w;
@@ -479,7 +487,8 @@ int build_host_plan(const mk_config &c, const mk_plan_options &o, int n_cus,
         segs.push_back({1, g * hd, hd, grp[g]});
         segs.push_back({2, g * hd, hd, grp[g]});
       }
-      if (add_gemv(b, OP_QKV, l, segs, H, 1, n_workers, pmax_for(H), x_ev[l], 0, nullptr) < 0)
+      if (add_gemv(b, OP_QKV, l, segs, H, 1, n_workers, pmax_for(H), x_ev[l], 0, nullptr, 1,
+                   -1, oproj_w.empty() ? nullptr : &oproj_w) < 0)
         ok = false;
     }
     // Shared-sequence plans: every slot's key and value go into the cache
