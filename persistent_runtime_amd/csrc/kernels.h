@@ -379,8 +379,13 @@ DEV bool wait_deps(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws,
     // drops lines the XCD's L2 may hold from before the producers wrote.
     // Plans whose tiles copy their activations device-coherently (mx_sc1)
     // skip it for those tiles: every other input of a tile (residuals,
-    // split-K partials) is read with coherent loads as well.
-    if (ok && d.mfma && !(d.mx_sc1 && static_weights(t.op)))
+    // split-K partials) is read with coherent loads as well.  Attention
+    // skips it too, unless the layer's KVAPP tasks wrote cache pages in this
+    // step: it reads the query, key and value with coherent loads, and the
+    // pages and the page table were written before the launch (8B ragged:
+    // 4 slots -1.2 %, 8 slots -1.7 %, 16 slots -0.8 %).
+    if (ok && d.mfma && !(d.mx_sc1 && static_weights(t.op)) &&
+        !(t.op == OP_ATTN && !d.kv_first))
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tidx() == 0) sm.imisc[0] = ok;
   }
