@@ -941,10 +941,17 @@ DEV void route_wave(Smem &sm, CP &d, const CallArgs &ca, const TD &t, int &sid, 
   const size_t r0 = ((size_t)t.layer * d.B + t.a0) * E;
   constexpr int kPer = 8;  // logits per lane: E <= 512
   uint32_t key[kPer];
+  uint64_t raw[kPer];  // every logit load issued before any is waited for
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    raw[i] = 0u;
+    if (i * 64 < E && i * 64 + lane < E) raw[i] = ldt_raw(d.rl, r0 + i * 64 + lane);
+  }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     key[i] = 0u;
-    if (i * 64 < E && i * 64 + lane < E) key[i] = fkey(ldt_wait(sm, d, ca, t, d.rl, r0 + i * 64 + lane));
+    if (i * 64 < E && i * 64 + lane < E)
+      key[i] = fkey(ldt_then(sm, d, ca, t, d.rl, r0 + i * 64 + lane, raw[i]));
   }
   uint32_t taken = 0;
   auto scan = [&](uint32_t &bk, uint32_t &bi) {  // best untaken (key, id) of this lane
@@ -1122,6 +1129,16 @@ DEV GemvShape2 gemv_shape(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WSta
   q.bb_max = B1 ? 1 : min(kMaxBatchGemv, kLdsXBytes / (q.g.K * 4));
   return q;
 }
+// An expert gate/up task stages its slot's activation row (ready since the
+// output projection) before it routes the slot: the router logits come
+// later, and the staging round trip then overlaps that wait instead of
+// following the routing.  All waves; the staging call after the routing
+// finds the row in place.  False when the step is abandoned.
+DEV bool prestage(Smem &sm, CP &d, const CallArgs &ca, const TD &t, WState &ws) {
+  if (t.op != OP_EGATEUP || ldg(ca.positions + t.a0) < 0) return true;
+  return stage_xt(sm, d, ca, t, ws, t.src, t.K, 1, t.gain);
+}
+
 // the planner never emits more passes x slots than the partial buffers hold
 DEV bool gemv_fits(CP &d, const TD &t, const GemvShape2 &q) {
   if (q.P > 1 && q.P * min(q.nb, q.bb_max) > kMaxPass) {
@@ -1137,6 +1154,7 @@ template <bool B1>
 DEV bool gemv_ctl(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persistent,
                   WState &ws) {
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  if (!prestage(sm, d, ca, t, ws)) return false;
   const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t, ws);
   if (q.fail) return false;
   if (q.skip) {
@@ -1200,6 +1218,7 @@ DEV bool gemv_cmp(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
                   WState &ws, Buf &w, bool w_loaded, bool pre, const Geo &gn, bool inter) {
   const int cw = uni(tidx() >> 6) - 1;
   if (persistent && !wait_deps(sm, d, ca, t, ws)) return false;
+  if (!prestage(sm, d, ca, t, ws)) return false;
   const GemvShape2 q = gemv_shape<B1>(sm, d, ca, t, ws);
   if (q.fail) return false;
   if (q.skip) return true;
