@@ -193,6 +193,7 @@ constexpr int kRowSlot = kMaxTileUnits * 2;    // rows per tile (rows hold >= 25
 #endif
 constexpr bool kRefillPerSlot = MK_REFILL_PER_SLOT;
 constexpr int kRing = 4;                          // task descriptors kept ahead
+constexpr int kAttnScratchOff = kLdsWbufOff - kWaves * 1024;  // attention: a kilobyte per wave
 
 struct Smem {
   float xs[kLdsXBytes / 4];                                 // staged activations
@@ -2054,9 +2055,10 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   float *wl = wm + kWaves * kMaxGroup;       // [kWaves][kMaxGroup]
   float *wo = wl + kWaves * kMaxGroup;       // [kWaves][kMaxGroup][HD]
   float *scur = wo + kWaves * kMaxGroup * HD;
-  // below the LDS weight slots, which may hold loads in flight
+  // below the waves' scratch kilobytes, which sit below the LDS weight
+  // slots (those may hold loads in flight)
   static_assert((kMaxGroup * QROW + 2 * HD + 2 * kWaves * kMaxGroup + kWaves * kMaxGroup * HD +
-                 kMaxGroup) * 4 <= kLdsWbufOff, "attention LDS overlaps the weight slots");
+                 kMaxGroup) * 4 <= kAttnScratchOff, "attention LDS overlaps its scratch");
 
   const int pos = uni(ldg(ca.positions + b));
   const size_t head0 = ((size_t)l * B + b) * nq + (size_t)g * G;  // first head row
@@ -2119,7 +2121,29 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   };
   // (shared-sequence plans: this step writes into the pages, so they are
   // read only after the wait)
-  if (!kvf) first_pair();
+  if (!kvf) {
+    first_pair();
+    // A wave with a second (and last) pair brings it into the L2 as well
+    // (LDS-DMA of each page's keys and values, 1 KiB at a time, into a
+    // scratch kilobyte of the wave above the attention's LDS): the page
+    // loop's own loads of it then come from the L2.  (Nothing reads the
+    // scratch; the copies complete before the task's first wait for its
+    // register loads, which counts them.)  Longer page walks skip it: the
+    // copies would sit ahead of the polls for the task's inputs.
+    const int nwarm = npw <= 4 ? npw : 0;
+    if (nwarm > 2) {
+      const uint32_t junk = (uint32_t)(uintptr_t)sm.xs + (uint32_t)(kAttnScratchOff + wave * 1024);
+      constexpr int kChunks = kPageSize * HD * 2 / 1024;  // 1 KiB pieces of a page
+      for (int i = 2; i < nwarm; ++i) {
+        const size_t pb = page_base(pid, i);
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          dma16((uint64_t)(d.k_pool + pb) + (uint64_t)(c * 1024 + lane * 16), junk);
+          dma16((uint64_t)(d.v_pool + pb) + (uint64_t)(c * 1024 + lane * 16), junk);
+        }
+      }
+    }
+  }
   // The rotation of this position (a thread's query and key elements all
   // use element (tid mod HD) mod HD/2 of it) and the page of the current
   // position do not depend on this step's data either: loaded before the
