@@ -2391,33 +2391,58 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
   __syncthreads();
   trace_mark(d, t, 1);
   if (S == 1 && persistent) trace_finish(d, t);  // before the (tagged) outputs
-  // merge the waves (fixed order) and the current key
-  for (int idx = tid; idx < G * HD; idx += kThreads) {
+  // merge the waves (fixed order) and the current key: four consecutive
+  // dims per thread, written 16 bytes at a time (fewer stores for the
+  // arrival's drain and the consumers' polls to wait for)
+  const __amdgpu_buffer_rsrc_t ro = rsrc(S == 1 ? (const void *)d.attn : (const void *)d.part);
+  for (int idx = tid * 4; idx < G * HD; idx += kThreads * 4) {
     const int h = idx / HD, dd = idx - h * HD;
     float M = -INFINITY;
     for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, wm[w2 * kMaxGroup + h]);
     if (has_cur) M = fmaxf(M, scur[h]);
-    float Ls = 0.f, Os = 0.f;
+    float Ls = 0.f;
+    f32x4 Os = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
       for (int w2 = 0; w2 < kWaves; ++w2) {
         const float mw = wm[w2 * kMaxGroup + h];
         if (mw == -INFINITY) continue;
         const float f = exp2f(mw - M);
         Ls = fmaf(f, wl[w2 * kMaxGroup + h], Ls);
-        Os = fmaf(f, wo[(w2 * kMaxGroup + h) * HD + dd], Os);
+        const f32x4 o = *(const f32x4 *)&wo[(w2 * kMaxGroup + h) * HD + dd];
+        Os.x = fmaf(f, o.x, Os.x);
+        Os.y = fmaf(f, o.y, Os.y);
+        Os.z = fmaf(f, o.z, Os.z);
+        Os.w = fmaf(f, o.w, Os.w);
       }
       if (has_cur) {
         const float f = exp2f(scur[h] - M);
         Ls += f;
-        Os = fmaf(f, vc[dd], Os);
+        const f32x4 v = *(const f32x4 *)&vc[dd];
+        Os.x = fmaf(f, v.x, Os.x);
+        Os.y = fmaf(f, v.y, Os.y);
+        Os.z = fmaf(f, v.z, Os.z);
+        Os.w = fmaf(f, v.w, Os.w);
       }
     }
     if (S == 1) {
-      stv(d, d.attn, (head0 + h) * HD + dd, Ls > 0.f ? Os / Ls : 0.f, ca.tag);
+      // (value, tag) pairs, two per 16-byte store: each pair is one 8-byte
+      // half of it, so a reader that sees a pair's tag sees its value
+      const f32x4 y = Ls > 0.f ? (f32x4){Os.x / Ls, Os.y / Ls, Os.z / Ls, Os.w / Ls}
+                               : (f32x4){0.f, 0.f, 0.f, 0.f};
+      const size_t e = (head0 + h) * HD + dd;
+      const u32x4 p0 = {__float_as_uint(y.x), ca.tag, __float_as_uint(y.y), ca.tag};
+      const u32x4 p1 = {__float_as_uint(y.z), ca.tag, __float_as_uint(y.w), ca.tag};
+      __builtin_amdgcn_raw_buffer_store_b128(p0, ro, (uint32_t)(e * 8), 0, kCpolSc1);
+      __builtin_amdgcn_raw_buffer_store_b128(p1, ro, (uint32_t)(e * 8 + 16), 0, kCpolSc1);
+      if (d.shadow)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y),
+                                               rsrc(shadow_of(d, d.attn)), (uint32_t)(e * 4), 0,
+                                               kCpolSc1);
     } else {
-      float *pp = d.part + ((head0 + h) * S + sp) * PS;
-      sta(pp + dd, Os);
-      if (dd == 0) { sta(pp + HD, M); sta(pp + HD + 1, Ls); }
+      const size_t o = ((head0 + h) * S + sp) * PS;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Os), ro,
+                                             (uint32_t)((o + dd) * 4), 0, kCpolSc1);
+      if (dd == 0) { sta(d.part + o + HD, M); sta(d.part + o + HD + 1, Ls); }
     }
   }
   return true;
