@@ -2546,6 +2546,7 @@ DEV void run_merge(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
     }
   }
   f32x4 *red = (f32x4 *)sm.xs;  // [nsub][nvec]
+  const __amdgpu_buffer_rsrc_t ro = rsrc(d.attn);
   if (act) red[sub * nvec + v] = o;
   __syncthreads();
   for (int vv = tid; vv < nvec; vv += kThreads) {
@@ -2553,10 +2554,15 @@ DEV void run_merge(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
     for (int q = 1; q < nsub; ++q) sum += red[q * nvec + vv];
     const int hh = vv / hv, d0 = (vv - hh * hv) * 4;
     const size_t e = (head0 + hh) * HD + d0;
-    stv(d, d.attn, e + 0, sum.x, ca.tag);
-    stv(d, d.attn, e + 1, sum.y, ca.tag);
-    stv(d, d.attn, e + 2, sum.z, ca.tag);
-    stv(d, d.attn, e + 3, sum.w, ca.tag);
+    // two (value, tag) pairs per 16-byte store, as the attention writes them
+    const u32x4 p0 = {__float_as_uint(sum.x), ca.tag, __float_as_uint(sum.y), ca.tag};
+    const u32x4 p1 = {__float_as_uint(sum.z), ca.tag, __float_as_uint(sum.w), ca.tag};
+    __builtin_amdgcn_raw_buffer_store_b128(p0, ro, (uint32_t)(e * 8), 0, kCpolSc1);
+    __builtin_amdgcn_raw_buffer_store_b128(p1, ro, (uint32_t)(e * 8 + 16), 0, kCpolSc1);
+    if (d.shadow)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sum),
+                                             rsrc(shadow_of(d, d.attn)), (uint32_t)(e * 4), 0,
+                                             kCpolSc1);
   }
 }
 
