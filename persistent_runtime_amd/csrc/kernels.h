@@ -2442,7 +2442,10 @@ DEV bool run_attn(Smem &sm, CP &d, const CallArgs &ca, const TD &t, bool persist
       const size_t o = ((head0 + h) * S + sp) * PS;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Os), ro,
                                              (uint32_t)((o + dd) * 4), 0, kCpolSc1);
-      if (dd == 0) { sta(d.part + o + HD, M); sta(d.part + o + HD + 1, Ls); }
+      if (dd == 0)  // (max, sum) in one 8-byte store
+        __hip_atomic_store((AS1 uint64_t *)(d.part + o + HD),
+                           ((uint64_t)__float_as_uint(Ls) << 32) | __float_as_uint(M),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   return true;
@@ -2516,7 +2519,9 @@ DEV void run_merge(Smem &sm, CP &d, const CallArgs &ca, const TD &t) {
   float2 *ml = (float2 *)&sm.red[0][0];  // [G * S]: (m, l), then (weight, -)
   for (int i = tid; i < npairs; i += kThreads) {
     const float *pp = part0 + (size_t)i * PS + HD;  // pair i = head * S + split
-    ml[i] = make_float2(lda(pp), lda(pp + 1));
+    const uint64_t w = __hip_atomic_load((const AS1 uint64_t *)pp, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);  // (max, sum)
+    ml[i] = make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
   }
   __syncthreads();
   for (int hh = wave; hh < G; hh += kWaves) {
