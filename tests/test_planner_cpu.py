@@ -490,3 +490,34 @@ def test_single_split_for_short_single_sequence_contexts():
     assert splits(551) == 1 and splits(768) == 1
     assert splits(769) == 6 and splits(1047) == 8
     assert splits(768, B=4) > 1
+
+
+def test_split_counts_and_attention_worker_roles():
+    """Split rule: at most 128 partials (query heads x splits) per merge, so
+    the MoE shape (8 query heads per KV head) plans 16 splits at an
+    8192-token context and the 8B shape (4 per KV head) 32 at 131072;
+    claimed attention from 8 slots with 2 x workers / (KV heads x slots)
+    splits.  Where attention has workers of its own (single sequence), they
+    take no QKV rows, and on the MoE shape they hold the router rows."""
+    def attn(tasks, layer=3):
+        return [t for t in tasks if mk.OPS[t.op] == "ATTN" and t.layer == layer]
+    moe, _ = mk.inspect_plan(_cfg(MOE30B, maxp=(8192 + 64) // 16),
+                             mk.default_options(n_cus=256, planned_ctx=8192 + 64))
+    a = attn(moe)
+    assert max(t.a2 for t in a) + 1 == 16
+    aw = {t.worker for t in a}
+    assert len(aw) == len(a) == MOE30B["n_kv_heads"] * 16
+    router = [t for t in moe if mk.OPS[t.op] == "ROUTER" and t.layer == 3]
+    assert {t.worker for t in router} <= aw
+    assert sum(t.a2 for t in router) == MOE30B["n_experts"]
+    qkv = [t for t in moe if mk.OPS[t.op] == "QKV" and t.layer == 3]
+    assert not {t.worker for t in qkv} & aw
+    lc, _ = mk.inspect_plan(_cfg(LLAMA8B, maxp=(131072 + 64) // 16),
+                            mk.default_options(n_cus=256, planned_ctx=131072 + 64))
+    assert max(t.a2 for t in attn(lc)) + 1 == 32
+    for B, S in ((8, 8), (16, 4), (32, 2), (64, 1)):
+        tasks, _ = mk.inspect_plan(_cfg(LLAMA8B, B=B, maxp=1024),
+                                   mk.default_options(n_cus=256, planned_ctx=16384))
+        a = attn(tasks)
+        assert max(t.a2 for t in a) + 1 == S, B
+        assert all(t.a4 == a[0].a4 for t in a) and sum(t.a3 for t in a) == len(a), B  # claimed
